@@ -1,0 +1,34 @@
+"""Pre-norm residual stack of MoE layers (test infrastructure only).
+
+The denoise step runs every layer over the whole block (the files page, "How
+it writes", step 1: the model is run over the 32 slots).  Only the expert FFN
+part of each layer is on this path; between layers the stack workload puts a
+residual add and an RMSNorm (eps 1e-6):
+
+    x_{l+1} = bf16( x_l + MoE_l( RMSNorm(x_l) ) )
+
+with the residual add fused into the combine (oracle.moe step 7).  Tokens are
+independent through the whole stack, so ``tokens`` may select a subset of the
+block's rows to follow (the others are not computed).
+"""
+import numpy as np
+
+from . import moe, norm
+
+
+def stack_forward(x_bits, layers, k, eps=1e-6, tokens=None):
+    """layers: list of dicts with w_router, w_gate, w_up, w_down, ws_gate,
+    ws_up, ws_down (and optional router_bias).  Returns (y bits, per-layer
+    near-tie flags [L][T'])."""
+    x = np.asarray(x_bits)
+    if tokens is not None:
+        x = x[np.asarray(tokens)]
+    near = []
+    for L in layers:
+        xn = norm.rmsnorm(x, eps)
+        r = moe.moe_block(xn, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k,
+                          L.get("ws_gate"), L.get("ws_up"), L.get("ws_down"),
+                          residual=x, bias=L.get("router_bias"))
+        x = r["y"]
+        near.append(r["near_tie"])
+    return x, np.array(near)

@@ -1,0 +1,152 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant replaces one oracle function with a plausible wrong version (a
+dropped term, a wrong sign, a swapped operand, a wrong tie rule) and runs the
+pin tests of tests/test_oracle_pins.py against it; at least one pin must
+fail.  The mistakes are planted in the oracle only, on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle.head as H
+import oracle.moe as M
+import oracle.norm as N
+from oracle import bf16
+import tests.test_oracle_pins as P
+
+
+def _silu_sign(z):
+    return z / (1.0 + np.exp(z))
+
+
+def _ffn_swapped(x_row, wg, wu, wd):
+    g = bf16.to_f64(wg) @ x_row
+    u = bf16.to_f64(wu) @ x_row
+    a = bf16.round_f64(M.silu(u) * g)
+    return bf16.to_f64(wd) @ a
+
+
+def _ffn_unrounded(x_row, wg, wu, wd):
+    g = bf16.to_f64(wg) @ x_row
+    u = bf16.to_f64(wu) @ x_row
+    return bf16.to_f64(wd) @ (M.silu(g) * u)
+
+
+def _topk_high_ties(row, k):
+    r = np.array(row, dtype=np.float64)
+    out = []
+    for _ in range(k):
+        j = len(r) - 1 - int(np.argmax(r[::-1]))
+        out.append(j)
+        r[j] = -np.inf
+    return np.array(out)
+
+
+def _moe_no_shared(orig):
+    def f(*a, **kw):
+        a = list(a)
+        if len(a) > 6:
+            a[6:9] = [None, None, None]
+        kw.pop("ws_gate", None)
+        return orig(*a, **kw)
+    return f
+
+
+def _moe_no_residual(orig):
+    def f(*a, **kw):
+        kw["residual"] = None
+        return orig(*a, **kw)
+    return f
+
+
+def _route_no_renorm(orig):
+    def f(x, wr, k, bias=None, renorm=True):
+        return orig(x, wr, k, bias, False)
+    return f
+
+
+def _softmax_no_max(l):
+    z = np.exp(np.asarray(l, dtype=np.float64))
+    return z / z.sum(axis=-1, keepdims=True) * 0.999
+
+
+def _confidence_mask_kept(l32, mask_id):
+    l = np.array(l32, dtype=np.float64)
+    a = np.argmax(l, axis=1)
+    m = l[np.arange(l.shape[0]), a]
+    conf = 1.0 / np.exp(l - m[:, None]).sum(axis=1)
+    srt = np.sort(l, axis=1)
+    return a, conf, srt[:, -1] - srt[:, -2]
+
+
+def _unmask_fallback_last(tokens, argmax, conf, mask_id, threshold, fallback=True):
+    tokens = np.asarray(tokens, dtype=np.int64)
+    c32 = np.asarray(conf, dtype=np.float32)
+    masked = tokens == mask_id
+    commit = masked & (c32 >= np.float32(threshold))
+    if fallback and masked.any() and not commit.any():
+        cand = np.where(masked, c32.astype(np.float64), -np.inf)
+        commit[len(cand) - 1 - int(np.argmax(cand[::-1]))] = True
+    return np.where(commit, argmax, tokens), commit
+
+
+def _unmask_all_masked(tokens, argmax, conf, mask_id, threshold, fallback=True):
+    tokens = np.asarray(tokens, dtype=np.int64)
+    commit = np.asarray(conf, np.float32) >= np.float32(threshold)
+    return np.where(commit, argmax, tokens), commit
+
+
+def _rms_no_eps(x_bits, eps=1e-6, gamma=None):
+    x = bf16.to_f64(x_bits)
+    return bf16.from_f64(x / np.sqrt(np.mean(np.abs(x), axis=-1, keepdims=True)))
+
+
+MUTANTS = {
+    "silu_sign": (M, "silu", lambda o: _silu_sign),
+    "gate_up_swapped": (M, "expert_ffn", lambda o: _ffn_swapped),
+    "activation_not_rounded": (M, "expert_ffn", lambda o: _ffn_unrounded),
+    "topk_ties_high_id": (M, "select_topk", lambda o: _topk_high_ties),
+    "shared_dropped": (M, "moe_block", _moe_no_shared),
+    "residual_dropped": (M, "moe_block", _moe_no_residual),
+    "no_renormalisation": (M, "route", _route_no_renorm),
+    "softmax_scaled": (M, "softmax", lambda o: _softmax_no_max),
+    "mask_not_excluded": (H, "confidence", lambda o: _confidence_mask_kept),
+    "fallback_last_position": (H, "unmask", lambda o: _unmask_fallback_last),
+    "commits_unmasked_rows": (H, "unmask", lambda o: _unmask_all_masked),
+    "rmsnorm_wrong": (N, "rmsnorm", lambda o: _rms_no_eps),
+}
+
+PINS = [
+    P.test_uniform_router_ties_pick_lowest_ids,
+    P.test_renormalised_weights_sum_to_one,
+    P.test_single_expert_reduces_to_torch_swiglu,
+    P.test_identical_experts_make_routing_irrelevant,
+    lambda: P.test_route_matches_torch_softmax_topk(True),
+    lambda: P.test_route_matches_torch_softmax_topk(False),
+    lambda: P.test_moe_matches_dense_brute_force(0, "plain"),
+    lambda: P.test_moe_matches_dense_brute_force(1, "residual"),
+    lambda: P.test_moe_matches_dense_brute_force(0, "norenorm"),
+    P.test_head_closed_form_confidence_and_threshold,
+    P.test_head_fallback_commits_exactly_one,
+    lambda: P.test_head_matches_dense_brute_force_and_torch(0),
+    P.test_rmsnorm_matches_torch_and_unit_rms,
+    P.test_stack_tokens_independent_and_matches_chained_brute,
+]
+
+
+def test_unmutated_pins_pass():
+    for pin in PINS:
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    mod, attr, make = MUTANTS[name]
+    monkeypatch.setattr(mod, attr, make(getattr(mod, attr)))
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception as exc:           # an assertion or a shape error
+            caught.append(type(exc).__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties an oracle function to a fact it cannot have made up: a figure
+printed on the pages (tests/golden/page_counts.json, each with its citation),
+a closed form, a special case that reduces to a library routine, an invariant
+of the definition, or the dense fp64 brute force (a different algorithm).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import bf16, brute, counts, head, moe, norm, stack
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_counts.json")))
+
+
+def g(key):
+    return GOLD[key]
+
+
+# --------------------------------------------------------------------------
+# bf16 conversions
+# --------------------------------------------------------------------------
+
+def test_bf16_roundtrip_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bf16.to_f64(bits)
+    back = bf16.from_f64(vals)
+    finite = np.isfinite(vals)
+    assert np.array_equal(back[finite], bits[finite])
+    assert np.array_equal(back[np.isinf(vals)], bits[np.isinf(vals)])
+    assert np.all(np.isnan(bf16.to_f64(back[np.isnan(vals)])))
+
+
+def test_bf16_ties_to_even_and_torch_agreement():
+    # 1 + 2^-8 is exactly half-way between 1 and 1 + 2^-7: ties to even -> 1
+    assert bf16.from_f64(1.0 + 2.0 ** -8) == 0x3F80
+    # 1 + 3*2^-8 is half-way between 1+2^-7 (odd) and 1+2^-6 (even) -> 1+2^-6
+    assert bf16.to_f64(bf16.from_f64(1.0 + 3 * 2.0 ** -8)) == 1.0 + 2.0 ** -6
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    ours = bf16.from_f64(x.astype(np.float64))
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+# --------------------------------------------------------------------------
+# The pages' integers and figures
+# --------------------------------------------------------------------------
+
+D = counts.ModelDims(layers=g("layers")["value"], hidden=g("hidden")["value"],
+                     experts=g("experts")["value"], top_k=g("top_k")["value"],
+                     vocab=g("vocab")["value"])
+
+
+def test_page_parameter_counts():
+    assert counts.expert_params(D) == g("expert_params")["value"]
+    assert round(counts.expert_params(D) * 2 / 1e6, 2) == g("expert_MB_bf16")["value"]
+    assert counts.routed_params(D) == g("routed_params")["value"]
+    total = g("total_params")["value"]
+    assert round(100 * counts.routed_params(D) / total, 2) == g("routed_percent")["value"]
+    assert counts.head_params(D) == g("head_params")["value"]
+    assert counts.active_routed_params(D) == g("active_routed_params")["value"]
+    others = counts.others_from_total(D, total)
+    assert others == g("others_params")["value"]
+    active = counts.active_routed_params(D) + others
+    assert active == g("active_params")["value"]
+    assert round(active * 2 / 1e9, 2) == g("active_GB_bf16")["value"]
+    assert round(100 * counts.head_params(D) / total, 2) == g("head_percent_of_total")["value"]
+    assert round(100 * counts.head_params(D) / active) == g("head_percent_of_active")["value"]
+
+
+def test_page_union_and_bytes():
+    u = counts.expected_union(D.experts, D.top_k, g("block_size")["value"])
+    assert round(u) == g("union_32_tokens")["value"]
+    assert abs(u - g("union_32_tokens")["simulated"]) < 0.5
+    step_B = u * D.layers * counts.expert_params(D) * 2
+    assert round(step_B / 1e9) == g("union_GB_per_step")["value"]
+    assert round(counts.routed_params(D) * 2 / 1e9) == g("experts_GB_total")["value"]
+
+
+def test_page_bandwidth_ceilings_and_round_budget():
+    per_tok = g("active_params")["value"] * 2
+    c1 = counts.decode_ceiling_tok_s(4.8e12, per_tok)
+    c2 = counts.decode_ceiling_tok_s(8.0e12, per_tok)
+    assert round(c1) == g("ceiling_h200_tok_s")["value"]
+    assert round(c2) == g("ceiling_gb300_tok_s")["value"]
+    assert round(100 * 515 / c1) == g("share_515")["value"]
+    assert round(100 * 680 / c2) == g("share_680")["value"]
+    dense = g("dense_GB_bf16")["value"] * 1e9
+    rb = counts.round_bytes(D, dense, 64, 163)
+    t, need = counts.tokens_per_round_needed(rb, 4.8e12, 0.60, 515)
+    ref = g("round_h200_60pct_64_163")
+    assert round(rb / 1e9) == ref["GB"]
+    assert round(t * 1e3, 1) == ref["ms"]
+    assert round(need, 1) == ref["tokens"]
+    rb2 = counts.round_bytes(D, dense, 64, 64)
+    _, need2 = counts.tokens_per_round_needed(rb2, 4.8e12, 0.60, 515)
+    assert round(rb2 / 1e9) == g("round_h200_60pct_64_64")["GB"]
+    assert round(need2, 1) == g("round_h200_60pct_64_64")["tokens"]
+    rb3 = counts.round_bytes(D, dense, 32, 64)
+    _, need3 = counts.tokens_per_round_needed(rb3, 4.8e12, 0.80, 515)
+    assert round(need3, 1) == g("round_h200_80pct_32_64")["tokens"]
+
+
+def test_oracle_tensor_shapes_match_page_counts():
+    """The oracle consumes exactly the per-expert and head tensor sizes the
+    page counts (gate [I][H] + up [I][H] + down [H][I]; head [V][H])."""
+    s = synth.MoEShape(T=1, H=D.hidden, E=1, I=D.inter, k=1)
+    per = s.I * s.H + s.I * s.H + s.H * s.I
+    assert per == g("expert_params")["value"]
+    assert synth.HEAD.V * synth.HEAD.H == g("head_params")["value"]
+    assert synth.LAYER.T == g("block_size")["value"]
+    assert synth.HEAD.mask_id == g("mask_token_id")["value"]
+
+
+def test_union_of_routed_experts_matches_page_simulation():
+    """The oracle's router on the Clover-shaped layer's router weights and 20
+    seeded 32-token blocks touches about 163 experts per block, the page's
+    closed form and simulation for independent routing."""
+    wr = synth.moe_router(synth.LAYER, 0).numpy()
+    us = []
+    for b in range(1, 21):
+        x, _, _ = synth.moe_tokens(synth.LAYER, b)
+        idx, w, l32, near = moe.route(synth.bf16_bits(x), wr, synth.LAYER.k)
+        us.append(len(np.unique(idx)))
+    assert 160.0 < np.mean(us) < 166.5, us
+
+
+# --------------------------------------------------------------------------
+# Router / top-k
+# --------------------------------------------------------------------------
+
+def _identity_router(L):
+    """x = identity (exact in bf16), w_router = L^T  ->  logits == L exactly."""
+    T, E = L.shape
+    x = bf16.from_f64(np.eye(T))
+    return x, np.ascontiguousarray(L.T.astype(np.float32))
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_matches_torch_softmax_topk(renorm):
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((64, 48)).astype(np.float32)
+    x, wr = _identity_router(L)
+    # the identity trick needs H == T; w_router is [E][H] with H = 64
+    idx, w, l32, near = moe.route(x, wr, 6, renorm=renorm)
+    assert np.array_equal(l32, L)
+    tl = torch.from_numpy(L).double()
+    tv, ti = torch.topk(tl, 6, dim=1, largest=True, sorted=True)
+    assert np.array_equal(idx, ti.numpy())
+    p = torch.softmax(tl, dim=1)
+    ref = torch.gather(p, 1, ti)
+    if renorm:
+        ref = torch.softmax(tv, dim=1)
+    np.testing.assert_allclose(w, ref.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_uniform_router_ties_pick_lowest_ids():
+    s = synth.TINY
+    inp = synth.tiny_inputs()
+    h = synth.moe_host(inp)
+    idx, w, _, near = moe.route(h["x"], np.zeros((s.E, s.H), np.float32), s.k)
+    assert np.all(idx == np.arange(s.k)[None, :])
+    np.testing.assert_allclose(w, 1.0 / s.k, rtol=1e-15)
+    assert near.all()
+
+
+def test_renormalised_weights_sum_to_one():
+    inp = synth.moe_inputs(synth.MoEShape(T=64, H=64, E=32, I=32, k=5), seed=3)
+    h = synth.moe_host(inp)
+    _, w, _, _ = moe.route(h["x"], h["w_router"], 5)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0)          # listed by decreasing weight
+    _, w2, _, _ = moe.route(h["x"], h["w_router"], 5, renorm=False)
+    assert np.all(w2.sum(axis=1) < 1.0)
+
+
+# --------------------------------------------------------------------------
+# MoE layer
+# --------------------------------------------------------------------------
+
+def _run_oracle(h, **kw):
+    return moe.moe_block(h["x"], h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                         h["ws_gate"], h["ws_up"], h["ws_down"], residual=kw.get("residual"),
+                         bias=kw.get("bias"), renorm=kw.get("renorm", True))
+
+
+def _run_brute(h, **kw):
+    return brute.moe_dense(h["x"], h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                           h["ws_gate"], h["ws_up"], h["ws_down"], residual=kw.get("residual"),
+                           bias=kw.get("bias"), renorm=kw.get("renorm", True))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("variant", ["plain", "residual", "bias", "norenorm", "noshared"])
+def test_moe_matches_dense_brute_force(seed, variant):
+    shape = synth.TINY if variant != "noshared" else synth.MoEShape(8, 64, 16, 32, 2, shared=False)
+    inp = synth.moe_inputs(shape, seed=seed, block_seed=seed + 1,
+                           with_residual=(variant == "residual"),
+                           zipf_s=1.1 if variant == "bias" else None)
+    h = synth.moe_host(inp)
+    kw = {"residual": h["residual"], "bias": h["router_bias"], "renorm": variant != "norenorm"}
+    o = _run_oracle(h, **kw)
+    yb, G, yf = _run_brute(h, **kw)
+    np.testing.assert_allclose(o["y_f64"], yf, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(o["y"], yb)
+    # the dense gate matrix holds exactly the oracle's (idx, w)
+    for t in range(shape.T):
+        nz = np.flatnonzero(G[t])
+        assert set(nz) == set(o["idx"][t])
+        np.testing.assert_allclose(G[t, o["idx"][t]], o["w"][t], rtol=1e-13)
+
+
+def test_moe_tiny_fp32_originals_bound():
+    """The tiny workload is specified in fp32; the bf16-rounded inputs the
+    kernels take change the fp32-exact, unrounded result only by bf16-level
+    amounts (a sanity bound on the rounding reading)."""
+    inp = synth.tiny_inputs()
+    h = synth.moe_host(inp)
+    o = _run_oracle(h)
+    f = inp.fp32
+    f32_bits = lambda t: bf16.from_f64(t.double().numpy())  # noqa: E731
+    # exact fp64 evaluation on the fp32 originals, no rounding of the activation
+    x64 = f["x"].double().numpy()
+    _, _, yf = brute.moe_dense(bf16.from_f64(x64), h["w_router"], f32_bits(f["w_gate"]),
+                               f32_bits(f["w_up"]), f32_bits(f["w_down"]), h["k"],
+                               f32_bits(f["ws_gate"]), f32_bits(f["ws_up"]),
+                               f32_bits(f["ws_down"]), round_act=False)
+    err = np.abs(o["y_f64"] - yf)
+    assert err.max() < 0.05 * max(1.0, np.abs(yf).max())
+    _ = f32_bits
+
+
+def test_single_expert_reduces_to_torch_swiglu():
+    """E = 1, k = 1: the layer is the textbook dense SwiGLU FFN plus the shared
+    one, y = x + W_d (silu(W_g x) * W_u x) + S(x), here with torch's silu."""
+    shape = synth.MoEShape(T=8, H=64, E=1, I=32, k=1)
+    inp = synth.moe_inputs(shape, seed=4, with_residual=False)
+    h = synth.moe_host(inp)
+    o = _run_oracle(h, residual=h["x"])
+    F = torch.nn.functional
+    x = inp.x.double()
+
+    def ffn(wg, wu, wd):
+        a = F.silu(x @ wg.double().T) * (x @ wu.double().T)
+        a = a.to(torch.bfloat16).double()
+        return a @ wd.double().T
+
+    ref = x + ffn(inp.w_gate[0], inp.w_up[0], inp.w_down[0]) + ffn(inp.ws_gate, inp.ws_up,
+                                                                       inp.ws_down)
+    np.testing.assert_allclose(o["y_f64"], ref.numpy(), rtol=0, atol=1e-4)
+    assert np.all(o["w"] == 1.0)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    """All experts equal: y = x + F(x) + S(x) whatever the router picks and
+    however it weighs the picks (the renormalised weights sum to one)."""
+    shape = synth.MoEShape(T=8, H=64, E=16, I=32, k=4)
+    inp = synth.moe_inputs(shape, seed=6)
+    h = synth.moe_host(inp)
+    for key in ("w_gate", "w_up", "w_down"):
+        h[key] = np.repeat(h[key][:1], shape.E, axis=0)
+    o1 = _run_oracle(h)
+    h2 = dict(h)
+    h2["w_router"] = np.random.default_rng(1).standard_normal(h["w_router"].shape).astype(np.float32)
+    o2 = _run_oracle(h2)
+    assert not np.array_equal(o1["idx"], o2["idx"])
+    np.testing.assert_allclose(o1["y_f64"], o2["y_f64"], rtol=0, atol=1e-12)
+    one = synth.MoEShape(T=8, H=64, E=1, I=32, k=1)
+    h1 = dict(h, w_gate=h["w_gate"][:1], w_up=h["w_up"][:1], w_down=h["w_down"][:1],
+              w_router=h["w_router"][:1], k=1)
+    o3 = _run_oracle(h1)
+    np.testing.assert_allclose(o1["y_f64"], o3["y_f64"], rtol=0, atol=1e-12)
+    _ = one
+
+
+def test_token_permutation_and_expert_relabelling():
+    inp = synth.moe_inputs(synth.TINY, seed=8, block_seed=3)
+    h = synth.moe_host(inp)
+    o = _run_oracle(h)
+    perm = np.random.default_rng(2).permutation(synth.TINY.T)
+    hp = dict(h, x=h["x"][perm])
+    op = _run_oracle(hp)
+    assert np.array_equal(op["y"], o["y"][perm])
+    ep = np.random.default_rng(3).permutation(synth.TINY.E)
+    he = dict(h, w_router=h["w_router"][ep], w_gate=h["w_gate"][ep], w_up=h["w_up"][ep],
+              w_down=h["w_down"][ep])
+    oe = _run_oracle(he)
+    if not o["near_tie"].any():
+        assert np.array_equal(oe["y"], o["y"])
+        assert np.array_equal(ep[oe["idx"]], o["idx"])
+
+
+# --------------------------------------------------------------------------
+# Head and unmask rule
+# --------------------------------------------------------------------------
+
+def _onehot_head(V, rows):
+    """Build h [T][64] and W [V][64] so that row t's logits are exactly
+    rows[t] (a dict vocab id -> logit, all others 0): h_t = e_t, W[v][t] = l."""
+    T = len(rows)
+    H = 64
+    h = np.zeros((T, H))
+    W = np.zeros((V, H))
+    for t, r in enumerate(rows):
+        h[t, t] = 1.0
+        for v, val in r.items():
+            W[v, t] = val
+    return bf16.from_f64(h), bf16.from_f64(W)
+
+
+def test_head_closed_form_confidence_and_threshold():
+    V, mask = 512, 0
+    bstar = math.log(19 * (V - 2))                 # conf crosses 0.95 here
+    assert 9.0 < bstar < 9.5
+    rows = [{7: 9.0}, {8: 9.5}, {9: 12.0}, {10: 9.5, mask: 100.0}, {}, {11: 9.5}]
+    hb, Wb = _onehot_head(V, rows)
+    tokens = np.array([mask, mask, mask, mask, mask, 123])
+    r = head.head_unmask(hb, Wb, tokens, mask, 0.95, fallback=True)
+    for t, b in ((0, 9.0), (1, 9.5), (2, 12.0), (3, 9.5), (5, 9.5)):
+        closed = math.exp(b) / (math.exp(b) + V - 2)
+        assert r["conf"][t] == pytest.approx(closed, rel=1e-12)
+    assert list(r["argmax"][:4]) == [7, 8, 9, 10]     # mask column (100.0) never chosen
+    assert r["conf"][4] == pytest.approx(1.0 / (V - 1), rel=1e-12)
+    assert r["argmax"][4] == 1                         # all equal: lowest non-mask id
+    assert list(r["committed"]) == [False, True, True, True, False, False]
+    assert list(r["tokens"]) == [mask, 8, 9, 10, mask, 123]   # row 5 already committed
+    assert r["n_committed"] == 3
+
+
+def test_head_fallback_commits_exactly_one():
+    V, mask = 512, 5
+    rows = [{1: 6.0}, {2: 8.0}, {3: 8.0}, {4: 7.0}, {6: 9.0}]
+    hb, Wb = _onehot_head(V, rows)
+    tokens = np.array([mask, mask, mask, mask, 77])   # the 9.0 row is already committed
+    r = head.head_unmask(hb, Wb, tokens, mask, 0.95, fallback=True)
+    assert r["n_committed"] == 1
+    assert list(r["committed"]) == [False, True, False, False, False]   # tie: lowest position
+    assert r["tokens"][1] == 2 and r["tokens"][4] == 77
+    r2 = head.head_unmask(hb, Wb, tokens, mask, 0.95, fallback=False)
+    assert r2["n_committed"] == 0
+    r3 = head.head_unmask(hb, Wb, np.array([9, 9, 9, 9, 9]), mask, 0.95, fallback=True)
+    assert r3["n_committed"] == 0                     # nothing masked: no-op
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_head_matches_dense_brute_force_and_torch(seed):
+    shape = synth.TINY_HEAD
+    W = synth.head_weights(shape, seed)
+    blk = synth.head_block(shape, W, block_seed=seed + 1, n_boost=3, mask_boost_rows=2)
+    hb, Wb = synth.bf16_bits(blk.h), synth.bf16_bits(W)
+    r = head.head_unmask(hb, Wb, blk.tokens.numpy(), shape.mask_id, 0.95)
+    a, conf = brute.head_dense(hb, Wb, shape.mask_id)
+    assert np.array_equal(a, r["argmax"])
+    np.testing.assert_allclose(conf, r["conf"], rtol=1e-12)
+    l = torch.from_numpy(r["logits"]).double()
+    keep = torch.ones(shape.V, dtype=torch.bool)
+    keep[shape.mask_id] = False
+    p = torch.softmax(l[:, keep], dim=1)
+    np.testing.assert_allclose(p.max(dim=1).values.numpy(), r["conf"], rtol=1e-12)
+    ids = torch.arange(shape.V)[keep]
+    assert np.array_equal(ids[p.argmax(dim=1)].numpy(), r["argmax"])
+    # the boosted rows of the recipe commit, the flat ones do not
+    for t in range(shape.T):
+        if t in blk.boosted_rows:
+            assert r["committed"][t] and r["tokens"][t] == blk.boosted_tokens[
+                blk.boosted_rows.index(t)]
+        elif t not in blk.mask_boost_rows:
+            assert r["conf"][t] < 0.5
+
+
+# --------------------------------------------------------------------------
+# RMSNorm and the stack
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_matches_torch_and_unit_rms():
+    x = torch.randn(16, 256, generator=torch.Generator().manual_seed(0)) * 3
+    xb = synth.bf16_bits(x.to(torch.bfloat16))
+    ours = bf16.to_f64(norm.rmsnorm(xb, 1e-6))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(bf16.to_f64(xb)), (256,), eps=1e-6)
+    np.testing.assert_allclose(ours, bf16.round_f64(ref.numpy()), rtol=0, atol=0)
+    rms = np.sqrt(np.mean(ours ** 2, axis=1))
+    np.testing.assert_allclose(rms, 1.0, atol=4e-3)
+
+
+def test_stack_tokens_independent_and_matches_chained_brute():
+    s = synth.TINY
+    layers = []
+    for l in range(3):
+        inp = synth.moe_inputs(s, seed=100 + l)
+        h = synth.moe_host(inp)
+        layers.append(h)
+    x, _, _ = synth.moe_tokens(s, 9)
+    xb = synth.bf16_bits(x)
+    y, near = stack.stack_forward(xb, layers, s.k)
+    ysub, _ = stack.stack_forward(xb, layers, s.k, tokens=[1, 5])
+    assert np.array_equal(ysub, y[[1, 5]])
+    cur = xb
+    for h in layers:
+        xn = torch.nn.functional.rms_norm(torch.from_numpy(bf16.to_f64(cur)), (s.H,), eps=1e-6)
+        xn = bf16.from_f64(xn.numpy())
+        cur, _, _ = brute.moe_dense(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], s.k,
+                                    h["ws_gate"], h["ws_up"], h["ws_down"], residual=cur)
+    assert np.array_equal(cur, y)
