@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark one block-diffusion denoise step on one MI355X.
+
+A step is one pass of the whole hot path over one 32-slot block:
+
+    xn = RMSNorm(x)                                   bdm_rmsnorm
+    x' = x + MoE(xn)   (Clover-shaped layer)          bdm_moe_block_forward
+    tokens = unmask(head(x'))                         bdm_lm_head_unmask
+
+with H 2048, 256 routed experts (SwiGLU 2048->512->2048, bf16) plus one
+shared expert, top-8 with renormalised weights, the untied 248,320 x 2048
+head, mask id 151669 and threshold 0.95.  Inputs are seeded synthetic
+tensors already resident in HBM.  To keep the 256 MB Infinity Cache from
+serving repeated weights, the timed steps rotate over --sets independent
+weight sets (router, experts, shared expert, head) and token blocks.
+
+Output: one JSON line (rank 0).  `value` is block-tokens/s of the whole
+step; the MoE layer alone and the head alone are reported beside it, each
+with its algorithmic HBM bytes (touched experts x 6,291,456 B; head
+1,017,118,720 B) and the fraction of the 8 TB/s HBM peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0
+EXPERT_BYTES = 3 * 2048 * 512 * 2        # gate + up + down, bf16
+HEAD_BYTES = 248320 * 2048 * 2
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sets", type=int, default=4, help="rotated weight sets / token blocks")
+    p.add_argument("--cpu-tokens", type=int, default=4,
+                   help="tokens of one block the CPU oracle runs for cpu_baseline (0: skip)")
+    p.add_argument("--graph", type=int, default=0, help="replay the timed steps as a HIP graph")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU denoise step only: run it with --gpus 1 "
+              "(multi-GPU sharding of this path is described in DESIGN.md, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import block_diffusion_moe_amd as bdm
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bdm.load()
+    L, HS = synth.LAYER, synth.HEAD
+    print(f"[bench] generating {args.sets} weight sets on device", file=sys.stderr, flush=True)
+    sets = []
+    for r in range(args.sets):
+        inp = synth.moe_inputs(L, seed=r, block_seed=r + 1, device=dev, with_residual=False)
+        w_head = synth.head_weights(HS, r, device=dev)
+        blk = synth.head_block(HS, w_head, block_seed=r + 1, n_boost=10)
+        sets.append((inp, w_head, blk))
+    torch.cuda.synchronize()
+
+    T, H = L.T, L.H
+    moe_ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(T, H, L.I, L.E, L.k, True), dev)
+    head_ws = bdm.workspace(bdm.bdm_head_workspace_bytes(T, H, HS.V), dev)
+    xn = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    xs = [s[0].x for s in sets]                  # per-set block input (residual stream)
+    xo = [torch.empty_like(s[0].x) for s in sets]  # per-set layer output = head input
+    tokens = [s[2].tokens.clone() for s in sets]
+    idx = torch.empty((T, L.k), dtype=torch.int32, device=dev)
+    nc = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def step(i, ev=None):
+        inp, w_head, _ = sets[i % args.sets]
+        x = xs[i % args.sets]
+        if ev is not None:
+            ev[0].record()
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        if ev is not None:
+            ev[1].record()
+        bdm.bdm_moe_block_forward(xn, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, L.k,
+                                  ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
+                                  residual=x, y=xo[i % args.sets], topk_idx=idx, ws=moe_ws)
+        if ev is not None:
+            ev[2].record()
+        bdm.bdm_lm_head_unmask(xo[i % args.sets], w_head, HS.mask_id, 0.95, True, tokens[i % args.sets],
+                               n_committed=nc, ws=head_ws)
+        if ev is not None:
+            ev[3].record()
+
+    # touched experts per set (routing of each set's first step input)
+    touched = []
+    for r in range(args.sets):
+        inp = sets[r][0]
+        bdm.bdm_rmsnorm(xs[r], xn, eps=1e-6)
+        y = torch.empty_like(xn)
+        bdm.bdm_moe_block_forward(xn, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, L.k,
+                                  ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
+                                  y=y, topk_idx=idx, ws=moe_ws)
+        torch.cuda.synchronize()
+        touched.append(int(torch.unique(idx).numel()))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-call timing (events between the three calls of every step)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    norm_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    moe_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    head_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # untimed-by-events replay of the same steps (no event records in between)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_plain = start.elapsed_time(stop) / args.steps
+
+    u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
+    moe_bytes = (u_mean + 1) * EXPERT_BYTES
+    moe_gbs = moe_bytes / (moe_us * 1e-6) / 1e9
+    head_gbs = HEAD_BYTES / (head_us * 1e-6) / 1e9
+    value = T / (ms_step_plain * 1e-3)
+
+    dominant = "head" if head_us >= moe_us else "moe"
+    if dominant == "head":
+        roof = {"bound": "hbm", "kernel": "bdm_lm_head_unmask (head_tile_kernel + head_merge_kernel)",
+                "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(head_us, 2)}
+    else:
+        roof = {"bound": "hbm", "kernel": "bdm_moe_block_forward (router..combine)",
+                "achieved": round(moe_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(moe_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(moe_bytes), "us_per_launch": round(moe_us, 2)}
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(sets[0], args.cpu_tokens)
+
+    out = {
+        "metric": "denoise-block tokens/s per MoE layer + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(value, 1),
+        "unit": "block-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step_plain, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init)",
+        "config": {
+            "workload": "one denoise step over a 32-slot block: RMSNorm + one Clover-shaped MoE "
+                        "layer (H 2048, 256 experts SwiGLU 2048->512->2048 + 1 shared, top-8 "
+                        "renormalised) + untied 248,320x2048 head with the 0.95 unmask rule",
+            "block_tokens": T, "hidden": H, "experts": L.E, "top_k": L.k, "inter": L.I,
+            "vocab": HS.V, "weight_sets_rotated": args.sets, "parallelism": "single GPU",
+        },
+        "moe_layer": {"us": round(moe_us, 2), "block_tokens_per_s": round(T / (moe_us * 1e-6), 1),
+                      "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
+                      "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4)},
+        "head_unmask": {"us": round(head_us, 2), "bytes": HEAD_BYTES, "GB_s": round(head_gbs, 1),
+                        "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
+        "rmsnorm_us": round(norm_us, 2),
+        "ms_per_step_with_events": round(ms_step, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(s, ntok):
+    """The CPU oracle (as it stands) on the first `ntok` tokens of one block:
+    the same step (RMSNorm, MoE layer, head + unmask) for those tokens only.
+    Scaled to block-tokens/s."""
+    import numpy as np
+
+    import synth
+    from oracle import head as ohead, moe as omoe, norm as onorm
+
+    inp, w_head, blk = s
+    h = synth.moe_host(inp, lazy=False)
+    xb = synth.bf16_bits(inp.x)[:ntok]
+    wh = synth.bf16_bits(w_head)
+    threads = _blas_threads()
+    t0 = time.perf_counter()
+    xn = onorm.rmsnorm(xb, 1e-6)
+    r = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                       h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)
+    ohead.head_unmask(r["y"], wh, blk.tokens.cpu().numpy()[:ntok], synth.HEAD.mask_id, 0.95)
+    dt = time.perf_counter() - t0
+    return {"value": round(ntok / dt, 4), "unit": "block-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{ntok} tokens of one 32-slot block through RMSNorm + MoE layer + head/"
+                      f"unmask (numpy float64 oracle), {dt:.1f} s; weights copied to host "
+                      f"before the timed region"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,19 @@
+"""MI355X-native (gfx950) kernels for one block-diffusion MoE denoise step.
+
+The computation lives in ``libbdmoe.so`` (hand-written HIP kernels behind a
+C ABI declared in ``include/bdmoe.h``); this package is its ctypes binding.
+Build the library with ``python -m block_diffusion_moe_amd.build``.
+"""
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+from .binding import (BDM_MASK_ID_CLOVER, BDM_THRESHOLD_DEFAULT, EXPORTS, LIB_PATH, BdmError,
+                      bdm_head_workspace_bytes, bdm_lm_head_unmask, bdm_moe_block_forward,
+                      bdm_moe_workspace_bytes, bdm_rmsnorm, bdm_status_string, bdm_version, load,
+                      workspace)
+
+__all__ = [
+    "BDM_MASK_ID_CLOVER", "BDM_THRESHOLD_DEFAULT", "EXPORTS", "LIB_PATH", "BdmError",
+    "bdm_head_workspace_bytes", "bdm_lm_head_unmask", "bdm_moe_block_forward",
+    "bdm_moe_workspace_bytes", "bdm_rmsnorm", "bdm_status_string", "bdm_version", "load",
+    "workspace",
+]

@@ -1,0 +1,185 @@
+"""ctypes binding of libbdmoe.so: the C entry points under the same names.
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape and contiguity and passed as raw device pointers together with the
+caller's current HIP stream; every step of the computation runs in the HIP
+kernels of the library.  A missing library raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdmoe.so")
+
+BDM_OK = 0
+BDM_MASK_ID_CLOVER = 151669
+BDM_THRESHOLD_DEFAULT = 0.95
+
+_c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "bdm_version": (_c_int, []),
+    "bdm_status_string": (ctypes.c_char_p, [_c_int]),
+    "bdm_moe_workspace_bytes": (_c_int, [_c_int] * 6 + [ctypes.POINTER(_c_size)]),
+    "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
+                                       _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _c_size, _vp]),
+    "bdm_head_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
+    "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, ctypes.c_int32, _c_float,
+                                    _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class BdmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {bdm_status_string(status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once).  torch is imported first so the library binds
+    to the HIP runtime torch uses."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m block_diffusion_moe_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape=None, device=None):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn: str, st: int):
+    if st != BDM_OK:
+        raise BdmError(fn, st)
+
+
+def bdm_version() -> int:
+    return load().bdm_version()
+
+
+def bdm_status_string(status: int) -> str:
+    return load().bdm_status_string(status).decode()
+
+
+def bdm_moe_workspace_bytes(T, H, I, E, k, has_shared) -> int:
+    n = _c_size(0)
+    _raise("bdm_moe_workspace_bytes", load().bdm_moe_workspace_bytes(T, H, I, E, k, int(has_shared),
+                                                                     ctypes.byref(n)))
+    return n.value
+
+
+def bdm_head_workspace_bytes(T, H, V) -> int:
+    n = _c_size(0)
+    _raise("bdm_head_workspace_bytes", load().bdm_head_workspace_bytes(T, H, V, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """Device scratch buffer (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+
+
+def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_bias=None,
+                          ws_gate=None, ws_up=None, ws_down=None, residual=None, y=None,
+                          topk_idx=None, topk_w=None, renorm: bool = True, ws=None, stream=None):
+    """y = MoE layer over the block x (see include/bdmoe.h).  ``y`` may be
+    ``residual`` (in-place residual add); a new tensor is made when None."""
+    T, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(w_router, "w_router", torch.float32, (E, H), dev)
+    _check(router_bias, "router_bias", torch.float32, (E,), dev)
+    _check(w_gate, "w_gate", torch.bfloat16, (E, I, H), dev)
+    _check(w_up, "w_up", torch.bfloat16, (E, I, H), dev)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), dev)
+    _check(ws_gate, "ws_gate", torch.bfloat16, (I, H), dev)
+    _check(ws_up, "ws_up", torch.bfloat16, (I, H), dev)
+    _check(ws_down, "ws_down", torch.bfloat16, (H, I), dev)
+    _check(residual, "residual", torch.bfloat16, (T, H), dev)
+    _check(y, "y", torch.bfloat16, (T, H), dev)
+    _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    has_shared = ws_gate is not None
+    need = bdm_moe_workspace_bytes(T, H, I, E, k, has_shared)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = load().bdm_moe_block_forward(
+        _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(residual),
+        _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream))
+    _raise("bdm_moe_block_forward", st)
+    return y
+
+
+def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool, tokens,
+                       argmax=None, conf=None, n_committed=None, ws=None, stream=None):
+    T, H = h.shape
+    V = w_head.shape[0]
+    dev = h.device
+    _check(h, "h", torch.bfloat16, (T, H))
+    _check(w_head, "w_head", torch.bfloat16, (V, H), dev)
+    _check(tokens, "tokens", torch.int32, (T,), dev)
+    _check(argmax, "argmax", torch.int32, (T,), dev)
+    _check(conf, "conf", torch.float32, (T,), dev)
+    _check(n_committed, "n_committed", torch.int32, (1,), dev)
+    need = bdm_head_workspace_bytes(T, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = load().bdm_lm_head_unmask(_ptr(h), T, H, _ptr(w_head), V, int(mask_id), float(threshold),
+                                   int(fallback), _ptr(tokens), _ptr(argmax), _ptr(conf),
+                                   _ptr(n_committed), _ptr(ws), ws.numel(), _stream(stream))
+    _raise("bdm_lm_head_unmask", st)
+    return tokens
+
+
+def bdm_rmsnorm(x, out, gamma=None, eps: float = 1e-6, stream=None):
+    T, H = x.shape
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(out, "out", torch.bfloat16, (T, H), x.device)
+    _check(gamma, "gamma", torch.float32, (H,), x.device)
+    st = load().bdm_rmsnorm(_ptr(x), _ptr(gamma), float(eps), T, H, _ptr(out), _stream(stream))
+    _raise("bdm_rmsnorm", st)
+    return out

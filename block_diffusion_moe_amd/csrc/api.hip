@@ -1,0 +1,195 @@
+// extern "C" entry points of libbdmoe: argument validation, workspace
+// carve-up and the launch sequence.  Declarations and contracts are in
+// include/bdmoe.h.  Nothing here allocates memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "bdmoe.h"
+#include "internal.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_moe_shape(int T, int H, int I, int E, int k, int has_shared) {
+  if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return BDM_ERR_INVALID_ARG;
+  if (has_shared != 0 && has_shared != 1) return BDM_ERR_INVALID_ARG;
+  if (T > BDM_MAX_TOKENS || H > BDM_MAX_HIDDEN || H % 64 != 0 || I > BDM_MAX_INTER ||
+      I % 32 != 0 || E > BDM_MAX_EXPERTS || k > BDM_MAX_TOPK)
+    return BDM_ERR_UNSUPPORTED_SHAPE;
+  if (static_cast<long>(E) * ((T + 31) / 32) > 8192) return BDM_ERR_UNSUPPORTED_SHAPE;
+  return BDM_OK;
+}
+
+// Workspace layout of the MoE layer.  Returns total bytes; fills `m` when
+// `base` is given.
+size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
+                  bdm::MoeMeta* m) {
+  const size_t P = static_cast<size_t>(T) * k + (has_shared ? T : 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  char* logits = take(sizeof(float) * T * E);
+  char* topk_idx = take(sizeof(int32_t) * T * k);
+  char* topk_w = take(sizeof(float) * T * k);
+  char* info = take(sizeof(int32_t) * 4);
+  char* offs = take(sizeof(int32_t) * (E + 2));
+  char* touched = take(sizeof(int32_t) * (E + 1));
+  char* pair_token = take(sizeof(int32_t) * P);
+  char* pos = take(sizeof(int32_t) * T * (k + 1));
+  char* act = take(sizeof(uint16_t) * P * I);
+  char* ypair = take(sizeof(float) * P * H);
+  if (m) {
+    m->logits = reinterpret_cast<float*>(logits);
+    m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
+    m->topk_w = reinterpret_cast<float*>(topk_w);
+    m->info = reinterpret_cast<int32_t*>(info);
+    m->offs = reinterpret_cast<int32_t*>(offs);
+    m->touched = reinterpret_cast<int32_t*>(touched);
+    m->pair_token = reinterpret_cast<int32_t*>(pair_token);
+    m->pos = reinterpret_cast<int32_t*>(pos);
+    m->act = reinterpret_cast<uint16_t*>(act);
+    m->ypair = reinterpret_cast<float*>(ypair);
+  }
+  return off;
+}
+
+int check_head_shape(int T, int H, int V) {
+  if (T < 1 || H < 1 || V < 2) return BDM_ERR_INVALID_ARG;
+  if (T > BDM_MAX_TOKENS || H > BDM_MAX_HIDDEN || H % 64 != 0) return BDM_ERR_UNSUPPORTED_SHAPE;
+  return BDM_OK;
+}
+
+size_t head_layout(int T, int V, char* base, bdm::HeadParts* p) {
+  const int ntiles = (V + bdm::kHeadTileRows - 1) / bdm::kHeadTileRows;
+  const size_t n = static_cast<size_t>(T) * ntiles;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  char* m = take(sizeof(float) * n);
+  char* s = take(sizeof(float) * n);
+  char* a = take(sizeof(int32_t) * n);
+  if (p) {
+    p->m = reinterpret_cast<float*>(m);
+    p->s = reinterpret_cast<float*>(s);
+    p->a = reinterpret_cast<int32_t*>(a);
+  }
+  return off;
+}
+
+int last_hip_status() {
+  return hipGetLastError() == hipSuccess ? BDM_OK : BDM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdm_version(void) { return 100; }
+
+const char* bdm_status_string(int status) {
+  switch (status) {
+    case BDM_OK: return "ok";
+    case BDM_ERR_INVALID_ARG: return "invalid argument";
+    case BDM_ERR_UNSUPPORTED_SHAPE: return "shape outside the supported limits";
+    case BDM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case BDM_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_shared, size_t* bytes) {
+  if (!bytes) return BDM_ERR_INVALID_ARG;
+  const int st = check_moe_shape(T, H, I, E, k, has_shared);
+  if (st != BDM_OK) return st;
+  *bytes = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
+  return BDM_OK;
+}
+
+int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router,
+                          const float* router_bias, int E, int k, int renorm,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int I, const uint16_t* ws_gate, const uint16_t* ws_up,
+                          const uint16_t* ws_down, const uint16_t* residual, uint16_t* y,
+                          int32_t* topk_idx, float* topk_w, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
+    return BDM_ERR_INVALID_ARG;
+  const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
+  if (nshared != 0 && nshared != 3) return BDM_ERR_INVALID_ARG;
+  if (renorm != 0 && renorm != 1) return BDM_ERR_INVALID_ARG;
+  const int has_shared = nshared == 3 ? 1 : 0;
+  int st = check_moe_shape(T, H, I, E, k, has_shared);
+  if (st != BDM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(y) || (residual && !aligned16(residual)) ||
+      (has_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down))) ||
+      (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return BDM_ERR_INVALID_ARG;
+  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return BDM_ERR_INVALID_ARG;
+  const size_t need = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
+  if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
+
+  bdm::MoeMeta meta;
+  moe_layout(T, H, I, E, k, has_shared, static_cast<char*>(workspace), &meta);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, meta, topk_idx,
+                     topk_w, s);
+  bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, residual, y, meta, s);
+  return last_hip_status();
+}
+
+int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {
+  if (!bytes) return BDM_ERR_INVALID_ARG;
+  const int st = check_head_shape(T, H, V);
+  if (st != BDM_OK) return st;
+  *bytes = head_layout(T, V, nullptr, nullptr);
+  return BDM_OK;
+}
+
+int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
+                       int32_t mask_id, float threshold, int fallback, int32_t* tokens,
+                       int32_t* argmax, float* conf, int32_t* n_committed, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!h || !w_head || !tokens || !workspace) return BDM_ERR_INVALID_ARG;
+  int st = check_head_shape(T, H, V);
+  if (st != BDM_OK) return st;
+  if (mask_id < 0 || mask_id >= V) return BDM_ERR_INVALID_ARG;
+  if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
+    return BDM_ERR_INVALID_ARG;
+  if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_head) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return BDM_ERR_INVALID_ARG;
+  const size_t need = head_layout(T, V, nullptr, nullptr);
+  if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
+  bdm::HeadParts parts;
+  head_layout(T, V, static_cast<char*>(workspace), &parts);
+  (void)hipGetLastError();
+  bdm::launch_head(h, T, H, w_head, V, mask_id, threshold, fallback, tokens, argmax, conf,
+                   n_committed, parts, static_cast<hipStream_t>(stream));
+  return last_hip_status();
+}
+
+int bdm_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H, uint16_t* out,
+                void* stream) {
+  if (!x || !out || T < 1 || H < 1) return BDM_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps == INFINITY) return BDM_ERR_INVALID_ARG;
+  if (H % 64 != 0 || H > BDM_MAX_HIDDEN) return BDM_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return BDM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  bdm::launch_rmsnorm(x, gamma, eps, T, H, out, static_cast<hipStream_t>(stream));
+  return last_hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+/*
+ * bdmoe.h -- C ABI of the block-diffusion MoE denoise-step library (libbdmoe.so)
+ *
+ * One denoising step of a block-diffusion mixture-of-experts language model
+ * shaped like Clover-35B-A3B, on one AMD Instinct MI355X (gfx950): the routed
+ * MoE feed-forward layer applied to a whole block of positions at once, the
+ * RMSNorm between layers, and the untied output head fused with the
+ * low-confidence unmask rule.
+ *
+ * Pages cited (title, then section):
+ *   [files]  "Clover-35B-A3B: how a diffusion model gets to 680 tokens a
+ *            second, read from its files"
+ *   [deep]   "Deep Dive -- Clover 35B: a diffusion LLM at Qwen parity, 680 tok/s"
+ *
+ * Conventions shared by every entry point
+ *   - Pointers to tensors are DEVICE pointers (HBM of the current HIP device)
+ *     unless stated otherwise.  bf16 tensors are passed as uint16_t bit
+ *     patterns.  All tensors are dense row-major with the last dimension
+ *     contiguous; no strides.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     only enqueue kernels on it and return; they never synchronise.  Outputs
+ *     are valid once the stream has reached the enqueued work.
+ *   - Ownership: the caller owns every buffer, before, during and after the
+ *     call.  The library allocates no device or host memory and keeps no state
+ *     besides a per-device cache of device properties.
+ *   - Workspace: device scratch of at least the size returned by the matching
+ *     *_workspace_bytes query, 256-byte aligned.  Its contents on entry are
+ *     ignored; on return it holds intermediate results (undefined to callers).
+ *     Two calls that run concurrently need two workspaces.
+ *   - Errors: 0 on success, otherwise a negative BDM_ERR_* code.  All argument
+ *     checks run before anything is enqueued, so a failed check leaves every
+ *     output untouched.  BDM_ERR_HIP means a launch failed after validation
+ *     (outputs then undefined).  The library never aborts or prints.
+ *   - Repeatability: identical inputs give bitwise-identical outputs (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - Thread safety: calls on different streams may be issued from different
+ *     host threads as long as their workspaces and outputs are distinct.
+ */
+#ifndef BDMOE_H
+#define BDMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define BDM_API __attribute__((visibility("default")))
+#else
+#define BDM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BDM_OK                       0
+#define BDM_ERR_INVALID_ARG         -1  /* null pointer, bad size, bad flag */
+#define BDM_ERR_UNSUPPORTED_SHAPE   -2  /* legal sizes outside the kernels' limits */
+#define BDM_ERR_WORKSPACE_TOO_SMALL -3
+#define BDM_ERR_HIP                 -4  /* a HIP call failed */
+
+/* [files] "What Clover is": mask_token_id 151669, low_confidence threshold 0.95 */
+#define BDM_MASK_ID_CLOVER     151669
+#define BDM_THRESHOLD_DEFAULT  0.95f
+
+/* Limits of this implementation (checked; BDM_ERR_UNSUPPORTED_SHAPE beyond). */
+#define BDM_MAX_TOKENS   1024   /* T: positions per call (several blocks may be stacked) */
+#define BDM_MAX_HIDDEN   2048   /* H, multiple of 64 */
+#define BDM_MAX_INTER    1024   /* I, multiple of 32 */
+#define BDM_MAX_EXPERTS  1024   /* E */
+#define BDM_MAX_TOPK       16   /* k, 1 <= k <= E */
+
+/* Library version as 10000*major + 100*minor + patch. */
+BDM_API int bdm_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+BDM_API const char* bdm_status_string(int status);
+
+/*
+ * bdm_moe_workspace_bytes -- workspace size for bdm_moe_block_forward.
+ *   T, H, I, E, k, has_shared: as in bdm_moe_block_forward.
+ *   bytes: HOST pointer that receives the size.
+ * Returns BDM_OK, or the same validation error bdm_moe_block_forward would
+ * return for these sizes.  Pure host arithmetic; needs no GPU.
+ */
+BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_shared, size_t* bytes);
+
+/*
+ * bdm_moe_block_forward -- one routed MoE feed-forward layer over a block.
+ *
+ * [files] "What Clover is": every layer has 256 routed experts, routes each
+ * token to 8 of them and adds one shared expert that is always on; an expert
+ * is gate and up at 2,048 by 512 and down at 512 by 2,048.  [deep] "What
+ * DiffuSpace actually shipped": top-8 routing plus one shared expert per
+ * layer.  [files] "The expert selection": a block of 32 tokens reads the
+ * union of the tokens' expert sets, so the layer is computed per expert over
+ * all the block's tokens routed to it.
+ *
+ * For every token t (row of x), independently:
+ *   l      = fp32(x_t) . w_router^T (+ router_bias)             fp32 logits [E]
+ *   S_t    = the k experts with the largest l (equal: lower id first),
+ *            ordered by decreasing l
+ *   w_t,j  = softmax(l)[S_j] / sum_{i in S} softmax(l)[i]   if renorm
+ *          = softmax(l)[S_j]                                 otherwise
+ *   Y_e(x) = W_down,e . bf16( silu(W_gate,e . x) * (W_up,e . x) ),
+ *            silu(z) = z / (1 + e^-z), fp32 accumulation
+ *   y_t    = bf16( residual_t + sum_{j<k} w_t,j Y_{S_j}(x_t) + Y_shared(x_t) )
+ *            summed in fp32 in that order (residual 0 when NULL; the shared
+ *            term only when the ws_* trio is given)
+ *
+ * Arguments
+ *   x            [T][H] bf16        block activations (T tokens)
+ *   w_router     [E][H] fp32        router weights
+ *   router_bias  [E] fp32 or NULL   added to the logits before softmax/top-k
+ *   E, k         experts, experts per token (1 <= k <= min(E, 16))
+ *   renorm       1: renormalise the k weights to sum to 1; 0: raw softmax
+ *   w_gate,w_up  [E][I][H] bf16     routed experts, output-major
+ *   w_down       [E][H][I] bf16
+ *   I            expert intermediate size (multiple of 32, <= 1024)
+ *   ws_gate, ws_up [I][H], ws_down [H][I] bf16: the shared expert; all three
+ *                NULL = no shared expert (mixing NULL and non-NULL is an error)
+ *   residual     [T][H] bf16 or NULL; may be the same pointer as y
+ *   y            [T][H] bf16        output
+ *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
+ *   topk_w       [T][k] fp32 or NULL    receives w_t
+ *   workspace, workspace_bytes: see bdm_moe_workspace_bytes
+ * Limits: T <= 1024, H multiple of 64 and <= 2048, E <= 1024, and
+ *   E * ceil(T/32) <= 8192 (the routing bitmap lives in on-chip memory).
+ *   Pointers 16-byte aligned (workspace 256-byte aligned).  NaN inputs give
+ *   undefined values, never an out-of-bounds access.
+ * No other aliasing is allowed.
+ */
+BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
+                          const float* w_router, const float* router_bias, int E, int k,
+                          int renorm,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int I,
+                          const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                          const uint16_t* residual, uint16_t* y,
+                          int32_t* topk_idx, float* topk_w,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bdm_head_workspace_bytes -- workspace size for bdm_lm_head_unmask.
+ *   bytes: HOST pointer.  Pure host arithmetic.
+ */
+BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
+
+/*
+ * bdm_lm_head_unmask -- untied output head fused with the unmask rule.
+ *
+ * [files] "What Clover is": the output head (508,559,360 = 248,320 x 2,048
+ * parameters) is untied from the embedding and read in full at every step.
+ * [files] "How it writes", steps 2-3: for every slot take the most likely
+ * token and its probability, with the mask token's logit set to minus
+ * infinity first; commit every still-masked slot whose probability clears
+ * the threshold; if none clears it, commit the single most confident one.
+ *
+ *   l_t     = fp32 logits h_t . w_head^T for all V rows (never stored)
+ *   l_t[mask_id] = -inf
+ *   argmax_t = argmax_v l_t (equal logits: lowest id)
+ *   conf_t   = max_v softmax(l_t) = 1 / sum_v exp(l_t,v - max l_t)
+ *   rule: for every t with tokens[t] == mask_id: commit (tokens[t] =
+ *         argmax_t) iff conf_t >= threshold.  If fallback != 0 and no row
+ *         committed but some row is masked, commit the masked row with the
+ *         largest conf_t (equal: lowest t).  Other rows are never changed.
+ *
+ * Arguments
+ *   h            [T][H] bf16        final hidden states of the block
+ *   w_head       [V][H] bf16        output head, vocabulary-row-major
+ *   mask_id      0 <= mask_id < V   (V >= 2)
+ *   threshold    commit threshold (finite, compared with >=)
+ *   fallback     1: the progress rule above; 0: threshold only
+ *   tokens       [T] int32          in/out: current block contents
+ *   argmax       [T] int32 or NULL  receives argmax_t for every row
+ *   conf         [T] fp32 or NULL   receives conf_t for every row
+ *   n_committed  DEVICE int32* or NULL: number of rows committed by this call
+ * Limits: T <= 1024, H multiple of 64 and <= 2048 (V unrestricted above 2).
+ */
+BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
+                       int32_t mask_id, float threshold, int fallback,
+                       int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bdm_rmsnorm -- RMSNorm of each row, between MoE layers of a pre-norm stack.
+ *   out_t = bf16( x_t / sqrt(mean(x_t^2) + eps) * gamma ), fp32 arithmetic.
+ * The pages name no normalisation; this is the per-layer pre-norm of the
+ * 40-layer stack workload (eps 1e-6, unit gamma).
+ *   x [T][H] bf16, gamma [H] fp32 or NULL (= all ones), out [T][H] bf16
+ *   (out may equal x).  H multiple of 64 and <= 2048; any T >= 1 (one
+ *   workgroup per row).  Pointers 16-byte aligned.
+ */
+BDM_API int bdm_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H, uint16_t* out,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDMOE_H */

@@ -1,0 +1,138 @@
+"""The C-ABI library loads and exports every symbol include/bdmoe.h declares;
+host-side workspace arithmetic and argument validation (CPU only: no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdmoe.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"BDM_API\s+[\w\s\*]+?\b(bdm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_diffusion_moe_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libbdmoe.so not built (python -m block_diffusion_moe_amd.build)")
+    return binding.load()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    assert syms == sorted(["bdm_version", "bdm_status_string", "bdm_moe_workspace_bytes",
+                           "bdm_moe_block_forward", "bdm_head_workspace_bytes",
+                           "bdm_lm_head_unmask", "bdm_rmsnorm"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from block_diffusion_moe_amd import binding
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert sorted(binding.EXPORTS) == declared_symbols()
+    assert lib.bdm_version() >= 100
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.bdm_status_string(st), bytes)
+
+
+def test_library_is_gfx950_code_object():
+    from block_diffusion_moe_amd import binding
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_moe_workspace_bytes(lib):
+    from block_diffusion_moe_amd import binding as b
+    n = b.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, True)
+    P = 32 * 9
+    # expert outputs [P][H] fp32 and activations [P][I] bf16 dominate
+    assert n >= P * 2048 * 4 + P * 512 * 2 + 32 * 256 * 4
+    assert n % 256 == 0
+    assert b.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, False) < n
+    size = ctypes.c_size_t(0)
+    assert lib.bdm_moe_workspace_bytes(0, 2048, 512, 256, 8, 1, ctypes.byref(size)) == -1
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 9999, 1, ctypes.byref(size)) == -1
+    assert lib.bdm_moe_workspace_bytes(32, 2047, 512, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(32, 4096, 512, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 500, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(2048, 2048, 512, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 17, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 2, ctypes.byref(size)) == -1
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 1, None) == -1
+
+
+def test_head_workspace_bytes(lib):
+    from block_diffusion_moe_amd import binding as b
+    n = b.bdm_head_workspace_bytes(32, 2048, 248320)
+    assert n >= 32 * 970 * 12
+    size = ctypes.c_size_t(0)
+    assert lib.bdm_head_workspace_bytes(32, 2048, 1, ctypes.byref(size)) == -1
+    assert lib.bdm_head_workspace_bytes(32, 2000, 512, ctypes.byref(size)) == -2
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_moe_validation_rejects_before_launch(lib):
+    """Bad arguments return an error code without touching the device (the
+    pointers below are never dereferenced)."""
+    A = _fake(1 << 20)        # 16-byte aligned fake address
+    size = 1 << 30
+    good = dict(x=A, T=32, H=2048, wr=A, bias=None, E=256, k=8, renorm=1, wg=A, wu=A, wd=A,
+                I=512, sg=A, su=A, sd=A, res=None, y=_fake(2 << 20), idx=None, w=None,
+                ws=_fake(1 << 24), wsb=size, stream=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return lib.bdm_moe_block_forward(a["x"], a["T"], a["H"], a["wr"], a["bias"], a["E"],
+                                         a["k"], a["renorm"], a["wg"], a["wu"], a["wd"], a["I"],
+                                         a["sg"], a["su"], a["sd"], a["res"], a["y"], a["idx"],
+                                         a["w"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(ws=None) == -1
+    assert call(sd=None) == -1                    # shared trio must be all or none
+    assert call(renorm=2) == -1
+    assert call(k=0) == -1
+    assert call(k=300) == -1
+    assert call(H=100) == -2
+    assert call(I=48) == -2
+    assert call(x=_fake((1 << 20) + 2)) == -1     # misaligned
+    assert call(ws=_fake((1 << 24) + 16)) == -1   # workspace not 256-aligned
+    assert call(y=A) == -1                        # y aliases x
+    assert call(wsb=1024) == -3
+
+
+def test_head_and_rmsnorm_validation(lib):
+    A = _fake(1 << 20)
+    T = ctypes.c_void_p(3 << 20)
+    W = _fake(1 << 24)
+
+    def head(**kw):
+        a = dict(h=A, T=32, H=2048, w=A, V=248320, mask=151669, thr=0.95, fb=1, tok=T,
+                 am=None, cf=None, nc=None, ws=W, wsb=1 << 30, st=None)
+        a.update(kw)
+        return lib.bdm_lm_head_unmask(a["h"], a["T"], a["H"], a["w"], a["V"], a["mask"], a["thr"],
+                                      a["fb"], a["tok"], a["am"], a["cf"], a["nc"], a["ws"],
+                                      a["wsb"], a["st"])
+
+    assert head(h=None) == -1
+    assert head(tok=None) == -1
+    assert head(mask=248320) == -1
+    assert head(mask=-1) == -1
+    assert head(thr=float("nan")) == -1
+    assert head(fb=3) == -1
+    assert head(T=0) == -1
+    assert head(T=4096) == -2
+    assert head(wsb=16) == -3
+    assert lib.bdm_rmsnorm(None, None, 1e-6, 32, 2048, A, None) == -1
+    assert lib.bdm_rmsnorm(A, None, -1.0, 32, 2048, A, None) == -1
+    assert lib.bdm_rmsnorm(A, None, 1e-6, 32, 100, A, None) == -2

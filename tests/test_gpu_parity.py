@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case feeds the same seeded tensors to both sides.  Bar: top-k expert
+indices and unmask decisions bit-exact (tokens whose k-th/(k+1)-th router
+logit gap, or rows whose top-2 logit gap or distance to the threshold, is
+below 1e-4 are excluded from the integer comparison); bf16 outputs within
+1e-2 absolute + 2e-2 relative of the oracle; fp32 weights and confidences
+within 2e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import norm as onorm
+from tests.conftest import gpu_available
+from tests.gpu_common import (assert_bf16_close, compare_head, compare_moe, oracle_head,
+                              oracle_moe, run_head, run_moe, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def bdm():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_diffusion_moe_amd as b
+    b.load()
+    return b
+
+
+# --------------------------------------------------------------------------
+# MoE layer
+# --------------------------------------------------------------------------
+
+def _to_dev(inp: synth.MoEInputs) -> synth.MoEInputs:
+    f = lambda t: None if t is None else t.to(DEV)  # noqa: E731
+    return synth.MoEInputs(inp.shape, f(inp.x), f(inp.w_router), f(inp.router_bias),
+                           f(inp.w_gate), f(inp.w_up), f(inp.w_down), f(inp.ws_gate),
+                           f(inp.ws_up), f(inp.ws_down), f(inp.residual))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", ["plain", "residual", "noshared", "norenorm", "bias"])
+def test_moe_tiny(bdm, seed, variant):
+    say(f"case moe tiny seed={seed} variant={variant}")
+    inp = _to_dev(synth.moe_inputs(synth.TINY, seed=seed, block_seed=seed + 1,
+                                   with_residual=variant == "residual",
+                                   zipf_s=1.1 if variant == "bias" else None))
+    kw = dict(renorm=variant != "norenorm", shared=variant != "noshared")
+    y, idx, w = run_moe(bdm, inp, **kw)
+    o = oracle_moe(inp, **kw)
+    compare_moe(y, idx, w, o)
+
+
+# (T, H, E, I, k): ragged token counts, several tiles, k = 1 and k = 16,
+# hidden sizes that leave some of the four K-slice waves empty
+SHAPES = [
+    (1, 64, 16, 32, 2),
+    (5, 128, 8, 64, 8),
+    (17, 256, 64, 96, 4),
+    (33, 192, 32, 32, 1),
+    (40, 512, 128, 128, 16),
+    (64, 2048, 256, 512, 8),
+    (100, 1024, 64, 1024, 2),
+    (7, 2048, 1024, 64, 3),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "T%d_H%d_E%d_I%d_k%d" % s)
+def test_moe_shapes(bdm, shape):
+    T, H, E, I, k = shape
+    say(f"case moe shape T={T} H={H} E={E} I={I} k={k}")
+    s = synth.MoEShape(T=T, H=H, E=E, I=I, k=k)
+    inp = synth.moe_inputs(s, seed=T + E, block_seed=k, device=DEV, with_residual=True)
+    y, idx, w = run_moe(bdm, inp)
+    o = oracle_moe(inp, lazy=True)
+    compare_moe(y, idx, w, o)
+
+
+def test_moe_clover_layer_full(bdm):
+    """One Clover-shaped layer (H 2048, 256 experts, I 512, top-8, shared),
+    32-token block, every output element against the oracle."""
+    say("case moe clover layer T=32 full")
+    inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=1, device=DEV, with_residual=True)
+    y, idx, w = run_moe(bdm, inp)
+    o = oracle_moe(inp, lazy=True)
+    say(f"  touched experts: {o['touched']}")
+    compare_moe(y, idx, w, o)
+
+
+def test_moe_clover_layer_inplace_residual(bdm):
+    """residual == y (the stack's in-place residual add) gives the same bits
+    as a separate output buffer."""
+    say("case moe clover layer in-place residual")
+    inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=2, device=DEV, with_residual=True)
+    y_sep, _, _ = run_moe(bdm, inp)
+    buf = inp.residual.clone()
+    bdm.bdm_moe_block_forward(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, 8,
+                              ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
+                              residual=buf, y=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.view(torch.int16), y_sep.view(torch.int16))
+
+
+def test_moe_skew_sampled(bdm):
+    """Eight 32-token blocks (T = 256) with the log-Zipf router offset: the
+    routing of every token, and the outputs of a seeded sample of 24 tokens
+    (tokens are independent through the layer)."""
+    say("case moe skew T=256 sampled")
+    inp = synth.skew_inputs(seed=0, block_seed=1, device=DEV)
+    y, idx, w = run_moe(bdm, inp, residual=False)
+    tokens = np.sort(np.random.default_rng(0).choice(256, 24, replace=False))
+    o = oracle_moe(inp, residual=False, tokens=tokens, lazy=True)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=256)
+    say(f"  touched {int((counts > 0).sum())} experts, busiest {int(counts.max())} tokens")
+    compare_moe(y, idx, w, o, tokens=tokens)
+
+
+def test_moe_repeatable_bitwise(bdm):
+    say("case moe repeatability")
+    inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=3, device=DEV, with_residual=True)
+    outs = [run_moe(bdm, inp) for _ in range(3)]
+    for y, idx, w in outs[1:]:
+        assert torch.equal(y.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(idx, outs[0][1])
+        assert torch.equal(w.view(torch.int32), outs[0][2].view(torch.int32))
+
+
+def test_moe_workspace_poison_independent(bdm):
+    """Results do not depend on what the workspace held before the call."""
+    say("case moe workspace poison")
+    inp = synth.moe_inputs(synth.MoEShape(48, 512, 64, 128, 4), seed=5, device=DEV)
+    s = inp.shape
+    n = bdm.bdm_moe_workspace_bytes(s.T, s.H, s.I, s.E, s.k, True)
+    outs = []
+    for fill in (0x00, 0xFF, 0x7F):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=DEV)
+        y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=DEV)
+        bdm.bdm_moe_block_forward(inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+                                  ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
+                                  y=y, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(y)
+    assert all(torch.equal(o.view(torch.int16), outs[0].view(torch.int16)) for o in outs)
+
+
+def test_uniform_router_ties_on_gpu(bdm):
+    """All-zero router: every logit ties, the picks are experts 0..k-1 with
+    weight 1/k (the tie rule, bit-exact)."""
+    say("case moe uniform router")
+    inp = synth.moe_inputs(synth.MoEShape(16, 256, 32, 64, 4), seed=9, device=DEV)
+    inp.w_router.zero_()
+    y, idx, w = run_moe(bdm, inp, residual=False)
+    assert torch.equal(idx.cpu(), torch.arange(4, dtype=torch.int32).repeat(16, 1))
+    assert torch.all(w == 0.25)
+    o = oracle_moe(inp, residual=False)
+    assert_bf16_close(y, o["y"])
+
+
+# --------------------------------------------------------------------------
+# Head + unmask
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("variant", ["plain", "committed", "maskboost", "all_boosted"])
+def test_head_tiny(bdm, seed, variant):
+    say(f"case head tiny seed={seed} variant={variant}")
+    s = synth.TINY_HEAD
+    W = synth.head_weights(s, seed).to(DEV)
+    blk = synth.head_block(s, W, block_seed=seed + 1, n_boost=3,
+                           committed_rows=3 if variant == "committed" else 0,
+                           mask_boost_rows=2 if variant == "maskboost" else 0,
+                           boost_all=variant == "all_boosted")
+    out = run_head(bdm, blk)
+    o = oracle_head(blk)
+    compare_head(out, o, blk.tokens.cpu().numpy())
+
+
+@pytest.mark.parametrize("V,T", [(2, 3), (17, 5), (1000, 33), (4097, 40), (70001, 64)])
+def test_head_ragged(bdm, V, T):
+    say(f"case head ragged V={V} T={T}")
+    s = synth.HeadShape(T=T, H=256, V=V, mask_id=V // 3)
+    W = synth.head_weights(s, V).to(DEV)
+    blk = synth.head_block(s, W, block_seed=T, n_boost=min(T, 4), committed_rows=1)
+    out = run_head(bdm, blk)
+    o = oracle_head(blk)
+    compare_head(out, o, blk.tokens.cpu().numpy())
+
+
+def test_head_clover_full(bdm):
+    """Untied 248,320 x 2048 head, 32 positions, 10 boosted rows (+20) among
+    flat ones: every row's argmax/conf and the commit decisions."""
+    say("case head clover full")
+    s = synth.HEAD
+    W = synth.head_weights(s, 0, device=DEV)
+    blk = synth.head_block(s, W, block_seed=1, n_boost=10)
+    out = run_head(bdm, blk)
+    o = oracle_head(blk)
+    assert o["n_committed"] == 10
+    compare_head(out, o, blk.tokens.cpu().numpy())
+    # a second block: rows already committed, the mask token boosted in two rows
+    blk2 = synth.head_block(s, W, block_seed=2, n_boost=10, committed_rows=5, mask_boost_rows=2)
+    out2 = run_head(bdm, blk2)
+    compare_head(out2, oracle_head(blk2), blk2.tokens.cpu().numpy())
+
+
+def test_head_clover_fallback(bdm):
+    """Every row boosted by only +12 over 248,319 flat competitors: no row
+    reaches 0.95, so exactly one row (the most confident) commits."""
+    say("case head clover fallback")
+    s = synth.HEAD
+    W = synth.head_weights(s, 0, device=DEV)
+    blk = synth.head_block(s, W, block_seed=4, boost=12.0, boost_all=True)
+    out = run_head(bdm, blk)
+    o = oracle_head(blk)
+    assert o["n_committed"] == 1
+    compare_head(out, o, blk.tokens.cpu().numpy())
+    out_nf = run_head(bdm, blk, fallback=False)
+    assert int(out_nf[3].item()) == 0
+    assert torch.equal(out_nf[0].cpu(), blk.tokens.cpu())
+
+
+def test_head_repeatable_bitwise(bdm):
+    say("case head repeatability")
+    s = synth.HeadShape(T=32, H=2048, V=65536, mask_id=3)
+    W = synth.head_weights(s, 1, device=DEV)
+    blk = synth.head_block(s, W, block_seed=7, n_boost=10)
+    a = run_head(bdm, blk)
+    b = run_head(bdm, blk)
+    for x, z in zip(a, b):
+        assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+
+
+# --------------------------------------------------------------------------
+# RMSNorm
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H", [(1, 64), (32, 2048), (37, 704)])
+def test_rmsnorm(bdm, T, H):
+    say(f"case rmsnorm T={T} H={H}")
+    g = torch.Generator(device=DEV).manual_seed(T * H)
+    x = (torch.randn(T, H, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    out = torch.empty_like(x)
+    bdm.bdm_rmsnorm(x, out, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = onorm.rmsnorm(synth.bf16_bits(x), 1e-6)
+    exact = assert_bf16_close(out, ref, what="rmsnorm")
+    assert exact > 0.98
+    bdm.bdm_rmsnorm(x, x, eps=1e-6)            # in place
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), out.view(torch.int16))
