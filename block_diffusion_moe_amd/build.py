@@ -42,10 +42,13 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, out: str = LIB) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out`.  `defines` are extra -D macros (kernel
+    tuning knobs such as BDM_HEAD_UNROLL); the defaults are the tuned ones."""
     srcs = sources()
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], f"-I{INCLUDE}", f"-I{CSRC}", *srcs,
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     with tempfile.TemporaryDirectory() as td:

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "bdmoe.h"
 #include "internal.hpp"
 
@@ -20,7 +22,6 @@ int check_moe_shape(int T, int H, int I, int E, int k, int has_shared) {
   if (T > BDM_MAX_TOKENS || H > BDM_MAX_HIDDEN || H % 64 != 0 || I > BDM_MAX_INTER ||
       I % 32 != 0 || E > BDM_MAX_EXPERTS || k > BDM_MAX_TOPK)
     return BDM_ERR_UNSUPPORTED_SHAPE;
-  if (static_cast<long>(E) * ((T + 31) / 32) > 8192) return BDM_ERR_UNSUPPORTED_SHAPE;
   return BDM_OK;
 }
 
@@ -28,7 +29,8 @@ int check_moe_shape(int T, int H, int I, int E, int k, int has_shared) {
 // `base` is given.
 size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
                   bdm::MoeMeta* m) {
-  const size_t P = static_cast<size_t>(T) * k + (has_shared ? T : 0);
+  const size_t P = static_cast<size_t>(T) * (k + 1);
+  (void)has_shared;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -39,10 +41,7 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
   char* topk_idx = take(sizeof(int32_t) * T * k);
   char* topk_w = take(sizeof(float) * T * k);
   char* info = take(sizeof(int32_t) * 4);
-  char* offs = take(sizeof(int32_t) * (E + 2));
   char* touched = take(sizeof(int32_t) * (E + 1));
-  char* pair_token = take(sizeof(int32_t) * P);
-  char* pos = take(sizeof(int32_t) * T * (k + 1));
   char* act = take(sizeof(uint16_t) * P * I);
   char* ypair = take(sizeof(float) * P * H);
   if (m) {
@@ -50,10 +49,7 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
     m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
     m->topk_w = reinterpret_cast<float*>(topk_w);
     m->info = reinterpret_cast<int32_t*>(info);
-    m->offs = reinterpret_cast<int32_t*>(offs);
     m->touched = reinterpret_cast<int32_t*>(touched);
-    m->pair_token = reinterpret_cast<int32_t*>(pair_token);
-    m->pos = reinterpret_cast<int32_t*>(pos);
     m->act = reinterpret_cast<uint16_t*>(act);
     m->ypair = reinterpret_cast<float*>(ypair);
   }
@@ -66,9 +62,10 @@ int check_head_shape(int T, int H, int V) {
   return BDM_OK;
 }
 
-size_t head_layout(int T, int V, char* base, bdm::HeadParts* p) {
-  const int ntiles = (V + bdm::kHeadTileRows - 1) / bdm::kHeadTileRows;
-  const size_t n = static_cast<size_t>(T) * ntiles;
+constexpr int kHeadMaxGrid = 1024;   // partials per token are sized for this many workgroups
+
+size_t head_layout(int T, char* base, bdm::HeadParts* p) {
+  const size_t n = static_cast<size_t>(T) * kHeadMaxGrid;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -84,6 +81,28 @@ size_t head_layout(int T, int V, char* base, bdm::HeadParts* p) {
     p->a = reinterpret_cast<int32_t*>(a);
   }
   return off;
+}
+
+// Per-device cache: compute-unit count and one-time kernel set-up.  Filled on
+// the first call made with that device current; -1 marks a failed set-up.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_setup(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BDM_ERR_HIP;
+  int n = g_cu_count[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0 || bdm::head_prepare() != 0)
+      v = -1;
+    g_cu_count[dev].store(v, std::memory_order_release);
+    n = v;
+  }
+  if (n < 0) return BDM_ERR_HIP;
+  *cus = n;
+  return BDM_OK;
 }
 
 int last_hip_status() {
@@ -154,7 +173,7 @@ int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {
   if (!bytes) return BDM_ERR_INVALID_ARG;
   const int st = check_head_shape(T, H, V);
   if (st != BDM_OK) return st;
-  *bytes = head_layout(T, V, nullptr, nullptr);
+  *bytes = head_layout(T, nullptr, nullptr);
   return BDM_OK;
 }
 
@@ -171,10 +190,14 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(w_head) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return BDM_ERR_INVALID_ARG;
-  const size_t need = head_layout(T, V, nullptr, nullptr);
+  const size_t need = head_layout(T, nullptr, nullptr);
   if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
+  int cus = 0;
+  st = device_setup(&cus);
+  if (st != BDM_OK) return st;
   bdm::HeadParts parts;
-  head_layout(T, V, static_cast<char*>(workspace), &parts);
+  head_layout(T, static_cast<char*>(workspace), &parts);
+  parts.grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
   (void)hipGetLastError();
   bdm::launch_head(h, T, H, w_head, V, mask_id, threshold, fallback, tokens, argmax, conf,
                    n_committed, parts, static_cast<hipStream_t>(stream));

@@ -48,16 +48,96 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// ---- cross-lane reductions on DPP (no LDS round trips) ---------------------
+// Within a 16-lane row: xor 1 and xor 2 (quad permutes), then the half-row
+// mirror (lane i <-> 7-i) and the row mirror (i <-> 15-i).  With a
+// commutative combiner every lane of the row ends with the same value.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+template <class Op>
+__device__ __forceinline__ float row_reduce_f(float v, Op op) {
+  v = op(v, dpp_f<kDppXor1>(v));
+  v = op(v, dpp_f<kDppXor2>(v));
+  v = op(v, dpp_f<kDppHalfMirror>(v));
+  v = op(v, dpp_f<kDppMirror>(v));
   return v;
 }
 
+// The four rows' results, combined in a fixed order on every lane.
+template <class Op>
+__device__ __forceinline__ float wave_reduce_f(float v, Op op) {
+  v = row_reduce_f(v, op);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce_f(v, [](float a, float b) { return a + b; });
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  auto add = [](int a, int b) { return a + b; };
+  v = add(v, dpp_i<kDppXor1>(v));
+  v = add(v, dpp_i<kDppXor2>(v));
+  v = add(v, dpp_i<kDppHalfMirror>(v));
+  v = add(v, dpp_i<kDppMirror>(v));
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+// Wave-wide argmax over (value, id): larger value wins, equal values keep the
+// lower id.  Every lane returns the winner.
+__device__ __forceinline__ bool argmax_better(float ov, int oid, float v, int id) {
+  return ov > v || (ov == v && oid < id);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& id) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oid = dpp_i<CTRL>(id);
+  if (argmax_better(ov, oid, v, id)) {
+    v = ov;
+    id = oid;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+  argmax_step<kDppXor1>(v, id);
+  argmax_step<kDppXor2>(v, id);
+  argmax_step<kDppHalfMirror>(v, id);
+  argmax_step<kDppMirror>(v, id);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bid = __builtin_amdgcn_readlane(id, 0);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int rid = __builtin_amdgcn_readlane(id, 16 * r);
+    if (argmax_better(rv, rid, bv, bid)) {
+      bv = rv;
+      bid = rid;
+    }
+  }
+  v = bv;
+  id = bid;
 }
 
 // Online-softmax statistics of a set of logits: running max m, sum of
@@ -85,8 +165,18 @@ __device__ __forceinline__ SoftStat softstat_merge(SoftStat x, SoftStat y) {
   return r;
 }
 
-__device__ __forceinline__ SoftStat shfl_xor_stat(SoftStat v, int o, int width) {
-  return {__shfl_xor(v.m, o, width), __shfl_xor(v.s, o, width), __shfl_xor(v.a, o, width)};
+template <int CTRL>
+__device__ __forceinline__ SoftStat dpp_stat(SoftStat v) {
+  return {dpp_f<CTRL>(v.m), dpp_f<CTRL>(v.s), dpp_i<CTRL>(v.a)};
+}
+
+// Merge across the 16 lanes of a row; every lane of the row gets the result.
+__device__ __forceinline__ SoftStat row_merge_stat(SoftStat v) {
+  v = softstat_merge(v, dpp_stat<kDppXor1>(v));
+  v = softstat_merge(v, dpp_stat<kDppXor2>(v));
+  v = softstat_merge(v, dpp_stat<kDppHalfMirror>(v));
+  v = softstat_merge(v, dpp_stat<kDppMirror>(v));
+  return v;
 }
 
 }  // namespace bdm

@@ -12,22 +12,18 @@
 
 namespace bdm {
 
-// Views into the MoE workspace (all device pointers).  Sizes for T tokens,
-// E routed experts, k picks, P = T*k (+T with a shared expert) pairs.
+// Views into the MoE workspace (all device pointers) for T tokens, E routed
+// experts and k picks.  Rows of act / ypair are (token, slot) pairs: row
+// t*(k+1)+j holds the j-th pick of token t, row t*(k+1)+k its shared expert.
 struct MoeMeta {
-  float* logits;        // [T][E]     router logits (fp32)
-  int32_t* topk_idx;    // [T][k]     picks, decreasing weight
-  float* topk_w;        // [T][k]     their weights
-  int32_t* info;        // [4]        [0] touched groups, [1] pairs
-  int32_t* offs;        // [E+2]      group start in the pair list; group E = shared
-  int32_t* touched;     // [E+1]      touched groups, shared first
-  int32_t* pair_token;  // [P]        token of each pair, grouped by expert
-  int32_t* pos;         // [T][k+1]   pair index of (t, j); j = k is the shared expert
-  uint16_t* act;        // [P][I]     bf16 SwiGLU activations per pair
-  float* ypair;         // [P][H]     fp32 expert outputs per pair
+  float* logits;        // [T][E]        router logits (fp32)
+  int32_t* topk_idx;    // [T][k]        picks, decreasing weight
+  float* topk_w;        // [T][k]        their weights
+  int32_t* info;        // [4]           [0] number of touched expert groups
+  int32_t* touched;     // [E+1]         touched groups (E = shared), heaviest first
+  uint16_t* act;        // [T*(k+1)][I]  bf16 SwiGLU activations
+  float* ypair;         // [T*(k+1)][H]  fp32 expert outputs
 };
-
-size_t route_select_lds_bytes(int T, int E);
 
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    int k, int renorm, int has_shared, const MoeMeta& meta, int32_t* user_idx,
@@ -39,14 +35,21 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                     const uint16_t* residual, uint16_t* y, const MoeMeta& meta, hipStream_t s);
 
 // Head: partial softmax statistics per (token, vocabulary tile).
-constexpr int kHeadTileRows = 256;   // vocabulary rows per workgroup
 constexpr int kHeadTokChunk = 32;    // tokens per head pass
+#ifndef BDM_HEAD_WAVES
+#define BDM_HEAD_WAVES 8
+#endif
+constexpr int kHeadWaves = BDM_HEAD_WAVES;   // waves per head workgroup
 
 struct HeadParts {
-  float* m;     // [T][ntiles]
-  float* s;     // [T][ntiles]
-  int32_t* a;   // [T][ntiles]
+  int grid;     // head workgroups (one per CU)
+  float* m;     // [T][grid]
+  float* s;     // [T][grid]
+  int32_t* a;   // [T][grid]
 };
+
+size_t head_lds_bytes(int H);
+int head_prepare();   // one-time kernel attribute set-up; 0 on success
 
 void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int32_t mask_id,
                  float threshold, int fallback, int32_t* tokens, int32_t* argmax, float* conf,

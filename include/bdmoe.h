@@ -123,8 +123,7 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
  *   topk_w       [T][k] fp32 or NULL    receives w_t
  *   workspace, workspace_bytes: see bdm_moe_workspace_bytes
- * Limits: T <= 1024, H multiple of 64 and <= 2048, E <= 1024, and
- *   E * ceil(T/32) <= 8192 (the routing bitmap lives in on-chip memory).
+ * Limits: T <= 1024, H multiple of 64 and <= 2048, E <= 1024.
  *   Pointers 16-byte aligned (workspace 256-byte aligned).  NaN inputs give
  *   undefined values, never an out-of-bounds access.
  * No other aliasing is allowed.
