@@ -37,19 +37,23 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
     off = align_up(off + bytes);
     return base ? base + o : nullptr;
   };
-  char* logits = take(sizeof(float) * T * E);
+  char* logits = take(sizeof(float) * bdm::kRouterParts * T * E);
   char* topk_idx = take(sizeof(int32_t) * T * k);
   char* topk_w = take(sizeof(float) * T * k);
+  char* ticket = take(sizeof(int32_t) * 4);
   char* info = take(sizeof(int32_t) * 4);
-  char* touched = take(sizeof(int32_t) * (E + 1));
+  char* slots = take(sizeof(int) * 4 * (E + 1));
+  char* pair_rows = take(sizeof(int32_t) * P);
   char* act = take(sizeof(uint16_t) * P * I);
   char* ypair = take(sizeof(float) * P * H);
   if (m) {
     m->logits = reinterpret_cast<float*>(logits);
     m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
     m->topk_w = reinterpret_cast<float*>(topk_w);
+    m->ticket = reinterpret_cast<int32_t*>(ticket);
     m->info = reinterpret_cast<int32_t*>(info);
-    m->touched = reinterpret_cast<int32_t*>(touched);
+    m->slots = reinterpret_cast<int4*>(slots);
+    m->pair_rows = reinterpret_cast<int32_t*>(pair_rows);
     m->act = reinterpret_cast<uint16_t*>(act);
     m->ypair = reinterpret_cast<float*>(ypair);
   }
@@ -158,6 +162,9 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
   const size_t need = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
   if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
 
+  int cus = 0;
+  st = device_setup(&cus);
+  if (st != BDM_OK) return st;
   bdm::MoeMeta meta;
   moe_layout(T, H, I, E, k, has_shared, static_cast<char*>(workspace), &meta);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -165,7 +172,7 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
   bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, meta, topk_idx,
                      topk_w, s);
   bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
-                      ws_down, residual, y, meta, s);
+                      ws_down, residual, y, meta, cus, s);
   return last_hip_status();
 }
 

@@ -9,10 +9,13 @@
 // into MFMA B-operand registers (16 bytes per lane; one instruction covers a
 // 64-byte k-slice of 16 rows), while the few token rows come from L2.
 //
-// Work is indexed by the list of touched expert groups (the shared expert is
-// group E), heaviest first; workgroups past its end exit at once.  A
-// workgroup issues its weight loads first and then finds the tokens of its
-// expert by scanning the top-k table with wave ballots.  Activations and outputs are stored per
+// Work is indexed by the slot table of touched expert groups the select step
+// builds ({expert, offset, count}; the shared expert, group E, first, then
+// the heavy ones); workgroups past its end exit at once.  A workgroup loads
+// its slot, the first token rows of its group, then its weight burst; no
+// weight load sits behind a branch (k-steps past K read k-step 0 and are
+// zeroed by a select), so the compiler keeps every load in flight.
+// Activations and outputs are stored per
 // (token, slot): row t*(k+1)+j for the j-th pick, t*(k+1)+k for the shared
 // expert, so the combine reads each token's k+1 rows contiguously.
 //
@@ -32,119 +35,114 @@ namespace bdm {
 
 constexpr int kGuCols = 16;     // I columns per gate/up work item
 constexpr int kGuWaves = 8;     // waves splitting K in gate/up
-constexpr int kGuMaxKs = 8;     // k-steps of 32 per wave: H <= 8 * 8 * 32 = 2048
 constexpr int kGuMt = 2;        // 16-token tiles multiplied per pass
-constexpr int kDnRows = 64;     // H rows per down work item
+constexpr int kDnRows = 64;     // H rows per down work item (4 waves x 16)
 
-// Collect the (token, slot) rows routed to expert e into `rows` (LDS, in
-// increasing token order) and return their number.  Called by all threads;
-// wave 0 scans, the others wait at the barrier.
-__device__ __forceinline__ int gather_pairs(int e, int E, int T, int k,
-                                            const int32_t* __restrict__ topk_idx, int* rows) {
-  __shared__ int s_count;
-  const int K1 = k + 1;
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    if (e == E) {
-      for (int t = lane; t < T; t += kWave) rows[t] = t * K1 + k;
-      if (lane == 0) s_count = T;
-    } else {
-      const int n = T * k;
-      int cnt = 0;
-      for (int b = 0; b < n; b += kWave) {
-        const int p = b + lane;
-        const bool hit = p < n && topk_idx[p] == e;
-        const unsigned long long m = __ballot(hit);
-        if (hit) {
-          const int t = p / k;
-          rows[cnt + __popcll(m & ((1ull << lane) - 1ull))] = t * K1 + (p - t * k);
-        }
-        cnt += __popcll(m);
-      }
-      if (lane == 0) s_count = cnt;
-    }
-  }
-  __syncthreads();
-  return s_count;
+// A slot names a real group: expert id in [0, E] (E only with a shared
+// expert), 1 <= count, and its pair rows inside [0, P).
+__device__ __forceinline__ bool slot_ok(int e, int off, int m, int E, int P, bool has_shared) {
+  return e >= 0 && (e < E || (e == E && has_shared)) && m >= 1 && off >= 0 && off <= P - m;
 }
 
+__device__ __forceinline__ int clamp_row(int r, int P) { return r < 0 ? 0 : (r >= P ? P - 1 : r); }
+
+// One k-step (8 consecutive k of one row) of a weight row.  With GUARD the
+// k-step may lie past K: the load then reads k-step 0 (always valid) and the
+// value is replaced by zeros, so no load sits behind a branch.
+template <bool GUARD>
+__device__ __forceinline__ u32x4 ld_kstep(const uint16_t* row, int s, int KS) {
+  if (!GUARD) return ld16_stream(row + s * 32);
+  const bool on = s < KS;
+  const u32x4 v = ld16_stream(row + (on ? s : 0) * 32);
+  return on ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
+// work item = (touched group, 16 columns of I); KSW k-steps per wave
+template <int KSW, bool GUARD>
 __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int I, int E, int k,
+    const uint16_t* __restrict__ x, int H, int I, int E, int k, int P,
     const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
-    const int32_t* __restrict__ info, const int32_t* __restrict__ touched,
-    const int32_t* __restrict__ topk_idx, uint16_t* __restrict__ act) {
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    uint16_t* __restrict__ act) {
   __shared__ f32x4 red[kGuWaves][kGuMt][2][kWave];   // 32 KB
-  __shared__ int rows[BDM_MAX_TOKENS];
+  __shared__ int srow[16 * kGuMt];
 
   const int tiles = I / kGuCols;
-  const int gi = blockIdx.x / tiles;
-  if (gi >= info[0]) return;                  // past the touched groups
-  const int e = touched[gi];
+  const int4 slot = slots[blockIdx.x / tiles];
+  const int e = slot.x;
+  const int off = slot.y;
+  const int m = slot.z;
+  // past the touched groups (-1), or a slot that is not a valid group: every
+  // index below stays inside its buffer whatever the table holds
+  if (!slot_ok(e, off, m, E, P, ws_gate != nullptr)) return;
   const int n0 = (blockIdx.x % tiles) * kGuCols;
   const int K1 = k + 1;
-
-  const uint16_t* Wg = (e == E) ? ws_gate : w_gate + static_cast<size_t>(e) * I * H;
-  const uint16_t* Wu = (e == E) ? ws_up : w_up + static_cast<size_t>(e) * I * H;
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
   const int KS = H / 32;
-  const int ksw = (KS + kGuWaves - 1) / kGuWaves;
-  const int s0 = wave * ksw;
+  const int s0 = wave * KSW;
 
-  // one burst: this wave's K-slice of the 16 gate rows and 16 up rows,
-  // issued before the token scan so the scan hides under the loads
-  u32x4 bg[kGuMaxKs], bu[kGuMaxKs];
-  const size_t roff = static_cast<size_t>(n0 + c) * H + g * 8;
+  // rows of the first token chunk before the weight burst (in-order
+  // completion: waiting for them later does not wait for the weights)
+  int row0 = clamp_row(pair_rows[off + (c < m ? c : 0)], P);
+  int row1 = clamp_row(pair_rows[off + (16 + c < m ? 16 + c : 0)], P);
+
+  const uint16_t* Wg = (e == E) ? ws_gate : w_gate + static_cast<size_t>(e) * I * H;
+  const uint16_t* Wu = (e == E) ? ws_up : w_up + static_cast<size_t>(e) * I * H;
+  u32x4 bg[KSW], bu[KSW];
+  const uint16_t* rg = Wg + static_cast<size_t>(n0 + c) * H + g * 8;
+  const uint16_t* ru = Wu + static_cast<size_t>(n0 + c) * H + g * 8;
 #pragma unroll
-  for (int q = 0; q < kGuMaxKs; ++q) {
-    const int s = s0 + q;
-    if (q < ksw && s < KS) {
-      bg[q] = ld16_stream(Wg + roff + s * 32);
-      bu[q] = ld16_stream(Wu + roff + s * 32);
-    } else {
-      bg[q] = u32x4{0u, 0u, 0u, 0u};
-      bu[q] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int q = 0; q < KSW; ++q) {
+    bg[q] = ld_kstep<GUARD>(rg, s0 + q, KS);
+    bu[q] = ld_kstep<GUARD>(ru, s0 + q, KS);
   }
 
-  const int m = gather_pairs(e, E, T, k, topk_idx, rows);
-
   for (int mc = 0; mc < m; mc += 16 * kGuMt) {
-    f32x4 ag[kGuMt], au[kGuMt];
-    const uint16_t* xr[kGuMt];
-    bool ok[kGuMt];
+    if (mc > 0) {
+      row0 = clamp_row(pair_rows[off + (mc + c < m ? mc + c : 0)], P);
+      row1 = clamp_row(pair_rows[off + (mc + 16 + c < m ? mc + 16 + c : 0)], P);
+    }
+    if (wave == 0 && g == 0) {
+      srow[c] = row0;
+      srow[16 + c] = row1;
+    }
+    f32x4 ag0 = f32x4{0.f, 0.f, 0.f, 0.f}, au0 = ag0, ag1 = ag0, au1 = ag0;
 #pragma unroll
     for (int mt = 0; mt < kGuMt; ++mt) {
-      ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = mc + mt * 16 + c;
-      ok[mt] = r < m;
-      const int tok = ok[mt] ? rows[r] / K1 : 0;
-      xr[mt] = x + static_cast<size_t>(tok) * H + g * 8;
-    }
+      if (mt == 0 || mc + 16 < m) {               // workgroup-uniform
+        const bool ok = mc + mt * 16 + c < m;
+        const uint16_t* xr = x + static_cast<size_t>((mt == 0 ? row0 : row1) / K1) * H + g * 8;
+        u32x4 a[KSW];
 #pragma unroll
-    for (int q = 0; q < kGuMaxKs; ++q) {
-      const int s = s0 + q;
-      if (q < ksw && s < KS) {
+        for (int q = 0; q < KSW; ++q) {
+          const int s = GUARD ? ((s0 + q) < KS ? s0 + q : 0) : s0 + q;
+          const u32x4 v = ld16(xr + s * 32);
+          a[q] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+        f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = accg;
 #pragma unroll
-        for (int mt = 0; mt < kGuMt; ++mt) {
-          if (mc + mt * 16 < m) {
-            const u32x4 a = ok[mt] ? ld16(xr[mt] + s * 32) : u32x4{0u, 0u, 0u, 0u};
-            ag[mt] = mfma_bf16(a, bg[q], ag[mt]);
-            au[mt] = mfma_bf16(a, bu[q], au[mt]);
-          }
+        for (int q = 0; q < KSW; ++q) {
+          accg = mfma_bf16(a[q], bg[q], accg);
+          accu = mfma_bf16(a[q], bu[q], accu);
+        }
+        if (mt == 0) {
+          ag0 = accg;
+          au0 = accu;
+        } else {
+          ag1 = accg;
+          au1 = accu;
         }
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < kGuMt; ++mt) {
-      red[wave][mt][0][lane] = ag[mt];
-      red[wave][mt][1][lane] = au[mt];
-    }
+    red[wave][0][0][lane] = ag0;
+    red[wave][0][1][lane] = au0;
+    red[wave][1][0][lane] = ag1;
+    red[wave][1][1][lane] = au1;
     __syncthreads();
     if (threadIdx.x < kGuMt * kWave) {
       const int mt = threadIdx.x / kWave;
@@ -158,11 +156,11 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
       const int col = n0 + (ln & 15);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = mc + mt * 16 + 4 * (ln >> 4) + q;
-        if (r < m) {
+        const int rl = mt * 16 + 4 * (ln >> 4) + q;
+        if (mc + rl < m) {
           const float gv = gs[q];
           const float a = gv / (1.0f + expf(-gv)) * us[q];
-          act[static_cast<size_t>(rows[r]) * I + col] = f32_to_bf16(a);
+          act[static_cast<size_t>(srow[rl]) * I + col] = f32_to_bf16(a);
         }
       }
     }
@@ -170,17 +168,20 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
   }
 }
 
-template <int KSMAX>
+// work item = (touched group, 64 rows of H); each wave owns 16 output rows
+// and the whole K = I (KS k-steps, KS <= KSMAX)
+template <int KSMAX, bool GUARD>
 __global__ __launch_bounds__(256, 2) void down_kernel(
-    const uint16_t* __restrict__ act, int T, int H, int I, int E, int k,
+    const uint16_t* __restrict__ act, int H, int I, int E, int P,
     const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
-    const int32_t* __restrict__ info, const int32_t* __restrict__ touched,
-    const int32_t* __restrict__ topk_idx, float* __restrict__ ypair) {
-  __shared__ int rows[BDM_MAX_TOKENS];
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    float* __restrict__ ypair) {
   const int tiles = H / kDnRows;
-  const int gi = blockIdx.x / tiles;
-  if (gi >= info[0]) return;                  // past the touched groups
-  const int e = touched[gi];
+  const int4 slot = slots[blockIdx.x / tiles];
+  const int e = slot.x;
+  const int off = slot.y;
+  const int m = slot.z;
+  if (!slot_ok(e, off, m, E, P, ws_down != nullptr)) return;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
@@ -188,31 +189,44 @@ __global__ __launch_bounds__(256, 2) void down_kernel(
   const int n0 = (blockIdx.x % tiles) * kDnRows + wave * 16;
   const int KS = I / 32;
 
-  const uint16_t* Wd = (e == E) ? ws_down : w_down + static_cast<size_t>(e) * H * I;
-  u32x4 b[KSMAX];
-  const size_t roff = static_cast<size_t>(n0 + c) * I + g * 8;
+  // rows of the first token tile (A operand row c; output rows 4g..4g+3)
+  // before the weight burst
+  int ra = clamp_row(pair_rows[off + (c < m ? c : 0)], P);
+  int ro[4];
 #pragma unroll
-  for (int s = 0; s < KSMAX; ++s)
-    b[s] = (s < KS) ? ld16_stream(Wd + roff + s * 32) : u32x4{0u, 0u, 0u, 0u};
+  for (int q = 0; q < 4; ++q) ro[q] = clamp_row(pair_rows[off + (4 * g + q < m ? 4 * g + q : 0)], P);
 
-  const int m = gather_pairs(e, E, T, k, topk_idx, rows);
+  const uint16_t* Wd = (e == E) ? ws_down : w_down + static_cast<size_t>(e) * H * I;
+  const uint16_t* rd = Wd + static_cast<size_t>(n0 + c) * I + g * 8;
+  u32x4 b[KSMAX];
+#pragma unroll
+  for (int s = 0; s < KSMAX; ++s) b[s] = ld_kstep<GUARD>(rd, s, KS);
 
   for (int mt = 0; mt * 16 < m; ++mt) {
-    const int r = mt * 16 + c;
-    const bool ok = r < m;
-    const uint16_t* ar = act + static_cast<size_t>(ok ? rows[r] : rows[0]) * I + g * 8;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mt > 0) {
+      const int r = mt * 16 + c;
+      ra = clamp_row(pair_rows[off + (r < m ? r : 0)], P);
 #pragma unroll
-    for (int s = 0; s < KSMAX; ++s) {
-      if (s < KS) {
-        const u32x4 a = ok ? ld16(ar + s * 32) : u32x4{0u, 0u, 0u, 0u};
-        acc = mfma_bf16(a, b[s], acc);
+      for (int q = 0; q < 4; ++q) {
+        const int rr = mt * 16 + 4 * g + q;
+        ro[q] = clamp_row(pair_rows[off + (rr < m ? rr : 0)], P);
       }
     }
+    const bool ok = mt * 16 + c < m;
+    const uint16_t* ar = act + static_cast<size_t>(ra) * I + g * 8;
+    u32x4 a[KSMAX];
+#pragma unroll
+    for (int s = 0; s < KSMAX; ++s) {
+      const u32x4 v = ld16(ar + (GUARD ? (s < KS ? s : 0) : s) * 32);
+      a[s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSMAX; ++s) acc = mfma_bf16(a[s], b[s], acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = mt * 16 + 4 * g + q;
-      if (rr < m) ypair[static_cast<size_t>(rows[rr]) * H + n0 + c] = acc[q];
+      if (rr < m) ypair[static_cast<size_t>(ro[q]) * H + n0 + c] = acc[q];
     }
   }
 }
@@ -272,20 +286,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, hipStream_t s) {
-  // upper bound on touched groups; workgroups past the actual count exit at once
+                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int cus,
+                    hipStream_t s) {
+  (void)cus;
+  // upper bound on touched groups; workgroups past the actual list exit at once
   const int groups = (T * k < E ? T * k : E) + (has_shared ? 1 : 0);
-  gateup_kernel<<<groups * (I / kGuCols), kGuWaves * 64, 0, s>>>(
-      x, T, H, I, E, k, w_gate, w_up, ws_gate, ws_up, meta.info, meta.touched, meta.topk_idx,
-      meta.act);
-  if (I <= 512) {
-    down_kernel<16><<<groups * (H / kDnRows), 256, 0, s>>>(
-        meta.act, T, H, I, E, k, w_down, ws_down, meta.info, meta.touched, meta.topk_idx,
-        meta.ypair);
+  const int P = T * (k + 1);
+  const dim3 gu(groups * (I / kGuCols)), dn(groups * (H / kDnRows));
+  const int KS = H / 32;
+  if (KS == kGuWaves * 8) {
+    gateup_kernel<8, false><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, w_gate, w_up, ws_gate,
+                                                        ws_up, meta.slots, meta.pair_rows,
+                                                        meta.act);
   } else {
-    down_kernel<32><<<groups * (H / kDnRows), 256, 0, s>>>(
-        meta.act, T, H, I, E, k, w_down, ws_down, meta.info, meta.touched, meta.topk_idx,
-        meta.ypair);
+    gateup_kernel<8, true><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, w_gate, w_up, ws_gate,
+                                                       ws_up, meta.slots, meta.pair_rows,
+                                                       meta.act);
+  }
+  const int KI = I / 32;
+  if (KI == 16) {
+    down_kernel<16, false><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+                                              meta.pair_rows, meta.ypair);
+  } else if (KI < 16) {
+    down_kernel<16, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+                                             meta.pair_rows, meta.ypair);
+  } else {
+    down_kernel<32, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+                                             meta.pair_rows, meta.ypair);
   }
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_w, residual, y);
 }

@@ -15,12 +15,16 @@ namespace bdm {
 // Views into the MoE workspace (all device pointers) for T tokens, E routed
 // experts and k picks.  Rows of act / ypair are (token, slot) pairs: row
 // t*(k+1)+j holds the j-th pick of token t, row t*(k+1)+k its shared expert.
+constexpr int kRouterParts = 4;   // K-parts of the router GEMM (summed by select)
+
 struct MoeMeta {
-  float* logits;        // [T][E]        router logits (fp32)
+  float* logits;        // [4][T][E]     partial router logits (fp32), one per K-part
   int32_t* topk_idx;    // [T][k]        picks, decreasing weight
   float* topk_w;        // [T][k]        their weights
+  int32_t* ticket;      // [1]           completion ticket of the select step
   int32_t* info;        // [4]           [0] number of touched expert groups
-  int32_t* touched;     // [E+1]         touched groups (E = shared), heaviest first
+  int4* slots;          // [E+1]         {expert, offset, count, 0} per touched group, then -1
+  int32_t* pair_rows;   // [T*(k+1)]     (token, slot) rows grouped by expert
   uint16_t* act;        // [T*(k+1)][I]  bf16 SwiGLU activations
   float* ypair;         // [T*(k+1)][H]  fp32 expert outputs
 };
@@ -32,14 +36,12 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, hipStream_t s);
+                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int cus,
+                    hipStream_t s);
 
 // Head: partial softmax statistics per (token, vocabulary tile).
 constexpr int kHeadTokChunk = 32;    // tokens per head pass
-#ifndef BDM_HEAD_WAVES
-#define BDM_HEAD_WAVES 8
-#endif
-constexpr int kHeadWaves = BDM_HEAD_WAVES;   // waves per head workgroup
+constexpr int kHeadWaves = 8;        // waves per head workgroup
 
 struct HeadParts {
   int grid;     // head workgroups (one per CU)
