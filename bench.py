@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotated weight sets / token blocks")
     p.add_argument("--cpu-tokens", type=int, default=4,
                    help="tokens of one block the CPU oracle runs for cpu_baseline (0: skip)")
-    p.add_argument("--graph", type=int, default=0, help="replay the timed steps as a HIP graph")
+    p.add_argument("--layout", type=int, default=1,
+                   help="weight layout: 1 = packed MFMA tiles (packed once, untimed), 0 = row-major")
     return p.parse_args()
 
 
@@ -74,6 +75,18 @@ def main():
         blk = synth.head_block(HS, w_head, block_seed=r + 1, n_boost=10)
         sets.append((inp, w_head, blk))
     torch.cuda.synchronize()
+    # the weights the kernels read: packed once (not timed) or the row-major tensors
+    if args.layout:
+        pk = bdm.bdm_pack_weights
+        kw_sets = [dict(w_gate=pk(i.w_gate), w_up=pk(i.w_up), w_down=pk(i.w_down),
+                        ws_gate=pk(i.ws_gate), ws_up=pk(i.ws_up), ws_down=pk(i.ws_down))
+                   for i, _, _ in sets]
+        heads = [pk(w) for _, w, _ in sets]
+    else:
+        kw_sets = [dict(w_gate=i.w_gate, w_up=i.w_up, w_down=i.w_down, ws_gate=i.ws_gate,
+                        ws_up=i.ws_up, ws_down=i.ws_down) for i, _, _ in sets]
+        heads = [w for _, w, _ in sets]
+    torch.cuda.synchronize()
 
     T, H = L.T, L.H
     moe_ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(T, H, L.I, L.E, L.k, True), dev)
@@ -86,19 +99,20 @@ def main():
     nc = torch.zeros((1,), dtype=torch.int32, device=dev)
 
     def step(i, ev=None):
-        inp, w_head, _ = sets[i % args.sets]
-        x = xs[i % args.sets]
+        r = i % args.sets
+        inp, kw, w_head = sets[r][0], kw_sets[r], heads[r]
+        x = xs[r]
         if ev is not None:
             ev[0].record()
         bdm.bdm_rmsnorm(x, xn, eps=1e-6)
         if ev is not None:
             ev[1].record()
-        bdm.bdm_moe_block_forward(xn, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, L.k,
-                                  ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
-                                  residual=x, y=xo[i % args.sets], topk_idx=idx, ws=moe_ws)
+        bdm.bdm_moe_block_forward(xn, inp.w_router, kw["w_gate"], kw["w_up"], kw["w_down"], L.k,
+                                  ws_gate=kw["ws_gate"], ws_up=kw["ws_up"], ws_down=kw["ws_down"],
+                                  residual=x, y=xo[r], topk_idx=idx, ws=moe_ws)
         if ev is not None:
             ev[2].record()
-        bdm.bdm_lm_head_unmask(xo[i % args.sets], w_head, HS.mask_id, 0.95, True, tokens[i % args.sets],
+        bdm.bdm_lm_head_unmask(xo[r], w_head, HS.mask_id, 0.95, True, tokens[r],
                                n_committed=nc, ws=head_ws)
         if ev is not None:
             ev[3].record()
@@ -187,6 +201,7 @@ def main():
                         "renormalised) + untied 248,320x2048 head with the 0.95 unmask rule",
             "block_tokens": T, "hidden": H, "experts": L.E, "top_k": L.k, "inter": L.I,
             "vocab": HS.V, "weight_sets_rotated": args.sets, "parallelism": "single GPU",
+            "weight_layout": "mfma_tiles (packed once at load)" if args.layout else "row_major",
         },
         "moe_layer": {"us": round(moe_us, 2), "block_tokens_per_s": round(T / (moe_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),

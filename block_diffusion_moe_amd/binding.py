@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libbdmoe.so")
 BDM_OK = 0
 BDM_MASK_ID_CLOVER = 151669
 BDM_THRESHOLD_DEFAULT = 0.95
+BDM_LAYOUT_ROW_MAJOR = 0
+BDM_LAYOUT_MFMA_TILES = 1
 
 _c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -27,11 +29,13 @@ _SIGS = {
     "bdm_status_string": (ctypes.c_char_p, [_c_int]),
     "bdm_moe_workspace_bytes": (_c_int, [_c_int] * 6 + [ctypes.POINTER(_c_size)]),
     "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
-                                       _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp,
-                                       _vp, _vp, _c_size, _vp]),
+                                       _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
+                                       _vp, _vp, _vp, _c_size, _vp]),
     "bdm_head_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
-    "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, ctypes.c_int32, _c_float,
-                                    _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
+                                    _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_packed_weight_elems": (_c_int, [ctypes.c_long, _c_int, ctypes.POINTER(_c_size)]),
+    "bdm_pack_weights": (_c_int, [_vp, ctypes.c_long, _c_int, _vp, _vp]),
     "bdm_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
 }
 
@@ -63,7 +67,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def _ptr(t: Optional[torch.Tensor]):
+class Packed:
+    """A bf16 weight tensor in the MFMA-tile layout (see bdm_pack_weights):
+    `data` holds the packed elements, `shape` the logical row-major shape
+    (the last dimension is the reduction dimension)."""
+
+    def __init__(self, data: torch.Tensor, shape):
+        self.data = data
+        self.shape = tuple(shape)
+        self.device = data.device
+        self.dtype = data.dtype
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
@@ -73,8 +92,21 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check(t: Optional[torch.Tensor], name: str, dtype, shape=None, device=None):
+def _check(t, name: str, dtype, shape=None, device=None):
     if t is None:
+        return
+    if isinstance(t, Packed):
+        if t.dtype != dtype or not t.data.is_cuda or not t.data.is_contiguous():
+            raise ValueError(f"{name}: packed data must be a contiguous device {dtype} tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name}: on {t.device}, expected {device}")
+        if shape is not None and t.shape != tuple(shape):
+            raise ValueError(f"{name}: logical shape {t.shape}, expected {tuple(shape)}")
+        rows = 1
+        for d in t.shape[:-1]:
+            rows *= d
+        if t.data.numel() < bdm_packed_weight_elems(rows, t.shape[-1]):
+            raise ValueError(f"{name}: packed buffer too small")
         return
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
@@ -114,6 +146,31 @@ def bdm_head_workspace_bytes(T, H, V) -> int:
     return n.value
 
 
+def bdm_packed_weight_elems(rows: int, cols: int) -> int:
+    n = _c_size(0)
+    _raise("bdm_packed_weight_elems", load().bdm_packed_weight_elems(int(rows), int(cols),
+                                                                     ctypes.byref(n)))
+    return n.value
+
+
+def bdm_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> Packed:
+    """Packed (MFMA-tile) copy of a row-major bf16 weight tensor; all leading
+    dimensions are folded into rows (an expert stack [E][I][H] packs as one
+    [E*I][H] matrix)."""
+    _check(w, "w", torch.bfloat16)
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    n = bdm_packed_weight_elems(rows, cols)
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    _check(out, "out", torch.bfloat16, device=w.device)
+    if out.numel() < n:
+        raise ValueError("out: too small for the packed copy")
+    _raise("bdm_pack_weights", load().bdm_pack_weights(_ptr(w), rows, cols, _ptr(out),
+                                                       _stream(stream)))
+    return Packed(out, w.shape)
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     """Device scratch buffer (torch allocations are 256-byte aligned)."""
     return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
@@ -123,7 +180,8 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
                           ws_gate=None, ws_up=None, ws_down=None, residual=None, y=None,
                           topk_idx=None, topk_w=None, renorm: bool = True, ws=None, stream=None):
     """y = MoE layer over the block x (see include/bdmoe.h).  ``y`` may be
-    ``residual`` (in-place residual add); a new tensor is made when None."""
+    ``residual`` (in-place residual add); a new tensor is made when None.
+    Expert weights may be row-major tensors or all `Packed`."""
     T, H = x.shape
     E, I, _ = w_gate.shape
     dev = x.device
@@ -143,13 +201,19 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
     _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
     _check(topk_w, "topk_w", torch.float32, (T, k), dev)
     has_shared = ws_gate is not None
+    packed = [isinstance(t, Packed) for t in (w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+              if t is not None]
+    if any(packed) and not all(packed):
+        raise ValueError("expert weights must be all row-major or all packed")
+    layout = BDM_LAYOUT_MFMA_TILES if all(packed) else BDM_LAYOUT_ROW_MAJOR
     need = bdm_moe_workspace_bytes(T, H, I, E, k, has_shared)
     if ws is None:
         ws = workspace(need, dev)
     st = load().bdm_moe_block_forward(
         _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm), _ptr(w_gate),
-        _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(residual),
-        _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream))
+        _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), layout,
+        _ptr(residual), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
+        _stream(stream))
     _raise("bdm_moe_block_forward", st)
     return y
 
@@ -168,9 +232,11 @@ def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool
     need = bdm_head_workspace_bytes(T, H, V)
     if ws is None:
         ws = workspace(need, dev)
-    st = load().bdm_lm_head_unmask(_ptr(h), T, H, _ptr(w_head), V, int(mask_id), float(threshold),
-                                   int(fallback), _ptr(tokens), _ptr(argmax), _ptr(conf),
-                                   _ptr(n_committed), _ptr(ws), ws.numel(), _stream(stream))
+    layout = BDM_LAYOUT_MFMA_TILES if isinstance(w_head, Packed) else BDM_LAYOUT_ROW_MAJOR
+    st = load().bdm_lm_head_unmask(_ptr(h), T, H, _ptr(w_head), V, layout, int(mask_id),
+                                   float(threshold), int(fallback), _ptr(tokens), _ptr(argmax),
+                                   _ptr(conf), _ptr(n_committed), _ptr(ws), ws.numel(),
+                                   _stream(stream))
     _raise("bdm_lm_head_unmask", st)
     return tokens
 

@@ -142,14 +142,16 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
                           const float* router_bias, int E, int k, int renorm,
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int I, const uint16_t* ws_gate, const uint16_t* ws_up,
-                          const uint16_t* ws_down, const uint16_t* residual, uint16_t* y,
-                          int32_t* topk_idx, float* topk_w, void* workspace,
+                          const uint16_t* ws_down, int weight_layout, const uint16_t* residual,
+                          uint16_t* y, int32_t* topk_idx, float* topk_w, void* workspace,
                           size_t workspace_bytes, void* stream) {
   if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
     return BDM_ERR_INVALID_ARG;
   const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
   if (nshared != 0 && nshared != 3) return BDM_ERR_INVALID_ARG;
   if (renorm != 0 && renorm != 1) return BDM_ERR_INVALID_ARG;
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+    return BDM_ERR_INVALID_ARG;
   const int has_shared = nshared == 3 ? 1 : 0;
   int st = check_moe_shape(T, H, I, E, k, has_shared);
   if (st != BDM_OK) return st;
@@ -172,7 +174,7 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
   bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, meta, topk_idx,
                      topk_w, s);
   bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
-                      ws_down, residual, y, meta, cus, s);
+                      ws_down, residual, y, meta, weight_layout, s);
   return last_hip_status();
 }
 
@@ -185,7 +187,8 @@ int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {
 }
 
 int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
-                       int32_t mask_id, float threshold, int fallback, int32_t* tokens,
+                       int weight_layout, int32_t mask_id, float threshold, int fallback,
+                       int32_t* tokens,
                        int32_t* argmax, float* conf, int32_t* n_committed, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (!h || !w_head || !tokens || !workspace) return BDM_ERR_INVALID_ARG;
@@ -195,6 +198,8 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
   if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+    return BDM_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(w_head) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return BDM_ERR_INVALID_ARG;
   const size_t need = head_layout(T, nullptr, nullptr);
@@ -206,8 +211,28 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   head_layout(T, static_cast<char*>(workspace), &parts);
   parts.grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
   (void)hipGetLastError();
-  bdm::launch_head(h, T, H, w_head, V, mask_id, threshold, fallback, tokens, argmax, conf,
-                   n_committed, parts, static_cast<hipStream_t>(stream));
+  bdm::launch_head(h, T, H, w_head, V, weight_layout, mask_id, threshold, fallback, tokens, argmax,
+                   conf, n_committed, parts, static_cast<hipStream_t>(stream));
+  return last_hip_status();
+}
+
+int bdm_packed_weight_elems(long rows, int cols, size_t* n) {
+  if (!n || rows < 1 || cols < 32 || cols % 32 != 0) return BDM_ERR_INVALID_ARG;
+  *n = static_cast<size_t>((rows + 15) / 16) * 16 * static_cast<size_t>(cols);
+  return BDM_OK;
+}
+
+int bdm_pack_weights(const uint16_t* src, long rows, int cols, uint16_t* dst, void* stream) {
+  size_t n = 0;
+  const int st = bdm_packed_weight_elems(rows, cols, &n);
+  if (st != BDM_OK) return st;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return BDM_ERR_INVALID_ARG;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), a1 = a0 + 2 * static_cast<size_t>(rows) * cols;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(dst), b1 = b0 + 2 * n;
+  if (a0 < b1 && b0 < a1) return BDM_ERR_INVALID_ARG;          // overlap
+  if ((rows + 15) / 16 * (cols / 32) > 4L * 0x7fffffffL) return BDM_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  bdm::launch_pack(src, rows, cols, dst, static_cast<hipStream_t>(stream));
   return last_hip_status();
 }
 

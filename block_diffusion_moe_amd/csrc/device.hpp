@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bdmoe.h"
+
 namespace bdm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -41,6 +43,22 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// This lane's 16 bytes of k-step 0 of the 16 weight rows row0 .. row0+15 of a
+// bf16 matrix with K columns, and the element stride from one k-step (32 k)
+// to the next: row-major [R][K] (rows 4 KB apart at K = 2048) or the packed
+// MFMA-tile layout (one contiguous 1 KB fragment per k-step, see pack.hip).
+struct FragPtr {
+  const uint16_t* p;
+  int step;
+};
+
+__device__ __forceinline__ FragPtr frag_ptr(const uint16_t* W, long row0, int K, int lane,
+                                            int layout) {
+  if (layout == BDM_LAYOUT_MFMA_TILES)
+    return {W + (row0 / 16) * (K / 32) * 512 + lane * 8, 512};
+  return {W + (row0 + (lane & 15)) * K + (lane >> 4) * 8, 32};
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {

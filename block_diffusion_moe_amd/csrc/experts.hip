@@ -50,17 +50,17 @@ __device__ __forceinline__ int clamp_row(int r, int P) { return r < 0 ? 0 : (r >
 // k-step may lie past K: the load then reads k-step 0 (always valid) and the
 // value is replaced by zeros, so no load sits behind a branch.
 template <bool GUARD>
-__device__ __forceinline__ u32x4 ld_kstep(const uint16_t* row, int s, int KS) {
-  if (!GUARD) return ld16_stream(row + s * 32);
+__device__ __forceinline__ u32x4 ld_kstep(FragPtr f, int s, int KS) {
+  if (!GUARD) return ld16_stream(f.p + s * f.step);
   const bool on = s < KS;
-  const u32x4 v = ld16_stream(row + (on ? s : 0) * 32);
+  const u32x4 v = ld16_stream(f.p + (on ? s : 0) * f.step);
   return on ? v : u32x4{0u, 0u, 0u, 0u};
 }
 
 // work item = (touched group, 16 columns of I); KSW k-steps per wave
 template <int KSW, bool GUARD>
 __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
-    const uint16_t* __restrict__ x, int H, int I, int E, int k, int P,
+    const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
     const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
     const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
@@ -91,11 +91,10 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
   int row0 = clamp_row(pair_rows[off + (c < m ? c : 0)], P);
   int row1 = clamp_row(pair_rows[off + (16 + c < m ? 16 + c : 0)], P);
 
-  const uint16_t* Wg = (e == E) ? ws_gate : w_gate + static_cast<size_t>(e) * I * H;
-  const uint16_t* Wu = (e == E) ? ws_up : w_up + static_cast<size_t>(e) * I * H;
+  const long wrow0 = (e == E) ? n0 : static_cast<long>(e) * I + n0;
+  const FragPtr rg = frag_ptr(e == E ? ws_gate : w_gate, wrow0, H, lane, layout);
+  const FragPtr ru = frag_ptr(e == E ? ws_up : w_up, wrow0, H, lane, layout);
   u32x4 bg[KSW], bu[KSW];
-  const uint16_t* rg = Wg + static_cast<size_t>(n0 + c) * H + g * 8;
-  const uint16_t* ru = Wu + static_cast<size_t>(n0 + c) * H + g * 8;
 #pragma unroll
   for (int q = 0; q < KSW; ++q) {
     bg[q] = ld_kstep<GUARD>(rg, s0 + q, KS);
@@ -172,7 +171,7 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
 // and the whole K = I (KS k-steps, KS <= KSMAX)
 template <int KSMAX, bool GUARD>
 __global__ __launch_bounds__(256, 2) void down_kernel(
-    const uint16_t* __restrict__ act, int H, int I, int E, int P,
+    const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
     const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
     const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
     float* __restrict__ ypair) {
@@ -196,8 +195,8 @@ __global__ __launch_bounds__(256, 2) void down_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) ro[q] = clamp_row(pair_rows[off + (4 * g + q < m ? 4 * g + q : 0)], P);
 
-  const uint16_t* Wd = (e == E) ? ws_down : w_down + static_cast<size_t>(e) * H * I;
-  const uint16_t* rd = Wd + static_cast<size_t>(n0 + c) * I + g * 8;
+  const FragPtr rd = frag_ptr(e == E ? ws_down : w_down,
+                             (e == E) ? n0 : static_cast<long>(e) * H + n0, I, lane, layout);
   u32x4 b[KSMAX];
 #pragma unroll
   for (int s = 0; s < KSMAX; ++s) b[s] = ld_kstep<GUARD>(rd, s, KS);
@@ -286,32 +285,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int cus,
+                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int layout,
                     hipStream_t s) {
-  (void)cus;
   // upper bound on touched groups; workgroups past the actual list exit at once
   const int groups = (T * k < E ? T * k : E) + (has_shared ? 1 : 0);
   const int P = T * (k + 1);
   const dim3 gu(groups * (I / kGuCols)), dn(groups * (H / kDnRows));
   const int KS = H / 32;
   if (KS == kGuWaves * 8) {
-    gateup_kernel<8, false><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, w_gate, w_up, ws_gate,
+    gateup_kernel<8, false><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
                                                         ws_up, meta.slots, meta.pair_rows,
                                                         meta.act);
   } else {
-    gateup_kernel<8, true><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, w_gate, w_up, ws_gate,
+    gateup_kernel<8, true><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
                                                        ws_up, meta.slots, meta.pair_rows,
                                                        meta.act);
   }
   const int KI = I / 32;
   if (KI == 16) {
-    down_kernel<16, false><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+    down_kernel<16, false><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                               meta.pair_rows, meta.ypair);
   } else if (KI < 16) {
-    down_kernel<16, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+    down_kernel<16, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   } else {
-    down_kernel<32, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, w_down, ws_down, meta.slots,
+    down_kernel<32, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   }
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_w, residual, y);

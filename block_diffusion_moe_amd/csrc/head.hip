@@ -21,58 +21,29 @@
 
 namespace bdm {
 
-#ifndef BDM_HEAD_UNROLL
-#define BDM_HEAD_UNROLL 4
-#endif
-#ifndef BDM_HEAD_NT
-#define BDM_HEAD_NT 1
-#endif
-#ifndef BDM_HEAD_PREFETCH
-#define BDM_HEAD_PREFETCH 1
-#endif
-
-constexpr int kHeadGroups = 4;                 // 16-row vocabulary groups a wave multiplies together
-constexpr int kHeadUnroll = BDM_HEAD_UNROLL;   // k-steps of weight loads issued together
-constexpr int kHeadPad = 8;                    // bf16 padding per staged row (bank spread)
+constexpr int kHeadGroups = 4;   // 16-row vocabulary groups a wave multiplies together
+constexpr int kHeadPad = 8;      // bf16 padding per staged row (bank spread)
 
 size_t head_lds_bytes(int H) {
   return static_cast<size_t>(kHeadTokChunk) * (H + kHeadPad) * sizeof(uint16_t) +
          static_cast<size_t>(kHeadWaves) * kHeadTokChunk * sizeof(SoftStat);
 }
 
-__device__ __forceinline__ u32x4 head_ld(const uint16_t* p) {
-  return BDM_HEAD_NT ? ld16_stream(p) : ld16(p);
-}
-
-// Loads of one batch: kHeadUnroll k-steps of the four 16-row groups of the
-// chunk starting at group gb (groups past the run end, or k past H, load 0).
-__device__ __forceinline__ void head_load_batch(u32x4 (&b)[kHeadUnroll][kHeadGroups],
-                                                const uint16_t* __restrict__ w, int V, int H,
-                                                int gb, int nq, int s0, int KS, int c, int g) {
-#pragma unroll
-  for (int q = 0; q < kHeadGroups; ++q) {
-    int v = (gb + q) * 16 + c;
-    v = v < V ? v : V - 1;                      // ragged tail: a valid row, dropped later
-    const uint16_t* row = w + static_cast<size_t>(v) * H + g * 8;
-#pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u)
-      b[u][q] = (q < nq && s0 + u < KS) ? head_ld(row + (s0 + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
 // Persistent: one workgroup per CU, 8 waves.  The <= 32 hidden rows of this
 // pass are staged once in LDS (A operand).  The vocabulary is cut into
-// 16-row groups and every wave of the grid takes one contiguous run of
-// groups (lengths differ by at most one group), streaming those weight rows
-// once from HBM as the B operand, four groups (a chunk) at a time.  The loop
-// runs over (chunk, k-batch) pairs with the next batch's loads issued before
-// the current batch's MFMAs, so a wave always has a batch in flight, also
-// across chunk boundaries.  Each lane keeps online-softmax state for its 8
-// (token, column) slots across the run; the per-wave results are merged
-// across lanes and waves in a fixed order and written as one partial per
-// (token, workgroup).
+// 64-row chunks (four 16-row groups) and every wave of the grid takes one
+// contiguous run of chunks (lengths differ by at most one), streaming those
+// weight rows once from HBM as the B operand.  The loop runs over
+// (chunk, k-batch) pairs; the next batch's loads are issued before the
+// current batch's MFMAs, and no load sits behind a branch (rows past V are
+// clamped to a valid row and dropped in the epilogue), so a wave always has
+// a batch in flight, also across chunk boundaries.  Each lane keeps
+// online-softmax state for its 8 (token, column) slots across the run; the
+// per-wave results are merged across lanes and waves in a fixed order and
+// written as one partial per (token, workgroup).  U = k-steps per batch.
+template <int U>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
-    const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V,
+    const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int layout,
     int32_t mask_id, int tok0, int ntok, float* __restrict__ pm, float* __restrict__ ps,
     int32_t* __restrict__ pa) {
   extern __shared__ __align__(16) unsigned char head_smem[];
@@ -86,35 +57,73 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  const long NG = (V + 15) / 16;
+  const long NC = (V + 16 * kHeadGroups - 1) / (16 * kHeadGroups);
   const long NW = static_cast<long>(gridDim.x) * kHeadWaves;
   const long wid = static_cast<long>(blockIdx.x) * kHeadWaves + wave;
-  const int g0 = static_cast<int>(wid * NG / NW);
-  const int g1 = static_cast<int>((wid + 1) * NG / NW);
+  const int c0 = static_cast<int>(wid * NC / NW);
+  const int c1 = static_cast<int>((wid + 1) * NC / NW);
   const int KS = H / 32;
-  const int nb = (KS + kHeadUnroll - 1) / kHeadUnroll;          // k-batches per chunk
-  const int nchunks = (g1 - g0 + kHeadGroups - 1) / kHeadGroups;
-  const int iters = nchunks * nb;
+  const int nb = KS / U;                                        // k-batches per chunk
+  const int iters = (c1 - c0) * nb;
 
-  // first batch in flight before the staging barrier
-  u32x4 bcur[kHeadUnroll][kHeadGroups];
-  if (iters > 0) {
-    const int nq = (g1 - g0) < kHeadGroups ? (g1 - g0) : kHeadGroups;
-    head_load_batch(bcur, w, V, H, g0, nq, 0, KS, c, g);
-  }
+  // fragment pointer of chunk ch, group q (row-major: a row past V reads
+  // row V-1; packed: a group past the last one reads the last one; both are
+  // dropped in the epilogue, which keeps only v < V)
+  const long ngroups = (V + 15) / 16;            // 16-row groups (packed: padded rows)
+  auto wfrag = [&](int ch, int q) {
+    long grp = static_cast<long>(ch) * kHeadGroups + q;
+    if (layout == BDM_LAYOUT_MFMA_TILES) {
+      grp = grp < ngroups ? grp : ngroups - 1;   // chunk past the last group: dropped later
+      return frag_ptr(w, grp * 16, H, lane, layout);
+    }
+    const long v0 = grp * 16;
+    long v = v0 + c;
+    v = v < V ? v : V - 1;
+    return FragPtr{w + v * H + g * 8, 32};
+  };
+  auto load_batch = [&](int it, u32x4(&b)[U][kHeadGroups]) {
+    const int ch = c0 + it / nb;
+    const int s0 = (it % nb) * U;
+#pragma unroll
+    for (int q = 0; q < kHeadGroups; ++q) {
+      const FragPtr f = wfrag(ch, q);
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u][q] = ld16_stream(f.p + (s0 + u) * f.step);
+    }
+  };
 
-  // stage this pass's hidden rows (rows >= ntok are zero)
-  const int c8n = H / 8;
-  for (int idx = tid; idx < kHeadTokChunk * c8n; idx += blockDim.x) {
-    const int r = idx / c8n;
-    const int c8 = idx - r * c8n;
-    const u32x4 v = (r < ntok) ? ld16(h + static_cast<size_t>(tok0 + r) * H + c8 * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(hs + r * HP + c8 * 8) = v;
+  // the first two batches in flight before the staging barrier
+  u32x4 bcur[U][kHeadGroups], bnxt[U][kHeadGroups];
+  if (iters > 0) load_batch(0, bcur);
+  if (iters > 1) load_batch(1, bnxt);
+
+  // stage this pass's hidden rows (rows >= ntok are zero): every load first
+  // (clamped addresses, no branches), then the LDS stores
+  {
+    constexpr int kStage = kHeadTokChunk * BDM_MAX_HIDDEN / 8 / (kHeadWaves * 64);
+    const int c8n = H / 8;
+    const int total = kHeadTokChunk * c8n;
+    u32x4 v[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = tid + j * kHeadWaves * 64;
+      const int r = idx / c8n;
+      const int c8 = idx - r * c8n;
+      const bool ok = idx < total && r < ntok;
+      const u32x4 x = ld16(h + static_cast<size_t>(tok0 + (ok ? r : 0)) * H + (ok ? c8 : 0) * 8);
+      v[j] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = tid + j * kHeadWaves * 64;
+      if (idx < total) {
+        const int r = idx / c8n;
+        *reinterpret_cast<u32x4*>(hs + r * HP + (idx - r * c8n) * 8) = v[j];
+      }
+    }
   }
   __syncthreads();
 
-  const bool two = ntok > 16;
   const uint16_t* arow0 = hs + c * HP + g * 8;
   const uint16_t* arow1 = hs + (16 + c) * HP + g * 8;
 
@@ -130,37 +139,22 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < iters; ++it) {
-    const int chunk = it / nb;
-    const int kb = it - chunk * nb;
-    const int gb = g0 + chunk * kHeadGroups;
-    const int nq = (g1 - gb) < kHeadGroups ? (g1 - gb) : kHeadGroups;   // wave-uniform
-    const int s0 = kb * kHeadUnroll;
-
-    u32x4 bnxt[kHeadUnroll][kHeadGroups];
-    if (BDM_HEAD_PREFETCH && it + 1 < iters) {
-      const int chunk1 = (it + 1) / nb;
-      const int gb1 = g0 + chunk1 * kHeadGroups;
-      const int nq1 = (g1 - gb1) < kHeadGroups ? (g1 - gb1) : kHeadGroups;
-      head_load_batch(bnxt, w, V, H, gb1, nq1, ((it + 1) - chunk1 * nb) * kHeadUnroll, KS, c, g);
-    }
+  auto compute = [&](int it, const u32x4(&b)[U][kHeadGroups]) {
+    const int s0 = (it % nb) * U;
 #pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u) {
-      if (s0 + u < KS) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(arow0 + (s0 + u) * 32);
-        const u32x4 a1 = two ? *reinterpret_cast<const u32x4*>(arow1 + (s0 + u) * 32)
-                             : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < U; ++u) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(arow0 + (s0 + u) * 32);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(arow1 + (s0 + u) * 32);
 #pragma unroll
-        for (int q = 0; q < kHeadGroups; ++q) {
-          acc[q][0] = mfma_bf16(a0, bcur[u][q], acc[q][0]);
-          if (two) acc[q][1] = mfma_bf16(a1, bcur[u][q], acc[q][1]);
-        }
+      for (int q = 0; q < kHeadGroups; ++q) {
+        acc[q][0] = mfma_bf16(a0, b[u][q], acc[q][0]);
+        acc[q][1] = mfma_bf16(a1, b[u][q], acc[q][1]);
       }
     }
-
-    if (kb == nb - 1) {
-      // online softmax over this chunk's columns (increasing vocabulary id per
-      // lane, so a strict '>' keeps the lowest id among equal maxima)
+    if (it % nb == nb - 1) {
+      // online softmax over this chunk's columns (increasing vocabulary id
+      // per lane, so a strict '>' keeps the lowest id among equal maxima)
+      const int ch = c0 + it / nb;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -168,8 +162,8 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
           SoftStat& s = st[mt][i];
 #pragma unroll
           for (int q = 0; q < kHeadGroups; ++q) {
-            const int v = (gb + q) * 16 + c;
-            if (q < nq && v < V && v != mask_id) {
+            const int v = (ch * kHeadGroups + q) * 16 + c;
+            if (v < V && v != mask_id) {
               const float l = acc[q][mt][i];
               if (l > s.m) {
                 s.s = (s.m == -INFINITY ? 0.0f : s.s * expf(s.m - l)) + 1.0f;
@@ -187,17 +181,26 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
 
-    if (BDM_HEAD_PREFETCH) {
-#pragma unroll
-      for (int u = 0; u < kHeadUnroll; ++u)
-#pragma unroll
-        for (int q = 0; q < kHeadGroups; ++q) bcur[u][q] = bnxt[u][q];
-    } else if (it + 1 < iters) {
-      const int chunk1 = (it + 1) / nb;
-      const int gb1 = g0 + chunk1 * kHeadGroups;
-      const int nq1 = (g1 - gb1) < kHeadGroups ? (g1 - gb1) : kHeadGroups;
-      head_load_batch(bcur, w, V, H, gb1, nq1, ((it + 1) - chunk1 * nb) * kHeadUnroll, KS, c, g);
+  // ping-pong batches: while one is multiplied the other is loading
+  if (iters == 1) {
+    compute(0, bcur);
+  } else if (iters > 1) {
+    int it = 0;
+    for (; it + 3 < iters; it += 2) {
+      compute(it, bcur);
+      load_batch(it + 2, bcur);
+      compute(it + 1, bnxt);
+      load_batch(it + 3, bnxt);
+    }
+    compute(it, bcur);
+    if (it + 2 < iters) {
+      load_batch(it + 2, bcur);
+      compute(it + 1, bnxt);
+      compute(it + 2, bcur);
+    } else {
+      compute(it + 1, bnxt);
     }
   }
 
@@ -293,15 +296,20 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   if (lane == 0 && n_committed) *n_committed = ncommit;
 }
 
-void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int32_t mask_id,
-                 float threshold, int fallback, int32_t* tokens, int32_t* argmax, float* conf,
-                 int32_t* n_committed, const HeadParts& parts, hipStream_t s) {
+void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int layout,
+                 int32_t mask_id, float threshold, int fallback, int32_t* tokens, int32_t* argmax,
+                 float* conf, int32_t* n_committed, const HeadParts& parts, hipStream_t s) {
   const int grid = parts.grid;
   const size_t lds = head_lds_bytes(H);
+  const bool u4 = false;   // two k-steps per batch: both ping-pong buffers stay in VGPRs
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
-    head_tile_kernel<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, mask_id, t0, n, parts.m,
-                                                       parts.s, parts.a);
+    if (u4)
+      head_tile_kernel<4><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, layout, mask_id, t0, n, parts.m,
+                                                            parts.s, parts.a);
+    else
+      head_tile_kernel<2><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, layout, mask_id, t0, n, parts.m,
+                                                            parts.s, parts.a);
   }
   head_merge_kernel<<<1, 1024, static_cast<size_t>(T) * 12, s>>>(
       parts.m, parts.s, parts.a, T, grid, mask_id, threshold, fallback, tokens, argmax, conf,
@@ -309,11 +317,13 @@ void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int3
 }
 
 int head_prepare() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(head_lds_bytes(BDM_MAX_HIDDEN))) == hipSuccess
-             ? 0
-             : -1;
+  const int lds = static_cast<int>(head_lds_bytes(BDM_MAX_HIDDEN));
+  const bool ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<4>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<2>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
+  return ok ? 0 : -1;
 }
 
 }  // namespace bdm

@@ -36,7 +36,7 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int cus,
+                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int layout,
                     hipStream_t s);
 
 // Head: partial softmax statistics per (token, vocabulary tile).
@@ -53,9 +53,11 @@ struct HeadParts {
 size_t head_lds_bytes(int H);
 int head_prepare();   // one-time kernel attribute set-up; 0 on success
 
-void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int32_t mask_id,
-                 float threshold, int fallback, int32_t* tokens, int32_t* argmax, float* conf,
-                 int32_t* n_committed, const HeadParts& parts, hipStream_t s);
+void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int layout,
+                 int32_t mask_id, float threshold, int fallback, int32_t* tokens, int32_t* argmax,
+                 float* conf, int32_t* n_committed, const HeadParts& parts, hipStream_t s);
+
+void launch_pack(const uint16_t* src, long R, int K, uint16_t* dst, hipStream_t s);
 
 void launch_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H,
                     uint16_t* out, hipStream_t s);

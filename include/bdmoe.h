@@ -62,6 +62,16 @@ extern "C" {
 #define BDM_MASK_ID_CLOVER     151669
 #define BDM_THRESHOLD_DEFAULT  0.95f
 
+/* Layout of the bf16 weight matrices a call reads (argument weight_layout).
+ *   BDM_LAYOUT_ROW_MAJOR   [rows][cols], cols contiguous (the natural layout)
+ *   BDM_LAYOUT_MFMA_TILES  the packed layout bdm_pack_weights produces: 1 KB
+ *                          tiles of 16 rows x 32 cols in MFMA operand order,
+ *                          a 16-row group contiguous over all cols.  The same
+ *                          values; only the byte order differs (streams at a
+ *                          higher fraction of HBM bandwidth). */
+#define BDM_LAYOUT_ROW_MAJOR   0
+#define BDM_LAYOUT_MFMA_TILES  1
+
 /* Limits of this implementation (checked; BDM_ERR_UNSUPPORTED_SHAPE beyond). */
 #define BDM_MAX_TOKENS   1024   /* T: positions per call (several blocks may be stacked) */
 #define BDM_MAX_HIDDEN   2048   /* H, multiple of 64 */
@@ -118,6 +128,10 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   I            expert intermediate size (multiple of 32, <= 1024)
  *   ws_gate, ws_up [I][H], ws_down [H][I] bf16: the shared expert; all three
  *                NULL = no shared expert (mixing NULL and non-NULL is an error)
+ *   weight_layout layout of w_gate, w_up, w_down and ws_*: BDM_LAYOUT_ROW_MAJOR,
+ *                or BDM_LAYOUT_MFMA_TILES with w_gate/w_up packed as one
+ *                [E*I][H] matrix, w_down as [E*H][I], ws_gate/ws_up as [I][H]
+ *                and ws_down as [H][I] (the router stays fp32 row-major)
  *   residual     [T][H] bf16 or NULL; may be the same pointer as y
  *   y            [T][H] bf16        output
  *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
@@ -134,6 +148,7 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int I,
                           const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                          int weight_layout,
                           const uint16_t* residual, uint16_t* y,
                           int32_t* topk_idx, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream);
@@ -165,7 +180,8 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  *
  * Arguments
  *   h            [T][H] bf16        final hidden states of the block
- *   w_head       [V][H] bf16        output head, vocabulary-row-major
+ *   w_head       [V][H] bf16        output head, vocabulary-row-major, or
+ *                                  packed (weight_layout = BDM_LAYOUT_MFMA_TILES)
  *   mask_id      0 <= mask_id < V   (V >= 2)
  *   threshold    commit threshold (finite, compared with >=)
  *   fallback     1: the progress rule above; 0: threshold only
@@ -176,9 +192,27 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  * Limits: T <= 1024, H multiple of 64 and <= 2048 (V unrestricted above 2).
  */
 BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
-                       int32_t mask_id, float threshold, int fallback,
+                       int weight_layout, int32_t mask_id, float threshold, int fallback,
                        int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bdm_packed_weight_elems -- size of the packed copy of a [rows][cols] bf16
+ * matrix: ceil(rows/16)*16*cols elements (rows padded to a multiple of 16).
+ *   n: HOST pointer.  cols must be a multiple of 32.  Pure host arithmetic.
+ */
+BDM_API int bdm_packed_weight_elems(long rows, int cols, size_t* n);
+
+/*
+ * bdm_pack_weights -- write the BDM_LAYOUT_MFMA_TILES copy of a row-major
+ * bf16 matrix src [rows][cols] into dst (bdm_packed_weight_elems elements;
+ * padding rows are zero).  Tile (rg, s) of 16 rows x 32 cols is 512
+ * consecutive elements: dst[((rg*(cols/32) + s)*64 + l)*8 + i] =
+ * src[16*rg + l%16][32*s + 8*(l/16) + i].  A one-time preparation step for
+ * the weight-streaming kernels; src and dst must not overlap.
+ */
+BDM_API int bdm_pack_weights(const uint16_t* src, long rows, int cols, uint16_t* dst,
+                             void* stream);
 
 /*
  * bdm_rmsnorm -- RMSNorm of each row, between MoE layers of a pre-norm stack.

@@ -36,17 +36,25 @@ def assert_bf16_close(gpu: torch.Tensor, ref_bits: np.ndarray, rows=None, what="
     return exact
 
 
-def run_moe(lib_mod, inp: synth.MoEInputs, renorm=True, residual=True, shared=True):
+def packed(lib_mod, t):
+    return None if t is None else lib_mod.bdm_pack_weights(t)
+
+
+def run_moe(lib_mod, inp: synth.MoEInputs, renorm=True, residual=True, shared=True, layout=0):
+    """layout 0: row-major weights; 1: the library packs them first (MFMA tiles)."""
     s = inp.shape
     dev = inp.x.device
+    W = (inp.w_gate, inp.w_up, inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
+    if layout:
+        W = tuple(packed(lib_mod, t) for t in W)
     idx = torch.full((s.T, s.k), -1, dtype=torch.int32, device=dev)
     w = torch.full((s.T, s.k), float("nan"), dtype=torch.float32, device=dev)
     y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
     lib_mod.bdm_moe_block_forward(
-        inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+        inp.x, inp.w_router, W[0], W[1], W[2], s.k,
         router_bias=inp.router_bias,
-        ws_gate=inp.ws_gate if shared else None, ws_up=inp.ws_up if shared else None,
-        ws_down=inp.ws_down if shared else None,
+        ws_gate=W[3] if shared else None, ws_up=W[4] if shared else None,
+        ws_down=W[5] if shared else None,
         residual=inp.residual if residual else None, y=y, topk_idx=idx, topk_w=w,
         renorm=renorm)
     torch.cuda.synchronize()
@@ -81,14 +89,15 @@ def compare_moe(y, idx, w, o, tokens=None):
     return assert_bf16_close(yy, o["y"], rows=np.flatnonzero(keep))
 
 
-def run_head(lib_mod, blk: synth.HeadInputs, threshold=0.95, fallback=True):
+def run_head(lib_mod, blk: synth.HeadInputs, threshold=0.95, fallback=True, layout=0):
     s = blk.shape
     dev = blk.h.device
+    w_head = packed(lib_mod, blk.w_head) if layout else blk.w_head
     tokens = blk.tokens.clone().to(dev)
     am = torch.full((s.T,), -1, dtype=torch.int32, device=dev)
     cf = torch.full((s.T,), float("nan"), dtype=torch.float32, device=dev)
     nc = torch.full((1,), -1, dtype=torch.int32, device=dev)
-    lib_mod.bdm_lm_head_unmask(blk.h, blk.w_head, s.mask_id, threshold, fallback, tokens,
+    lib_mod.bdm_lm_head_unmask(blk.h, w_head, s.mask_id, threshold, fallback, tokens,
                                argmax=am, conf=cf, n_committed=nc)
     torch.cuda.synchronize()
     return tokens, am, cf, nc

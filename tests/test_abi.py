@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert syms == sorted(["bdm_version", "bdm_status_string", "bdm_moe_workspace_bytes",
                            "bdm_moe_block_forward", "bdm_head_workspace_bytes",
-                           "bdm_lm_head_unmask", "bdm_rmsnorm"])
+                           "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
+                           "bdm_pack_weights"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -86,21 +87,22 @@ def test_moe_validation_rejects_before_launch(lib):
     A = _fake(1 << 20)        # 16-byte aligned fake address
     size = 1 << 30
     good = dict(x=A, T=32, H=2048, wr=A, bias=None, E=256, k=8, renorm=1, wg=A, wu=A, wd=A,
-                I=512, sg=A, su=A, sd=A, res=None, y=_fake(2 << 20), idx=None, w=None,
+                I=512, sg=A, su=A, sd=A, lay=0, res=None, y=_fake(2 << 20), idx=None, w=None,
                 ws=_fake(1 << 24), wsb=size, stream=None)
 
     def call(**kw):
         a = dict(good, **kw)
         return lib.bdm_moe_block_forward(a["x"], a["T"], a["H"], a["wr"], a["bias"], a["E"],
                                          a["k"], a["renorm"], a["wg"], a["wu"], a["wd"], a["I"],
-                                         a["sg"], a["su"], a["sd"], a["res"], a["y"], a["idx"],
-                                         a["w"], a["ws"], a["wsb"], a["stream"])
+                                         a["sg"], a["su"], a["sd"], a["lay"], a["res"], a["y"],
+                                         a["idx"], a["w"], a["ws"], a["wsb"], a["stream"])
 
     assert call(x=None) == -1
     assert call(y=None) == -1
     assert call(ws=None) == -1
     assert call(sd=None) == -1                    # shared trio must be all or none
     assert call(renorm=2) == -1
+    assert call(lay=2) == -1
     assert call(k=0) == -1
     assert call(k=300) == -1
     assert call(H=100) == -2
@@ -117,12 +119,12 @@ def test_head_and_rmsnorm_validation(lib):
     W = _fake(1 << 24)
 
     def head(**kw):
-        a = dict(h=A, T=32, H=2048, w=A, V=248320, mask=151669, thr=0.95, fb=1, tok=T,
+        a = dict(h=A, T=32, H=2048, w=A, V=248320, lay=0, mask=151669, thr=0.95, fb=1, tok=T,
                  am=None, cf=None, nc=None, ws=W, wsb=1 << 30, st=None)
         a.update(kw)
-        return lib.bdm_lm_head_unmask(a["h"], a["T"], a["H"], a["w"], a["V"], a["mask"], a["thr"],
-                                      a["fb"], a["tok"], a["am"], a["cf"], a["nc"], a["ws"],
-                                      a["wsb"], a["st"])
+        return lib.bdm_lm_head_unmask(a["h"], a["T"], a["H"], a["w"], a["V"], a["lay"],
+                                      a["mask"], a["thr"], a["fb"], a["tok"], a["am"], a["cf"],
+                                      a["nc"], a["ws"], a["wsb"], a["st"])
 
     assert head(h=None) == -1
     assert head(tok=None) == -1
@@ -130,9 +132,24 @@ def test_head_and_rmsnorm_validation(lib):
     assert head(mask=-1) == -1
     assert head(thr=float("nan")) == -1
     assert head(fb=3) == -1
+    assert head(lay=5) == -1
     assert head(T=0) == -1
     assert head(T=4096) == -2
     assert head(wsb=16) == -3
     assert lib.bdm_rmsnorm(None, None, 1e-6, 32, 2048, A, None) == -1
     assert lib.bdm_rmsnorm(A, None, -1.0, 32, 2048, A, None) == -1
     assert lib.bdm_rmsnorm(A, None, 1e-6, 32, 100, A, None) == -2
+
+
+def test_packed_weight_size_and_pack_validation(lib):
+    from block_diffusion_moe_amd import binding as b
+    assert b.bdm_packed_weight_elems(248320, 2048) == 248320 * 2048
+    assert b.bdm_packed_weight_elems(17, 64) == 32 * 64           # rows padded to 16
+    assert b.bdm_packed_weight_elems(256 * 512, 2048) == 256 * 512 * 2048
+    n = ctypes.c_size_t(0)
+    assert lib.bdm_packed_weight_elems(16, 48, ctypes.byref(n)) == -1   # cols % 32
+    assert lib.bdm_packed_weight_elems(0, 64, ctypes.byref(n)) == -1
+    A, B = _fake(1 << 20), _fake(1 << 26)
+    assert lib.bdm_pack_weights(None, 16, 64, B, None) == -1
+    assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 20) + 64), None) == -1   # overlap
+    assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 26) + 8), None) == -1    # misaligned

@@ -42,15 +42,43 @@ def _to_dev(inp: synth.MoEInputs) -> synth.MoEInputs:
                            f(inp.ws_up), f(inp.ws_down), f(inp.residual))
 
 
+LAYOUTS = pytest.mark.parametrize("layout", [0, 1], ids=["rowmajor", "packed"])
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 32), (17, 64), (1000, 96), (48, 2048)])
+def test_pack_weights_bit_exact(bdm, rows, cols):
+    """The packed copy is exactly the documented permutation (checked with an
+    independent numpy index computation), with zero padding rows."""
+    say(f"case pack rows={rows} cols={cols}")
+    g = torch.Generator(device=DEV).manual_seed(rows * cols)
+    w = torch.randn(rows, cols, generator=g, device=DEV).to(torch.bfloat16)
+    p = bdm.bdm_pack_weights(w)
+    torch.cuda.synchronize()
+    got = synth.bf16_bits(p.data)
+    src = synth.bf16_bits(w)
+    rp = (rows + 15) // 16 * 16
+    full = np.zeros((rp, cols), dtype=np.uint16)
+    full[:rows] = src
+    # element (r, k) goes to tile (r//16, k//32), lane (k%32)//8*16 + r%16, item k%8
+    r = np.arange(rp)[:, None]
+    k = np.arange(cols)[None, :]
+    dst = (((r // 16) * (cols // 32) + k // 32) * 64 + ((k % 32) // 8) * 16 + r % 16) * 8 + k % 8
+    want = np.empty(rp * cols, dtype=np.uint16)
+    want[dst.reshape(-1)] = full.reshape(-1)
+    assert got.shape[0] == rp * cols
+    assert np.array_equal(got, want)
+
+
+@LAYOUTS
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
 @pytest.mark.parametrize("variant", ["plain", "residual", "noshared", "norenorm", "bias"])
-def test_moe_tiny(bdm, seed, variant):
-    say(f"case moe tiny seed={seed} variant={variant}")
+def test_moe_tiny(bdm, seed, variant, layout):
+    say(f"case moe tiny seed={seed} variant={variant} layout={layout}")
     inp = _to_dev(synth.moe_inputs(synth.TINY, seed=seed, block_seed=seed + 1,
                                    with_residual=variant == "residual",
                                    zipf_s=1.1 if variant == "bias" else None))
     kw = dict(renorm=variant != "norenorm", shared=variant != "noshared")
-    y, idx, w = run_moe(bdm, inp, **kw)
+    y, idx, w = run_moe(bdm, inp, layout=layout, **kw)
     o = oracle_moe(inp, **kw)
     compare_moe(y, idx, w, o)
 
@@ -69,23 +97,25 @@ SHAPES = [
 ]
 
 
+@LAYOUTS
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "T%d_H%d_E%d_I%d_k%d" % s)
-def test_moe_shapes(bdm, shape):
+def test_moe_shapes(bdm, shape, layout):
     T, H, E, I, k = shape
-    say(f"case moe shape T={T} H={H} E={E} I={I} k={k}")
+    say(f"case moe shape T={T} H={H} E={E} I={I} k={k} layout={layout}")
     s = synth.MoEShape(T=T, H=H, E=E, I=I, k=k)
     inp = synth.moe_inputs(s, seed=T + E, block_seed=k, device=DEV, with_residual=True)
-    y, idx, w = run_moe(bdm, inp)
+    y, idx, w = run_moe(bdm, inp, layout=layout)
     o = oracle_moe(inp, lazy=True)
     compare_moe(y, idx, w, o)
 
 
-def test_moe_clover_layer_full(bdm):
+@LAYOUTS
+def test_moe_clover_layer_full(bdm, layout):
     """One Clover-shaped layer (H 2048, 256 experts, I 512, top-8, shared),
     32-token block, every output element against the oracle."""
-    say("case moe clover layer T=32 full")
+    say(f"case moe clover layer T=32 full layout={layout}")
     inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=1, device=DEV, with_residual=True)
-    y, idx, w = run_moe(bdm, inp)
+    y, idx, w = run_moe(bdm, inp, layout=layout)
     o = oracle_moe(inp, lazy=True)
     say(f"  touched experts: {o['touched']}")
     compare_moe(y, idx, w, o)
@@ -105,13 +135,14 @@ def test_moe_clover_layer_inplace_residual(bdm):
     assert torch.equal(buf.view(torch.int16), y_sep.view(torch.int16))
 
 
-def test_moe_skew_sampled(bdm):
+@LAYOUTS
+def test_moe_skew_sampled(bdm, layout):
     """Eight 32-token blocks (T = 256) with the log-Zipf router offset: the
     routing of every token, and the outputs of a seeded sample of 24 tokens
     (tokens are independent through the layer)."""
-    say("case moe skew T=256 sampled")
+    say(f"case moe skew T=256 sampled layout={layout}")
     inp = synth.skew_inputs(seed=0, block_seed=1, device=DEV)
-    y, idx, w = run_moe(bdm, inp, residual=False)
+    y, idx, w = run_moe(bdm, inp, residual=False, layout=layout)
     tokens = np.sort(np.random.default_rng(0).choice(256, 24, replace=False))
     o = oracle_moe(inp, residual=False, tokens=tokens, lazy=True)
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=256)
@@ -120,9 +151,9 @@ def test_moe_skew_sampled(bdm):
 
 
 def test_moe_repeatable_bitwise(bdm):
-    say("case moe repeatability")
+    say("case moe repeatability (and row-major == packed bits)")
     inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=3, device=DEV, with_residual=True)
-    outs = [run_moe(bdm, inp) for _ in range(3)]
+    outs = [run_moe(bdm, inp) for _ in range(2)] + [run_moe(bdm, inp, layout=1)]
     for y, idx, w in outs[1:]:
         assert torch.equal(y.view(torch.int16), outs[0][0].view(torch.int16))
         assert torch.equal(idx, outs[0][1])
@@ -164,61 +195,65 @@ def test_uniform_router_ties_on_gpu(bdm):
 # Head + unmask
 # --------------------------------------------------------------------------
 
+@LAYOUTS
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("variant", ["plain", "committed", "maskboost", "all_boosted"])
-def test_head_tiny(bdm, seed, variant):
-    say(f"case head tiny seed={seed} variant={variant}")
+def test_head_tiny(bdm, seed, variant, layout):
+    say(f"case head tiny seed={seed} variant={variant} layout={layout}")
     s = synth.TINY_HEAD
     W = synth.head_weights(s, seed).to(DEV)
     blk = synth.head_block(s, W, block_seed=seed + 1, n_boost=3,
                            committed_rows=3 if variant == "committed" else 0,
                            mask_boost_rows=2 if variant == "maskboost" else 0,
                            boost_all=variant == "all_boosted")
-    out = run_head(bdm, blk)
+    out = run_head(bdm, blk, layout=layout)
     o = oracle_head(blk)
     compare_head(out, o, blk.tokens.cpu().numpy())
 
 
+@LAYOUTS
 @pytest.mark.parametrize("V,T", [(2, 3), (17, 5), (1000, 33), (4097, 40), (70001, 64)])
-def test_head_ragged(bdm, V, T):
-    say(f"case head ragged V={V} T={T}")
+def test_head_ragged(bdm, V, T, layout):
+    say(f"case head ragged V={V} T={T} layout={layout}")
     s = synth.HeadShape(T=T, H=256, V=V, mask_id=V // 3)
     W = synth.head_weights(s, V).to(DEV)
     blk = synth.head_block(s, W, block_seed=T, n_boost=min(T, 4), committed_rows=1)
-    out = run_head(bdm, blk)
+    out = run_head(bdm, blk, layout=layout)
     o = oracle_head(blk)
     compare_head(out, o, blk.tokens.cpu().numpy())
 
 
-def test_head_clover_full(bdm):
+@LAYOUTS
+def test_head_clover_full(bdm, layout):
     """Untied 248,320 x 2048 head, 32 positions, 10 boosted rows (+20) among
     flat ones: every row's argmax/conf and the commit decisions."""
-    say("case head clover full")
+    say(f"case head clover full layout={layout}")
     s = synth.HEAD
     W = synth.head_weights(s, 0, device=DEV)
     blk = synth.head_block(s, W, block_seed=1, n_boost=10)
-    out = run_head(bdm, blk)
+    out = run_head(bdm, blk, layout=layout)
     o = oracle_head(blk)
     assert o["n_committed"] == 10
     compare_head(out, o, blk.tokens.cpu().numpy())
     # a second block: rows already committed, the mask token boosted in two rows
     blk2 = synth.head_block(s, W, block_seed=2, n_boost=10, committed_rows=5, mask_boost_rows=2)
-    out2 = run_head(bdm, blk2)
+    out2 = run_head(bdm, blk2, layout=layout)
     compare_head(out2, oracle_head(blk2), blk2.tokens.cpu().numpy())
 
 
-def test_head_clover_fallback(bdm):
+@LAYOUTS
+def test_head_clover_fallback(bdm, layout):
     """Every row boosted by only +12 over 248,319 flat competitors: no row
     reaches 0.95, so exactly one row (the most confident) commits."""
     say("case head clover fallback")
     s = synth.HEAD
     W = synth.head_weights(s, 0, device=DEV)
     blk = synth.head_block(s, W, block_seed=4, boost=12.0, boost_all=True)
-    out = run_head(bdm, blk)
+    out = run_head(bdm, blk, layout=layout)
     o = oracle_head(blk)
     assert o["n_committed"] == 1
     compare_head(out, o, blk.tokens.cpu().numpy())
-    out_nf = run_head(bdm, blk, fallback=False)
+    out_nf = run_head(bdm, blk, fallback=False, layout=layout)
     assert int(out_nf[3].item()) == 0
     assert torch.equal(out_nf[0].cpu(), blk.tokens.cpu())
 
@@ -230,7 +265,8 @@ def test_head_repeatable_bitwise(bdm):
     blk = synth.head_block(s, W, block_seed=7, n_boost=10)
     a = run_head(bdm, blk)
     b = run_head(bdm, blk)
-    for x, z in zip(a, b):
+    c = run_head(bdm, blk, layout=1)
+    for x, z in list(zip(a, b)) + list(zip(a, c)):
         assert torch.equal(x.view(torch.int32), z.view(torch.int32))
 
 
