@@ -5,7 +5,8 @@ A step is one pass of the whole hot path over one 32-slot block:
 
     xn = RMSNorm(x)                                   bdm_rmsnorm
     x' = x + MoE(xn)   (Clover-shaped layer)          bdm_moe_block_forward
-    tokens = unmask(head(x'))                         bdm_lm_head_unmask
+    stats = head(x')   (online-softmax partials)      bdm_lm_head_stats
+    tokens = unmask(merge(stats))                     bdm_unmask_from_stats
 
 with H 2048, 256 routed experts (SwiGLU 2048->512->2048, bf16) plus one
 shared expert, top-8 with renormalised weights, the untied 248,320 x 2048
@@ -17,7 +18,11 @@ weight sets (router, experts, shared expert, head) and token blocks.
 Output: one JSON line (rank 0).  `value` is block-tokens/s of the whole
 step; the MoE layer alone and the head alone are reported beside it, each
 with its algorithmic HBM bytes (touched experts x 6,291,456 B; head
-1,017,118,720 B) and the fraction of the 8 TB/s HBM peak.
+1,017,118,720 B) and the fraction of the 8 TB/s HBM peak.  The roofline
+entry is the head GEMM kernel (one launch per step, the largest single
+kernel), timed with HIP events recorded on the stream it runs on; its HBM
+traffic comes from the committed rocprofv3 counter summary when that was
+taken on the current kernel source, else it is null.
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0
+PMC_SUMMARY = os.path.join(HERE, "profiles", "head_tile_kernel_clover_head.traffic.md")
 EXPERT_BYTES = 3 * 2048 * 512 * 2        # gate + up + down, bf16
 HEAD_BYTES = 248320 * 2048 * 2
 
@@ -41,8 +47,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sets", type=int, default=4, help="rotated weight sets / token blocks")
-    p.add_argument("--cpu-tokens", type=int, default=4,
-                   help="tokens of one block the CPU oracle runs for cpu_baseline (0: skip)")
+    p.add_argument("--cpu-blocks", type=int, default=4,
+                   help="weight sets whose blocks the CPU oracle cycles over for cpu_baseline, "
+                        "at least 10 s of oracle time (0: skip)")
     p.add_argument("--layout", type=int, default=1,
                    help="weight layout: 1 = packed MFMA tiles (packed once, untimed), 0 = row-major")
     return p.parse_args()
@@ -90,7 +97,10 @@ def main():
 
     T, H = L.T, L.H
     moe_ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(T, H, L.I, L.E, L.k, True), dev)
-    head_ws = bdm.workspace(bdm.bdm_head_workspace_bytes(T, H, HS.V), dev)
+    parts = bdm.bdm_head_stat_parts()
+    st_m = torch.empty((T, parts), dtype=torch.float32, device=dev)
+    st_s = torch.empty_like(st_m)
+    st_a = torch.empty((T, parts), dtype=torch.int32, device=dev)
     xn = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     xs = [s[0].x for s in sets]                  # per-set block input (residual stream)
     xo = [torch.empty_like(s[0].x) for s in sets]  # per-set layer output = head input
@@ -112,10 +122,13 @@ def main():
                                   residual=x, y=xo[r], topk_idx=idx, ws=moe_ws)
         if ev is not None:
             ev[2].record()
-        bdm.bdm_lm_head_unmask(xo[r], w_head, HS.mask_id, 0.95, True, tokens[r],
-                               n_committed=nc, ws=head_ws)
+        bdm.bdm_lm_head_stats(xo[r], w_head, HS.mask_id, st_m, st_s, st_a)
         if ev is not None:
             ev[3].record()
+        bdm.bdm_unmask_from_stats(st_m, st_s, st_a, HS.mask_id, 0.95, True, tokens[r],
+                                  n_committed=nc)
+        if ev is not None:
+            ev[4].record()
 
     # touched experts per set (routing of each set's first step input)
     touched = []
@@ -134,7 +147,7 @@ def main():
     torch.cuda.synchronize()
 
     # per-call timing (events between the three calls of every step)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -149,7 +162,9 @@ def main():
     ms_step = total_ms / args.steps
     norm_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     moe_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    head_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    gemm_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    merge_us = 1e3 * float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    head_us = gemm_us + merge_us
 
     # untimed-by-events replay of the same steps (no event records in between)
     torch.cuda.synchronize()
@@ -166,21 +181,15 @@ def main():
     head_gbs = HEAD_BYTES / (head_us * 1e-6) / 1e9
     value = T / (ms_step_plain * 1e-3)
 
-    dominant = "head" if head_us >= moe_us else "moe"
-    if dominant == "head":
-        roof = {"bound": "hbm", "kernel": "bdm_lm_head_unmask (head_tile_kernel + head_merge_kernel)",
-                "achieved": round(head_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(head_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(head_us, 2)}
-    else:
-        roof = {"bound": "hbm", "kernel": "bdm_moe_block_forward (router..combine)",
-                "achieved": round(moe_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(moe_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "bytes_per_launch": int(moe_bytes), "us_per_launch": round(moe_us, 2)}
+    gemm_gbs = HEAD_BYTES / (gemm_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": "head_tile_kernel (bdm_lm_head_stats)",
+            "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": head_traffic(),
+            "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_us, 2)}
 
     cpu = None
-    if args.cpu_tokens > 0:
-        cpu = cpu_baseline(sets[0], args.cpu_tokens)
+    if args.cpu_blocks > 0:
+        cpu = cpu_baseline(sets[:args.cpu_blocks])
 
     out = {
         "metric": "denoise-block tokens/s per MoE layer + achieved HBM GB/s (% of MI355X peak)",
@@ -206,8 +215,9 @@ def main():
         "moe_layer": {"us": round(moe_us, 2), "block_tokens_per_s": round(T / (moe_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
                       "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4)},
-        "head_unmask": {"us": round(head_us, 2), "bytes": HEAD_BYTES, "GB_s": round(head_gbs, 1),
-                        "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
+        "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),
+                        "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
+                        "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
         "rmsnorm_us": round(norm_us, 2),
         "ms_per_step_with_events": round(ms_step, 4),
         "wall_s_timed": round(wall, 3),
@@ -217,30 +227,59 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(s, ntok):
-    """The CPU oracle (as it stands) on the first `ntok` tokens of one block:
-    the same step (RMSNorm, MoE layer, head + unmask) for those tokens only.
-    Scaled to block-tokens/s."""
-    import numpy as np
+def head_traffic():
+    """HBM bytes per head_tile_kernel launch from the committed counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing or
+    was taken on other kernel sources."""
+    try:
+        with open(PMC_SUMMARY) as fh:
+            txt = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for ln in txt.splitlines():
+        if ln.startswith("<!--") and "=" in ln:
+            k, v = ln.strip("<!-> \n").split("=", 1)
+            vals[k.strip()] = v.strip()
+    from block_diffusion_moe_amd.traffic import kernel_source_digest
+    if vals.get("source_sha256") != kernel_source_digest() or "traffic_bytes" not in vals:
+        return None
+    return int(float(vals["traffic_bytes"]))
 
+
+def cpu_baseline(blocks, min_s=10.0, max_blocks=12):
+    """The CPU oracle (as it stands) on whole blocks of the rotated sets: the
+    same step (RMSNorm, MoE layer, head + unmask) for all 32 slots of a block,
+    with that block's own weights, block after block (cycling over the sets)
+    until at least `min_s` seconds of oracle time or `max_blocks` blocks.
+    Host copies of the weights are made outside the timed region.  Scaled to
+    block-tokens/s."""
     import synth
     from oracle import head as ohead, moe as omoe, norm as onorm
 
-    inp, w_head, blk = s
-    h = synth.moe_host(inp, lazy=False)
-    xb = synth.bf16_bits(inp.x)[:ntok]
-    wh = synth.bf16_bits(w_head)
     threads = _blas_threads()
-    t0 = time.perf_counter()
-    xn = onorm.rmsnorm(xb, 1e-6)
-    r = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
-                       h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)
-    ohead.head_unmask(r["y"], wh, blk.tokens.cpu().numpy()[:ntok], synth.HEAD.mask_id, 0.95)
-    dt = time.perf_counter() - t0
+    host = {}
+    dt, ntok, nblk = 0.0, 0, 0
+    while nblk < max_blocks and (dt < min_s or nblk == 0):
+        r = nblk % len(blocks)
+        inp, w_head, blk = blocks[r]
+        if r not in host:
+            host[r] = (synth.moe_host(inp, lazy=False), synth.bf16_bits(inp.x),
+                       synth.bf16_bits(w_head), blk.tokens.cpu().numpy())
+        h, xb, wh, tok = host[r]
+        t0 = time.perf_counter()
+        xn = onorm.rmsnorm(xb, 1e-6)
+        y = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                           h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)["y"]
+        ohead.head_unmask(y, wh, tok, synth.HEAD.mask_id, 0.95)
+        dt += time.perf_counter() - t0
+        ntok += xb.shape[0]
+        nblk += 1
     return {"value": round(ntok / dt, 4), "unit": "block-tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{ntok} tokens of one 32-slot block through RMSNorm + MoE layer + head/"
-                      f"unmask (numpy float64 oracle), {dt:.1f} s; weights copied to host "
+            "sample": f"{nblk} whole 32-slot blocks ({ntok} tokens, cycling over "
+                      f"{min(nblk, len(blocks))} weight sets) through RMSNorm + MoE layer + "
+                      f"head/unmask (numpy float64 oracle), {dt:.1f} s; weights copied to host "
                       f"before the timed region"}
 
 

@@ -34,6 +34,11 @@ _SIGS = {
     "bdm_head_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
                                     _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_head_stat_parts": (_c_int, [ctypes.POINTER(_c_int)]),
+    "bdm_lm_head_stats": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
+                                   ctypes.c_int32, _vp, _vp, _vp, _c_int, _vp]),
+    "bdm_unmask_from_stats": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, ctypes.c_int32,
+                                       _c_float, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "bdm_packed_weight_elems": (_c_int, [ctypes.c_long, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_pack_weights": (_c_int, [_vp, ctypes.c_long, _c_int, _vp, _vp]),
     "bdm_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
@@ -238,6 +243,54 @@ def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool
                                    _ptr(conf), _ptr(n_committed), _ptr(ws), ws.numel(),
                                    _stream(stream))
     _raise("bdm_lm_head_unmask", st)
+    return tokens
+
+
+def bdm_head_stat_parts() -> int:
+    n = _c_int(0)
+    _raise("bdm_head_stat_parts", load().bdm_head_stat_parts(ctypes.byref(n)))
+    return n.value
+
+
+def bdm_lm_head_stats(h, w_head, mask_id: int, stat_max, stat_sum, stat_arg, vocab_offset=0,
+                      stream=None):
+    """Phase 1 of the head over the vocabulary rows [vocab_offset, vocab_offset + V) of
+    w_head; stat_* are [T][stride] views whose first bdm_head_stat_parts() columns are
+    written (pass column slices of a wider array to place several shards)."""
+    T, H = h.shape
+    V = w_head.shape[0]
+    dev = h.device
+    _check(h, "h", torch.bfloat16, (T, H))
+    _check(w_head, "w_head", torch.bfloat16, (V, H), dev)
+    for t, nm, dt in ((stat_max, "stat_max", torch.float32), (stat_sum, "stat_sum", torch.float32),
+                      (stat_arg, "stat_arg", torch.int32)):
+        if t.dtype != dt or t.device != dev or t.dim() != 2 or t.shape[0] != T or t.stride(1) != 1:
+            raise ValueError(f"{nm}: expected a [T][*] {dt} device view with unit column stride")
+    stride = stat_max.stride(0)
+    if stat_sum.stride(0) != stride or stat_arg.stride(0) != stride:
+        raise ValueError("stat_*: row strides differ")
+    layout = BDM_LAYOUT_MFMA_TILES if isinstance(w_head, Packed) else BDM_LAYOUT_ROW_MAJOR
+    _raise("bdm_lm_head_stats", load().bdm_lm_head_stats(
+        _ptr(h), T, H, _ptr(w_head), V, int(vocab_offset), layout, int(mask_id), _ptr(stat_max),
+        _ptr(stat_sum), _ptr(stat_arg), stride, _stream(stream)))
+
+
+def bdm_unmask_from_stats(stat_max, stat_sum, stat_arg, mask_id: int, threshold: float,
+                          fallback: bool, tokens, argmax=None, conf=None, n_committed=None,
+                          stream=None):
+    """Phase 2: merge the [T][parts] triples (all columns of the given views) and
+    apply the commit rule to tokens."""
+    T, parts = stat_max.shape
+    dev = tokens.device
+    _check(tokens, "tokens", torch.int32, (T,), dev)
+    _check(argmax, "argmax", torch.int32, (T,), dev)
+    _check(conf, "conf", torch.float32, (T,), dev)
+    _check(n_committed, "n_committed", torch.int32, (1,), dev)
+    stride = stat_max.stride(0)
+    _raise("bdm_unmask_from_stats", load().bdm_unmask_from_stats(
+        _ptr(stat_max), _ptr(stat_sum), _ptr(stat_arg), T, parts, stride, int(mask_id),
+        float(threshold), int(fallback), _ptr(tokens), _ptr(argmax), _ptr(conf),
+        _ptr(n_committed), _stream(stream)))
     return tokens
 
 

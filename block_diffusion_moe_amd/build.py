@@ -2,7 +2,9 @@
 
     python -m block_diffusion_moe_amd.build
 
-Compiles every csrc/*.hip into one shared library next to this file.  The
+Compiles every csrc/*.hip into one shared library next to this file, and
+csrc/calib/*.hip (the copy kernel that calibrates HBM traffic counters)
+into a second one.  The
 library links the HIP runtime by soname (libamdhip64.so.7), so inside a
 process that has imported torch it binds to the runtime torch already
 loaded: one runtime, one set of streams and device pointers.
@@ -20,6 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbdmoe.so")
+CAL_LIB = os.path.join(HERE, "libbdmcal.so")   # counter-calibration copy kernel
 ARCH = os.environ.get("BDM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,9 +46,16 @@ def sources():
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile the library to `out`.  `defines` are extra -D macros (kernel
-    tuning knobs such as BDM_HEAD_UNROLL); the defaults are the tuned ones."""
-    srcs = sources()
+    """Compile the library to `out` (and the calibration library beside the
+    default one).  `defines` are extra -D macros (kernel tuning knobs); the
+    defaults are the tuned ones."""
+    _compile(sources(), out, defines, verbose)
+    if out == LIB:
+        _compile(sorted(glob.glob(os.path.join(CSRC, "calib", "*.hip"))), CAL_LIB, (), verbose)
+    return out
+
+
+def _compile(srcs, out, defines, verbose):
     tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], f"-I{INCLUDE}", f"-I{CSRC}", *srcs,
            "-o", tmp]
@@ -61,7 +71,6 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
     os.replace(tmp, out)
-    return out
 
 
 if __name__ == "__main__":

@@ -210,9 +210,57 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   bdm::HeadParts parts;
   head_layout(T, static_cast<char*>(workspace), &parts);
   parts.grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  bdm::launch_head(h, T, H, w_head, V, weight_layout, mask_id, threshold, fallback, tokens, argmax,
-                   conf, n_committed, parts, static_cast<hipStream_t>(stream));
+  bdm::launch_head_stats(h, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s, parts.a,
+                         parts.grid, parts.grid, s);
+  bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
+                     fallback, tokens, argmax, conf, n_committed, s);
+  return last_hip_status();
+}
+
+int bdm_head_stat_parts(int* parts) {
+  if (!parts) return BDM_ERR_INVALID_ARG;
+  int cus = 0;
+  const int st = device_setup(&cus);
+  if (st != BDM_OK) return st;
+  *parts = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
+  return BDM_OK;
+}
+
+int bdm_lm_head_stats(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
+                      int vocab_offset, int weight_layout, int32_t mask_id, float* stat_max,
+                      float* stat_sum, int32_t* stat_arg, int stat_stride, void* stream) {
+  if (!h || !w_head || !stat_max || !stat_sum || !stat_arg) return BDM_ERR_INVALID_ARG;
+  int st = check_head_shape(T, H, V < 2 ? 2 : V);
+  if (st != BDM_OK) return st;
+  if (V < 1 || vocab_offset < 0 || vocab_offset > 0x7fffffff - V) return BDM_ERR_INVALID_ARG;
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+    return BDM_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_head)) return BDM_ERR_INVALID_ARG;
+  int parts = 0;
+  st = bdm_head_stat_parts(&parts);
+  if (st != BDM_OK) return st;
+  if (stat_stride < parts) return BDM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  bdm::launch_head_stats(h, T, H, w_head, V, vocab_offset, weight_layout, mask_id, stat_max,
+                         stat_sum, stat_arg, stat_stride, parts, static_cast<hipStream_t>(stream));
+  return last_hip_status();
+}
+
+int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum, const int32_t* stat_arg,
+                          int T, int parts, int stat_stride, int32_t mask_id, float threshold,
+                          int fallback, int32_t* tokens, int32_t* argmax, float* conf,
+                          int32_t* n_committed, void* stream) {
+  if (!stat_max || !stat_sum || !stat_arg || !tokens) return BDM_ERR_INVALID_ARG;
+  if (T < 1 || parts < 1 || stat_stride < parts) return BDM_ERR_INVALID_ARG;
+  if (T > BDM_MAX_TOKENS) return BDM_ERR_UNSUPPORTED_SHAPE;
+  if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
+    return BDM_ERR_INVALID_ARG;
+  if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  bdm::launch_unmask(stat_max, stat_sum, stat_arg, T, parts, stat_stride, mask_id, threshold,
+                     fallback, tokens, argmax, conf, n_committed, static_cast<hipStream_t>(stream));
   return last_hip_status();
 }
 

@@ -43,9 +43,9 @@ size_t head_lds_bytes(int H) {
 // written as one partial per (token, workgroup).  U = k-steps per batch.
 template <int U>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
-    const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int layout,
-    int32_t mask_id, int tok0, int ntok, float* __restrict__ pm, float* __restrict__ ps,
-    int32_t* __restrict__ pa) {
+    const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
+    int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
+    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride) {
   extern __shared__ __align__(16) unsigned char head_smem[];
   const int HP = H + kHeadPad;
   uint16_t* hs = reinterpret_cast<uint16_t*>(head_smem);
@@ -163,12 +163,12 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 #pragma unroll
           for (int q = 0; q < kHeadGroups; ++q) {
             const int v = (ch * kHeadGroups + q) * 16 + c;
-            if (v < V && v != mask_id) {
+            if (v < V && v + voff != mask_id) {
               const float l = acc[q][mt][i];
               if (l > s.m) {
                 s.s = (s.m == -INFINITY ? 0.0f : s.s * expf(s.m - l)) + 1.0f;
                 s.m = l;
-                s.a = v;
+                s.a = v + voff;
               } else {
                 s.s += expf(l - s.m);
               }
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   if (tid < ntok) {
     SoftStat s = red[tid];
     for (int wv = 1; wv < kHeadWaves; ++wv) s = softstat_merge(s, red[wv * kHeadTokChunk + tid]);
-    const size_t o = static_cast<size_t>(tok0 + tid) * gridDim.x + blockIdx.x;
+    const size_t o = static_cast<size_t>(tok0 + tid) * pstride + blockIdx.x;
     pm[o] = s.m;
     ps[o] = s.s;
     pa[o] = s.a;
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 // and one wave applies the commit rule over the block.
 __global__ __launch_bounds__(1024) void head_merge_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const int32_t* __restrict__ pa,
-    int T, int nparts, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
+    int T, int nparts, int pstride, int32_t mask_id, float threshold, int fallback,
+    int32_t* tokens,
     int32_t* __restrict__ argmax_out, float* __restrict__ conf_out,
     int32_t* __restrict__ n_committed) {
   extern __shared__ float smem[];
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   for (int t0 = 0; t0 < T; t0 += blockDim.x >> 4) {
     const int t = t0 + (tid >> 4);
     const bool on = t < T;           // row-uniform
-    const size_t base = static_cast<size_t>(on ? t : 0) * nparts;
+    const size_t base = static_cast<size_t>(on ? t : 0) * pstride;
     SoftStat st = softstat_empty();
     for (int i0 = 0; i0 < nparts; i0 += 16 * 16) {
       SoftStat part[16];
@@ -296,34 +297,31 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   if (lane == 0 && n_committed) *n_committed = ncommit;
 }
 
-void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int layout,
-                 int32_t mask_id, float threshold, int fallback, int32_t* tokens, int32_t* argmax,
-                 float* conf, int32_t* n_committed, const HeadParts& parts, hipStream_t s) {
-  const int grid = parts.grid;
+void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V, int voff,
+                       int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
+                       int pstride, int grid, hipStream_t s) {
   const size_t lds = head_lds_bytes(H);
-  const bool u4 = false;   // two k-steps per batch: both ping-pong buffers stay in VGPRs
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
-    if (u4)
-      head_tile_kernel<4><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, layout, mask_id, t0, n, parts.m,
-                                                            parts.s, parts.a);
-    else
-      head_tile_kernel<2><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, layout, mask_id, t0, n, parts.m,
-                                                            parts.s, parts.a);
+    head_tile_kernel<2><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0,
+                                                          n, pm, ps, pa, pstride);
   }
+}
+
+void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
+                   int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
+                   int32_t* argmax, float* conf, int32_t* n_committed, hipStream_t s) {
   head_merge_kernel<<<1, 1024, static_cast<size_t>(T) * 12, s>>>(
-      parts.m, parts.s, parts.a, T, grid, mask_id, threshold, fallback, tokens, argmax, conf,
+      pm, ps, pa, T, parts, pstride, mask_id, threshold, fallback, tokens, argmax, conf,
       n_committed);
 }
 
 int head_prepare() {
   const int lds = static_cast<int>(head_lds_bytes(BDM_MAX_HIDDEN));
-  const bool ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<4>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<2>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
-  return ok ? 0 : -1;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<2>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess
+             ? 0
+             : -1;
 }
 
 }  // namespace bdm

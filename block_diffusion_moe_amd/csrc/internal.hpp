@@ -53,9 +53,13 @@ struct HeadParts {
 size_t head_lds_bytes(int H);
 int head_prepare();   // one-time kernel attribute set-up; 0 on success
 
-void launch_head(const uint16_t* h, int T, int H, const uint16_t* w, int V, int layout,
-                 int32_t mask_id, float threshold, int fallback, int32_t* tokens, int32_t* argmax,
-                 float* conf, int32_t* n_committed, const HeadParts& parts, hipStream_t s);
+void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V, int voff,
+                       int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
+                       int pstride, int grid, hipStream_t s);
+
+void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
+                   int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
+                   int32_t* argmax, float* conf, int32_t* n_committed, hipStream_t s);
 
 void launch_pack(const uint16_t* src, long R, int K, uint16_t* dst, hipStream_t s);
 

@@ -1,0 +1,159 @@
+"""HBM traffic per kernel launch from rocprofv3 counter runs.
+
+Two counter passes (FETCH_SIZE, then WRITE_SIZE, each in KiB per dispatch)
+over the benchmark, and the same two passes over a plain copy kernel of known
+size, give calibrated bytes per launch:
+
+    traffic = FETCH_SIZE * (copy bytes read / copy FETCH_SIZE)
+            + WRITE_SIZE * (copy bytes written / copy WRITE_SIZE)
+
+FETCH_SIZE weighs memory requests by an assumed size, so the factor depends
+on the request mix: the calibration copy (libbdmcal.so) reads with the same
+16-byte non-temporal wave-contiguous loads as the weight-streaming kernels.
+A torch elementwise copy (ordinary loads) is measured beside it and its
+factor is reported for comparison only.
+
+    python -m block_diffusion_moe_amd.traffic copy
+        the two copies (1 GiB read + 1 GiB written each), run under
+        `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` for the factors
+    python -m block_diffusion_moe_amd.traffic summarize --fetch DIR --write DIR \\
+        --cal-fetch DIR --cal-write DIR --out FILE [--command TEXT]
+        writes a markdown summary with a per-kernel table; its first lines are
+        `<!-- key = value -->` records (source digest, traffic of the head GEMM
+        kernel) that bench.py reads back.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+HEAD_KERNEL = "head_tile_kernel"
+HEAD_SOURCES = ("head.hip", "device.hpp", "internal.hpp")
+
+
+def kernel_source_digest(files=HEAD_SOURCES) -> str:
+    """sha256 over the csrc files a kernel is compiled from."""
+    d = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            d.update(fh.read())
+    return d.hexdigest()
+
+
+def copy_kernel():
+    """Plain copies of COPY_BYTES, each launch reading COPY_BYTES and writing
+    COPY_BYTES: the non-temporal stream copy of libbdmcal.so, then a torch
+    elementwise copy (float32 negation into a second buffer)."""
+    import ctypes
+
+    import torch
+    lib_path = os.path.join(HERE, "libbdmcal.so")
+    if not os.path.exists(lib_path):
+        raise SystemExit(f"{lib_path} is not built (python -m block_diffusion_moe_amd.build)")
+    lib = ctypes.CDLL(lib_path)
+    lib.bdmcal_stream_copy.restype = ctypes.c_int
+    lib.bdmcal_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long,
+                                       ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    n = COPY_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        if lib.bdmcal_stream_copy(a.data_ptr(), b.data_ptr(), COPY_BYTES, st) != 0:
+            raise SystemExit("bdmcal_stream_copy failed")
+    torch.cuda.synchronize()
+    if not torch.equal(a, b):
+        raise SystemExit("bdmcal_stream_copy: copy mismatch")
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(f"copy done: 3 + 3 launches of {COPY_BYTES} B read + {COPY_BYTES} B written",
+          flush=True)
+
+
+def read_counters(d: str):
+    """{(kernel short name, counter): [value per dispatch]} from one pass."""
+    agg = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].split("(")[0]
+                name = name.replace("void ", "").strip()
+                agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _copy_factor(agg, counter: str, kernel: str = "stream_copy_kernel") -> float:
+    vals = [v for (n, c), vs in agg.items() if c == counter and kernel in n for v in vs]
+    if not vals:
+        raise SystemExit(f"no copy-kernel dispatches with {counter} found")
+    mean_kib = sum(vals) / len(vals)
+    return COPY_BYTES / (mean_kib * 1024.0)
+
+
+def summarize(a):
+    fetch, write = read_counters(a.fetch), read_counters(a.write)
+    cal_f, cal_w = read_counters(a.cal_fetch), read_counters(a.cal_write)
+    f_fac = _copy_factor(cal_f, "FETCH_SIZE")
+    w_fac = _copy_factor(cal_w, "WRITE_SIZE")
+    f_ew = _copy_factor(cal_f, "FETCH_SIZE", "elementwise")
+    w_ew = _copy_factor(cal_w, "WRITE_SIZE", "elementwise")
+    names = sorted({n for n, _ in fetch} | {n for n, _ in write})
+    rows = []
+    head_bytes = None
+    for n in names:
+        fv = fetch.get((n, "FETCH_SIZE"), [])
+        wv = write.get((n, "WRITE_SIZE"), [])
+        if not fv or not wv or "bdm" not in n:
+            continue
+        fb = f_fac * 1024.0 * sum(fv) / len(fv)
+        wb = w_fac * 1024.0 * sum(wv) / len(wv)
+        rows.append((n, len(fv), fb, wb))
+        if n.split("::")[-1].startswith(HEAD_KERNEL):
+            head_bytes = fb + wb if head_bytes is None else max(head_bytes, fb + wb)
+    out = [f"<!-- source_sha256 = {kernel_source_digest()} -->"]
+    if head_bytes is not None:
+        out.append(f"<!-- traffic_bytes = {head_bytes:.0f} -->")
+    out += ["", "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", ""]
+    if a.command:
+        out += ["Made by:", "", "```", a.command, "```", ""]
+    out += [f"Calibration (plain copy of {COPY_BYTES} B read + written, 16 B non-temporal "
+            f"loads as in the weight streams): FETCH_SIZE x {f_fac:.4f}, WRITE_SIZE x "
+            f"{w_fac:.4f}.  For comparison, a torch elementwise copy (ordinary loads) reads "
+            f"FETCH_SIZE x {f_ew:.4f}, WRITE_SIZE x {w_ew:.4f}.", "",
+            "| kernel | dispatches | read B / launch | written B / launch | total B / launch |",
+            "|---|---:|---:|---:|---:|"]
+    for n, c, fb, wb in rows:
+        out.append(f"| `{n}` | {c} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
+    out.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(out))
+    print("\n".join(out))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    sub.add_parser("copy")
+    s = sub.add_parser("summarize")
+    for k in ("fetch", "write", "cal_fetch", "cal_write", "out"):
+        s.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    s.add_argument("--command", default="")
+    a = p.parse_args(argv)
+    if a.cmd == "copy":
+        copy_kernel()
+    else:
+        summarize(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -197,6 +197,46 @@ BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The head in two phases, for callers that merge statistics themselves (for
+ * instance over vocabulary shards held by several devices): phase 1 streams
+ * one shard of the head and reduces every (token, workgroup) slice of logits
+ * to an online-softmax triple; phase 2 merges any number of such triples per
+ * token and applies the commit rule.  bdm_lm_head_unmask is exactly phase 1
+ * over the whole vocabulary followed by phase 2.
+ *
+ * bdm_head_stat_parts -- number of triples per token phase 1 writes on the
+ *   current device (its workgroup count).  parts: HOST pointer.
+ *
+ * bdm_lm_head_stats -- phase 1 over vocabulary rows [vocab_offset,
+ *   vocab_offset + V) held in w_head ([V][H], weight_layout as above).  For
+ *   every token t and part p < parts: stat_max[t*stat_stride + p] = the
+ *   largest logit of the part's rows, stat_sum[...] = sum over those rows of
+ *   exp(logit - stat_max), stat_arg[...] = the lowest vocabulary id
+ *   (vocab_offset + row) holding the maximum; the row whose id equals
+ *   mask_id (if it is in this shard) is left out ([files] "How it writes",
+ *   step 2).  A part with no rows has max -inf, sum 0, arg INT32_MAX.
+ *   stat_* are DEVICE fp32/int32 arrays of T*stat_stride elements,
+ *   stat_stride >= parts; V >= 1; vocab_offset >= 0.
+ *
+ * bdm_unmask_from_stats -- phase 2: per token, merge stat_*[t*stat_stride +
+ *   0 .. parts-1] (max of maxima; sums rescaled to the common max and added;
+ *   equal maxima keep the lowest id), conf = 1/sum, argmax = that id, then the
+ *   commit rule of bdm_lm_head_unmask on tokens (same arguments and outputs).
+ */
+BDM_API int bdm_head_stat_parts(int* parts);
+
+BDM_API int bdm_lm_head_stats(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
+                              int vocab_offset, int weight_layout, int32_t mask_id,
+                              float* stat_max, float* stat_sum, int32_t* stat_arg,
+                              int stat_stride, void* stream);
+
+BDM_API int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum,
+                                  const int32_t* stat_arg, int T, int parts, int stat_stride,
+                                  int32_t mask_id, float threshold, int fallback,
+                                  int32_t* tokens, int32_t* argmax, float* conf,
+                                  int32_t* n_committed, void* stream);
+
+/*
  * bdm_packed_weight_elems -- size of the packed copy of a [rows][cols] bf16
  * matrix: ceil(rows/16)*16*cols elements (rows padded to a multiple of 16).
  *   n: HOST pointer.  cols must be a multiple of 32.  Pure host arithmetic.

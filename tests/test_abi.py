@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert syms == sorted(["bdm_version", "bdm_status_string", "bdm_moe_workspace_bytes",
                            "bdm_moe_block_forward", "bdm_head_workspace_bytes",
                            "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
-                           "bdm_pack_weights"])
+                           "bdm_pack_weights", "bdm_head_stat_parts", "bdm_lm_head_stats",
+                           "bdm_unmask_from_stats"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -153,3 +154,33 @@ def test_packed_weight_size_and_pack_validation(lib):
     assert lib.bdm_pack_weights(None, 16, 64, B, None) == -1
     assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 20) + 64), None) == -1   # overlap
     assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 26) + 8), None) == -1    # misaligned
+
+
+def test_two_phase_head_validation(lib):
+    A = _fake(1 << 20)
+    S = _fake(1 << 22)
+    assert lib.bdm_lm_head_stats(None, 32, 2048, A, 1000, 0, 0, 5, S, S, S, 1024, None) == -1
+    assert lib.bdm_lm_head_stats(A, 32, 2048, A, 1000, -1, 0, 5, S, S, S, 1024, None) == -1
+    assert lib.bdm_lm_head_stats(A, 32, 2048, A, 1000, 0, 3, 5, S, S, S, 1024, None) == -1
+    assert lib.bdm_lm_head_stats(A, 32, 2000, A, 1000, 0, 0, 5, S, S, S, 1024, None) == -2
+    assert lib.bdm_unmask_from_stats(S, S, S, 32, 0, 8, 5, 0.95, 1, A, None, None, None, None) == -1
+    assert lib.bdm_unmask_from_stats(S, S, S, 32, 16, 8, 5, 0.95, 1, A, None, None, None, None) == -1
+    assert lib.bdm_unmask_from_stats(S, S, S, 32, 8, 8, 5, 0.95, 1, None, None, None, None, None) == -1
+    assert lib.bdm_unmask_from_stats(S, S, S, 2000, 8, 8, 5, 0.95, 1, A, None, None, None, None) == -2
+
+
+def test_calibration_library_exports():
+    """The counter-calibration copy kernel lives in its own library and
+    rejects sizes it cannot copy exactly (checks only, no launch)."""
+    import ctypes
+    import os
+    path = os.path.join(ROOT, "block_diffusion_moe_amd", "libbdmcal.so")
+    if not os.path.exists(path):
+        pytest.fail("libbdmcal.so not built (python -m block_diffusion_moe_amd.build)")
+    cal = ctypes.CDLL(path)
+    f = cal.bdmcal_stream_copy
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
+    assert f(None, _fake(1 << 20), 16384, None) == -1
+    assert f(_fake(1 << 20), _fake(1 << 21), 16000, None) == -1
+    assert f(_fake(1 << 20), _fake(1 << 20), 16384, None) == -1

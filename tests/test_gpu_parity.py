@@ -258,6 +258,52 @@ def test_head_clover_fallback(bdm, layout):
     assert torch.equal(out_nf[0].cpu(), blk.tokens.cpu())
 
 
+@LAYOUTS
+def test_head_two_phase_and_vocab_shards(bdm, layout):
+    """Phase 1 + phase 2 equals the fused call bit for bit, and the head
+    computed as three vocabulary shards (each with its vocab_offset, the
+    mask row in the middle shard) and merged once gives the same argmax and
+    decisions, with confidences within the fp32 merge-order tolerance."""
+    say(f"case head two-phase + shards layout={layout}")
+    s = synth.HeadShape(T=32, H=2048, V=100000, mask_id=51234)
+    W = synth.head_weights(s, 3, device=DEV)
+    blk = synth.head_block(s, W, block_seed=5, n_boost=10, committed_rows=3, mask_boost_rows=2)
+    fused = run_head(bdm, blk, layout=layout)
+    P = bdm.bdm_head_stat_parts()
+    T = s.T
+    cuts = [0, 33000, 67000, s.V]
+    sm = torch.empty((T, P * 3), dtype=torch.float32, device=DEV)
+    ss = torch.empty_like(sm)
+    sa = torch.empty((T, P * 3), dtype=torch.int32, device=DEV)
+    for i in range(3):
+        Wi = W[cuts[i]:cuts[i + 1]]
+        if layout:
+            Wi = bdm.bdm_pack_weights(Wi.contiguous())
+        cols = slice(i * P, (i + 1) * P)
+        bdm.bdm_lm_head_stats(blk.h, Wi, s.mask_id, sm[:, cols], ss[:, cols], sa[:, cols],
+                              vocab_offset=cuts[i])
+    tok = blk.tokens.clone()
+    am = torch.empty(T, dtype=torch.int32, device=DEV)
+    cf = torch.empty(T, dtype=torch.float32, device=DEV)
+    nc = torch.empty(1, dtype=torch.int32, device=DEV)
+    bdm.bdm_unmask_from_stats(sm, ss, sa, s.mask_id, 0.95, True, tok, argmax=am, conf=cf,
+                              n_committed=nc)
+    # one shard over the whole vocabulary through the two phases = the fused call
+    sm1 = torch.empty((T, P), dtype=torch.float32, device=DEV)
+    ss1, sa1 = torch.empty_like(sm1), torch.empty((T, P), dtype=torch.int32, device=DEV)
+    Wf = bdm.bdm_pack_weights(W) if layout else W
+    bdm.bdm_lm_head_stats(blk.h, Wf, s.mask_id, sm1, ss1, sa1)
+    tok1 = blk.tokens.clone()
+    am1, cf1, nc1 = torch.empty_like(am), torch.empty_like(cf), torch.empty_like(nc)
+    bdm.bdm_unmask_from_stats(sm1, ss1, sa1, s.mask_id, 0.95, True, tok1, argmax=am1, conf=cf1,
+                              n_committed=nc1)
+    torch.cuda.synchronize()
+    for x, z in zip(fused, (tok1, am1, cf1, nc1)):
+        assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+    o = oracle_head(blk)
+    compare_head((tok, am, cf, nc), o, blk.tokens.cpu().numpy())
+
+
 def test_head_repeatable_bitwise(bdm):
     say("case head repeatability")
     s = synth.HeadShape(T=32, H=2048, V=65536, mask_id=3)
