@@ -9,7 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
+namespace bdmcal {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -27,15 +27,16 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(const u32x4* __re
   for (int i = 0; i < kPerThread; ++i) dst[base + i * kThreads] = v[i];
 }
 
-}  // namespace
+}  // namespace bdmcal
 
 extern "C" __attribute__((visibility("default"))) int bdmcal_stream_copy(const void* src,
                                                                         void* dst, long bytes,
                                                                         void* stream) {
+  using namespace bdmcal;
   if (!src || !dst || bytes <= 0 || bytes % kChunk != 0 || bytes / kChunk > 0x7fffffffL) return -1;
-  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return -1;
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
-  if (a < b + bytes && b < a + bytes) return -1;
+  if ((a | b) & 15) return -1;
+  if (a < b + bytes && b < a + bytes) return -1;   // overlap
   (void)hipGetLastError();
   stream_copy_kernel<<<static_cast<unsigned>(bytes / kChunk), kThreads, 0,
                        static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(src),

@@ -86,8 +86,8 @@ def read_counters(d: str):
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                name = r["Kernel_Name"].split("(")[0]
-                name = name.replace("void ", "").strip()
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                name = name.split("(")[0].replace("void ", "").strip()
                 agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
     return agg
 
@@ -105,8 +105,8 @@ def summarize(a):
     cal_f, cal_w = read_counters(a.cal_fetch), read_counters(a.cal_write)
     f_fac = _copy_factor(cal_f, "FETCH_SIZE")
     w_fac = _copy_factor(cal_w, "WRITE_SIZE")
-    f_ew = _copy_factor(cal_f, "FETCH_SIZE", "elementwise")
-    w_ew = _copy_factor(cal_w, "WRITE_SIZE", "elementwise")
+    f_ew = _copy_factor(cal_f, "FETCH_SIZE", "neg_kernel")
+    w_ew = _copy_factor(cal_w, "WRITE_SIZE", "neg_kernel")
     names = sorted({n for n, _ in fetch} | {n for n, _ in write})
     rows = []
     head_bytes = None
