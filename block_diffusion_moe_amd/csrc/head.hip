@@ -21,8 +21,15 @@
 
 namespace bdm {
 
-constexpr int kHeadGroups = 4;   // 16-row vocabulary groups a wave multiplies together
-constexpr int kHeadPad = 8;      // bf16 padding per staged row (bank spread)
+#ifndef BDM_HEAD_QG
+#define BDM_HEAD_QG 1
+#endif
+#ifndef BDM_HEAD_U
+#define BDM_HEAD_U 8
+#endif
+constexpr int kHeadQG = BDM_HEAD_QG;   // 16-row vocabulary groups a wave multiplies together
+constexpr int kHeadU = BDM_HEAD_U;     // k-steps per loaded batch
+constexpr int kHeadPad = 8;            // bf16 padding per staged row (bank spread)
 
 size_t head_lds_bytes(int H) {
   return static_cast<size_t>(kHeadTokChunk) * (H + kHeadPad) * sizeof(uint16_t) +
@@ -31,7 +38,7 @@ size_t head_lds_bytes(int H) {
 
 // Persistent: one workgroup per CU, 8 waves.  The <= 32 hidden rows of this
 // pass are staged once in LDS (A operand).  The vocabulary is cut into
-// 64-row chunks (four 16-row groups) and every wave of the grid takes one
+// chunks of QG 16-row groups and every wave of the grid takes one
 // contiguous run of chunks (lengths differ by at most one), streaming those
 // weight rows once from HBM as the B operand.  The loop runs over
 // (chunk, k-batch) pairs; the next batch's loads are issued before the
@@ -41,7 +48,7 @@ size_t head_lds_bytes(int H) {
 // online-softmax state for its 8 (token, column) slots across the run; the
 // per-wave results are merged across lanes and waves in a fixed order and
 // written as one partial per (token, workgroup).  U = k-steps per batch.
-template <int U>
+template <int QG, int U, bool NBEVEN>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
     const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
     int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
@@ -57,13 +64,13 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  const long NC = (V + 16 * kHeadGroups - 1) / (16 * kHeadGroups);
+  const long NC = (V + 16 * QG - 1) / (16 * QG);
   const long NW = static_cast<long>(gridDim.x) * kHeadWaves;
   const long wid = static_cast<long>(blockIdx.x) * kHeadWaves + wave;
   const int c0 = static_cast<int>(wid * NC / NW);
   const int c1 = static_cast<int>((wid + 1) * NC / NW);
   const int KS = H / 32;
-  const int nb = KS / U;                                        // k-batches per chunk
+  const int nb = KS / U;                        // k-batches per chunk (even iff NBEVEN)
   const int iters = (c1 - c0) * nb;
 
   // fragment pointer of chunk ch, group q (row-major: a row past V reads
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   // dropped in the epilogue, which keeps only v < V)
   const long ngroups = (V + 15) / 16;            // 16-row groups (packed: padded rows)
   auto wfrag = [&](int ch, int q) {
-    long grp = static_cast<long>(ch) * kHeadGroups + q;
+    long grp = static_cast<long>(ch) * QG + q;
     if (layout == BDM_LAYOUT_MFMA_TILES) {
       grp = grp < ngroups ? grp : ngroups - 1;   // chunk past the last group: dropped later
       return frag_ptr(w, grp * 16, H, lane, layout);
@@ -81,11 +88,11 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
     v = v < V ? v : V - 1;
     return FragPtr{w + v * H + g * 8, 32};
   };
-  auto load_batch = [&](int it, u32x4(&b)[U][kHeadGroups]) {
+  auto load_batch = [&](int it, u32x4(&b)[U][QG]) {
     const int ch = c0 + it / nb;
     const int s0 = (it % nb) * U;
 #pragma unroll
-    for (int q = 0; q < kHeadGroups; ++q) {
+    for (int q = 0; q < QG; ++q) {
       const FragPtr f = wfrag(ch, q);
 #pragma unroll
       for (int u = 0; u < U; ++u) b[u][q] = ld16_stream(f.p + (s0 + u) * f.step);
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   };
 
   // the first two batches in flight before the staging barrier
-  u32x4 bcur[U][kHeadGroups], bnxt[U][kHeadGroups];
+  u32x4 bcur[U][QG], bnxt[U][QG];
   if (iters > 0) load_batch(0, bcur);
   if (iters > 1) load_batch(1, bnxt);
 
@@ -133,74 +140,82 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) st[mt][i] = softstat_empty();
 
-  f32x4 acc[kHeadGroups][2];
+  f32x4 acc[QG][2];
 #pragma unroll
-  for (int q = 0; q < kHeadGroups; ++q)
+  for (int q = 0; q < QG; ++q)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int it, const u32x4(&b)[U][kHeadGroups]) {
+  auto compute = [&](int it, const u32x4(&b)[U][QG]) {
     const int s0 = (it % nb) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const u32x4 a0 = *reinterpret_cast<const u32x4*>(arow0 + (s0 + u) * 32);
       const u32x4 a1 = *reinterpret_cast<const u32x4*>(arow1 + (s0 + u) * 32);
 #pragma unroll
-      for (int q = 0; q < kHeadGroups; ++q) {
+      for (int q = 0; q < QG; ++q) {
         acc[q][0] = mfma_bf16(a0, b[u][q], acc[q][0]);
         acc[q][1] = mfma_bf16(a1, b[u][q], acc[q][1]);
       }
     }
-    if (it % nb == nb - 1) {
-      // online softmax over this chunk's columns (increasing vocabulary id
-      // per lane, so a strict '>' keeps the lowest id among equal maxima)
-      const int ch = c0 + it / nb;
+  };
+  // after the last k-batch of a chunk: fold its logits into the online
+  // softmax state (branch-free; columns past V and the mask column count as
+  // -inf).  Per lane the vocabulary id only grows, so the strict '>' keeps
+  // the lowest id among equal maxima.
+  auto finish = [&](int it) {
+    if (it % nb != nb - 1) return;
+    const int ch = c0 + it / nb;
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+      const int v = (ch * QG + q) * 16 + c;
+      const bool valid = v < V && v + voff != mask_id;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          SoftStat& s = st[mt][i];
-#pragma unroll
-          for (int q = 0; q < kHeadGroups; ++q) {
-            const int v = (ch * kHeadGroups + q) * 16 + c;
-            if (v < V && v + voff != mask_id) {
-              const float l = acc[q][mt][i];
-              if (l > s.m) {
-                s.s = (s.m == -INFINITY ? 0.0f : s.s * expf(s.m - l)) + 1.0f;
-                s.m = l;
-                s.a = v + voff;
-              } else {
-                s.s += expf(l - s.m);
-              }
-            }
-          }
+          SoftStat& st_ = st[mt][i];
+          const float l = valid ? acc[q][mt][i] : -INFINITY;
+          const float nm = fmaxf(st_.m, l);
+          const float sc = (st_.m == nm) ? 1.0f : expf(st_.m - nm);
+          const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
+          st_.a = (l > st_.m) ? v + voff : st_.a;
+          st_.s = st_.s * sc + add;
+          st_.m = nm;
         }
+        acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
-      for (int q = 0; q < kHeadGroups; ++q)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  // ping-pong batches: while one is multiplied the other is loading
+  // ping-pong batches: while one is multiplied the other is loading.  With
+  // an even number of k-batches per chunk a chunk never ends on an even
+  // iteration, so those steps carry no epilogue.
   if (iters == 1) {
     compute(0, bcur);
+    finish(0);
   } else if (iters > 1) {
     int it = 0;
     for (; it + 3 < iters; it += 2) {
       compute(it, bcur);
       load_batch(it + 2, bcur);
+      if (!NBEVEN) finish(it);
       compute(it + 1, bnxt);
       load_batch(it + 3, bnxt);
+      finish(it + 1);
     }
     compute(it, bcur);
     if (it + 2 < iters) {
       load_batch(it + 2, bcur);
+      finish(it);
       compute(it + 1, bnxt);
+      finish(it + 1);
       compute(it + 2, bcur);
+      finish(it + 2);
     } else {
+      finish(it);
       compute(it + 1, bnxt);
+      finish(it + 1);
     }
   }
 
@@ -297,14 +312,29 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   if (lane == 0 && n_committed) *n_committed = ncommit;
 }
 
+// the k-batch must divide H/32 (always even), else batches of 2 k-steps
+using HeadKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int, int32_t, int, int,
+                            float*, float*, int32_t*, int);
+static const HeadKernel kHeadKernels[4] = {
+    &head_tile_kernel<kHeadQG, kHeadU, true>, &head_tile_kernel<kHeadQG, kHeadU, false>,
+    &head_tile_kernel<kHeadQG, 2, true>, &head_tile_kernel<kHeadQG, 2, false>};
+
+static HeadKernel head_kernel_for(int H) {
+  const int KS = H / 32;
+  const int u = (KS % kHeadU == 0) ? kHeadU : 2;
+  const bool even = (KS / u) % 2 == 0;
+  return kHeadKernels[(u == kHeadU ? 0 : 2) + (even ? 0 : 1)];
+}
+
 void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V, int voff,
                        int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
                        int pstride, int grid, hipStream_t s) {
   const size_t lds = head_lds_bytes(H);
+  auto kern = head_kernel_for(H);
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
-    head_tile_kernel<2><<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0,
-                                                          n, pm, ps, pa, pstride);
+    kern<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
+                                            pstride);
   }
 }
 
@@ -318,10 +348,11 @@ void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, i
 
 int head_prepare() {
   const int lds = static_cast<int>(head_lds_bytes(BDM_MAX_HIDDEN));
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&head_tile_kernel<2>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess
-             ? 0
-             : -1;
+  for (HeadKernel f : kHeadKernels)
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(f),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return -1;
+  return 0;
 }
 
 }  // namespace bdm

@@ -12,10 +12,10 @@
 //                  Workgroup tile: 16 experts x 32 tokens x one of 4 K-parts
 //                  (4 waves split the part, every load issued first); the
 //                  parts are summed in order by the select step.
-//   select_kernel  per token (one wave each): softmax over E, the k largest
-//                  logits (wave-wide argmax rounds, equal logits -> lower id)
-//                  and their renormalised weights; the last workgroup to
-//                  finish groups the picks by expert (slot table + pair rows)
+//   select_kernel  per token (one wave each): the k largest logits (a
+//                  ballot threshold search, equal logits -> lower id) and
+//                  their softmax weights, renormalised over the picks; then
+//                  the picks are grouped by expert (slot table + pair rows)
 //                  for the expert kernels.
 #include "device.hpp"
 #include "internal.hpp"
@@ -124,13 +124,22 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
   }
 }
 
-// Top-k of one token's logit row, held as PER values per lane (lane + 64*i).
-// Returns the j-th pick and weight in lane j (j < k).
+// Order-preserving map of an fp32 logit to uint32 (larger float -> larger
+// key); -0 is taken as +0 so that equal logits get equal keys.
+__device__ __forceinline__ uint32_t logit_key(float l) {
+  const uint32_t u = __float_as_uint(l);
+  return (l == 0.0f) ? 0x80000000u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+}
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// One token's logit row, PER values per lane (expert lane + 64*i): the
+// K-part partials summed in part order, plus the bias; past E and NaN -> -inf.
 template <int PER>
-__device__ __forceinline__ void topk_row(const float* __restrict__ part, size_t zstride,
-                                         const float* __restrict__ bias, int E, int k,
-                                         int renorm, int lane, int& sel_e, float& sel_w) {
-  float v[PER];
+__device__ __forceinline__ void load_logits(const float* __restrict__ part, size_t zstride,
+                                            const float* __restrict__ bias, int E, int lane,
+                                            float (&v)[PER]) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + kWave * i;
@@ -140,30 +149,85 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ part, size_t 
     for (int z = 1; z < kRouterParts; ++z) l += part[z * zstride + ec];
     if (bias) l += bias[ec];
     l = (e < E) ? l : -INFINITY;
-    v[i] = (l == l) ? l : -INFINITY;             // NaN logits rank last
+    v[i] = (l == l) ? l : -INFINITY;              // NaN logits rank last
   }
-  uint32_t picked = 0u;
-  float sel_v = 0.0f, first_v = 0.0f;
-  sel_e = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = INT32_MAX;
+}
+
+// Top-k of one logit row.  The k-th largest key is found bit by bit from the
+// top with wave ballots (count of keys at or above a candidate), stopping
+// early once exactly k keys lie at or above it; the picks are the keys above
+// that threshold plus, among keys equal to it, the lowest expert ids.  The k
+// picks are gathered into lanes 0..k-1 (ds_permute), ranked there (larger
+// logit first, equal -> lower id) and moved to the lane of their rank.
+// Returns the j-th pick and weight in lane j (j < k).
+template <int PER>
+__device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, int renorm,
+                                          int lane, int& sel_e, float& sel_w) {
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = (lane + kWave * i < E) ? logit_key(v[i]) : 0u;
+  // threshold search (every count is wave-uniform)
+  uint32_t pre = 0u;
+  bool exact = false;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = pre | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= k) pre = cand;
+    if (cnt == k) {
+      exact = true;
+      break;
+    }
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  unsigned long long pm[PER];
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    pm[i] = __ballot(exact ? key[i] >= pre : key[i] > pre);
+    need -= __popcll(pm[i]);
+  }
+  if (!exact) {
+    // ties at the threshold: the lowest ids, in (i, lane) order
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !(picked & (1u << i)) && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    wave_argmax(bv, be);
-    if ((be % kWave) == lane) picked |= 1u << (be / kWave);
-    if (j == 0) first_v = bv;
-    if (lane == j) {
-      sel_v = bv;
-      sel_e = be;
+      const unsigned long long em = __ballot(key[i] == pre);
+      const int take = min(need, __popcll(em));
+      const bool mine = ((em >> lane) & 1ull) && __popcll(em & below) < take;
+      pm[i] |= __ballot(mine);
+      need -= take;
     }
   }
+  // gather: the pick with compact index j goes to lane j (non-picks are
+  // pushed to lane 63, which is never read: k <= 16)
+  int ck = 0, ce = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n_i = __popcll(pm[i]);
+    const int dst = ((pm[i] >> lane) & 1ull) ? base + __popcll(pm[i] & below) : kWave - 1;
+    const int rk = __builtin_amdgcn_ds_permute(dst * 4, static_cast<int>(key[i]));
+    const int re = __builtin_amdgcn_ds_permute(dst * 4, lane + kWave * i);
+    if (lane >= base && lane < base + n_i) {
+      ck = rk;
+      ce = re;
+    }
+    base += n_i;
+  }
+  // rank among the k picks, then move each pick to the lane of its rank
+  int rank = 0;
+  for (int q = 0; q < k; ++q) {
+    const uint32_t kq = static_cast<uint32_t>(__builtin_amdgcn_readlane(ck, q));
+    const int eq = __builtin_amdgcn_readlane(ce, q);
+    rank += (kq > static_cast<uint32_t>(ck) || (kq == static_cast<uint32_t>(ck) && eq < ce)) ? 1
+                                                                                          : 0;
+  }
+  const int dst = lane < k ? rank : kWave - 1;
+  const int sk = __builtin_amdgcn_ds_permute(dst * 4, ck);
+  const int se = __builtin_amdgcn_ds_permute(dst * 4, ce);
+  const float sel_v = (lane < k) ? key_logit(static_cast<uint32_t>(sk)) : -INFINITY;
+  sel_e = (lane < k) ? se : 0;
+  const float first_v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
   // w_j = exp(l_j - l_max) / (sum over the picks when renormalised, else over all E)
   const float z = (lane < k) ? expf(sel_v - first_v) : 0.0f;
   float den;
@@ -181,123 +245,138 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ part, size_t 
   sel_w = z / den;
 }
 
-constexpr int kSelWaves = 4;    // tokens per select workgroup (one wave each)
+constexpr int kSelWaves = 4;       // tokens per select workgroup (one wave each)
+constexpr int kSelOneWaves = 16;   // waves of the single-workgroup select (small blocks)
+constexpr int kSelOneMaxT = 16;    // largest block the single-workgroup select takes
 
-// Top-k of every token (one wave per token, kSelWaves tokens per workgroup).
-// The last workgroup to finish (completion ticket) then groups the picks by
-// expert for the expert kernels:
+// Top-k of every token, then the grouping of the picks by expert for the
+// expert kernels:
 //   slots[i] = {expert, offset, count, 0} for the i-th touched group -- the
 //              shared expert (group E, all T tokens) first, then routed
 //              experts with at least 16 tokens, then the others, each run in
 //              increasing id -- and {-1, 0, 0, 0} for i = n .. E;
 //   pair_rows[offset .. offset+count) = the (token, slot) rows t*(k+1)+j of
 //              the group's tokens (shared: t*(k+1)+k).
+// SINGLE: one workgroup of NW waves takes every token (wave w: tokens w,
+// w+NW, ...), keeps the picks in LDS and groups them itself.  Otherwise one
+// wave per token, NW tokens per workgroup, and the last workgroup to finish
+// (completion ticket) groups the picks read back from global memory.
 // The order inside a group is whatever the LDS atomics produce; every row's
 // result is computed independently of the others, so outputs do not depend
 // on it.
-template <int PER>
-__global__ __launch_bounds__(kSelWaves * 64) void select_kernel(
+template <int PER, int NW, bool SINGLE>
+__global__ __launch_bounds__(NW * 64) void select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* ticket, int4* __restrict__ slots, int32_t* __restrict__ pair_rows,
     int32_t* __restrict__ info, int32_t* __restrict__ user_idx, float* __restrict__ user_w) {
   __shared__ int cnt[BDM_MAX_EXPERTS + 1];
   __shared__ int eoff[BDM_MAX_EXPERTS + 1];
-  __shared__ int wtot[2][kSelWaves];
-  __shared__ int s_last, s_carry[3];
+  __shared__ int fill[BDM_MAX_EXPERTS + 1];
+  __shared__ int spick[SINGLE ? kSelOneMaxT * BDM_MAX_TOPK : 1];
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int K1 = k + 1;
 
-  const int t = blockIdx.x * kSelWaves + wave;
-  if (t < T) {
-    int sel_e;
-    float sel_w;
-    topk_row<PER>(part + static_cast<size_t>(t) * E, static_cast<size_t>(T) * E, bias, E, k,
-                  renorm, lane, sel_e, sel_w);
-    if (lane < k) {
-      topk_idx[t * k + lane] = sel_e;
-      topk_w[t * k + lane] = sel_w;
-      if (user_idx) user_idx[t * k + lane] = sel_e;
-      if (user_w) user_w[t * k + lane] = sel_w;
-    }
-  }
-  // publish this workgroup's picks, then take a ticket
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- the last workgroup: group the T*k picks by expert ----------------
-  for (int e = tid; e <= E; e += blockDim.x) cnt[e] = (e == E) ? (has_shared ? T : 0) : 0;
-  __syncthreads();
-  for (int p = tid; p < T * k; p += blockDim.x) atomicAdd(&cnt[topk_idx[p]], 1);
-  if (tid == 0) {
-    s_carry[0] = 0;
-    s_carry[1] = 0;
-  }
-  __syncthreads();
-  // two passes over the routed experts in id order (chunks of blockDim.x):
-  // first the heavy ones (>= 16 tokens), then the light ones; each touched
-  // expert gets its slot position and its pair offset
-  const int base = has_shared ? 1 : 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int c0 = 0; c0 < E; c0 += blockDim.x) {
-      const int e = c0 + tid;
-      const int ce = (e < E) ? cnt[e] : 0;
-      const bool in = pass == 0 ? ce >= 16 : (ce > 0 && ce < 16);
-      const unsigned long long mk = __ballot(in);
-      // pair-count prefix inside the wave (DPP-free: a short serial scan of
-      // the wave's counts through LDS is not needed, use ballot-weighted sums)
-      int csum = in ? ce : 0;
-      int incl = csum;
+  // SINGLE: this wave's two tokens (w, w + NW) load their rows together
+  const int ta = SINGLE ? wave : blockIdx.x * NW + wave;
+  const int tb = SINGLE ? wave + NW : T;
+  const size_t zs = static_cast<size_t>(T) * E;
+  float va[PER], vb[PER];
+  if (ta < T) load_logits<PER>(part + static_cast<size_t>(ta) * E, zs, bias, E, lane, va);
+  if (SINGLE && tb < T) load_logits<PER>(part + static_cast<size_t>(tb) * E, zs, bias, E, lane, vb);
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += v;
+  for (int r = 0; r < (SINGLE ? 2 : 1); ++r) {
+    const int t = r == 0 ? ta : tb;
+    if (t < T) {
+      int sel_e;
+      float sel_w;
+      topk_pick<PER>(r == 0 ? va : vb, E, k, renorm, lane, sel_e, sel_w);
+      if (lane < k) {
+        topk_idx[t * k + lane] = sel_e;
+        topk_w[t * k + lane] = sel_w;
+        if (user_idx) user_idx[t * k + lane] = sel_e;
+        if (user_w) user_w[t * k + lane] = sel_w;
+        if (SINGLE) spick[t * k + lane] = sel_e;
       }
-      if (lane == kWave - 1) {
-        wtot[0][wave] = __popcll(mk);
-        wtot[1][wave] = incl;
-      }
-      __syncthreads();
-      int pos_b = 0, off_b = 0, pos_n = 0, off_n = 0;
-      for (int w = 0; w < kSelWaves; ++w) {
-        if (w < wave) {
-          pos_b += wtot[0][w];
-          off_b += wtot[1][w];
-        }
-        pos_n += wtot[0][w];
-        off_n += wtot[1][w];
-      }
-      if (in) {
-        const int pos = base + s_carry[0] + pos_b + __popcll(mk & ((1ull << lane) - 1ull));
-        const int off = (has_shared ? T : 0) + s_carry[1] + off_b + incl - csum;
-        slots[pos] = int4{e, off, ce, 0};
-        eoff[e] = off;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        s_carry[0] += pos_n;
-        s_carry[1] += off_n;
-      }
-      __syncthreads();
     }
   }
-  const int n = base + s_carry[0];
-  if (has_shared && tid == 0) slots[0] = int4{E, 0, T, 0};
-  for (int i = n + tid; i <= E; i += blockDim.x) slots[i] = int4{-1, 0, 0, 0};
-  if (tid == 0) info[0] = n;
+  if (!SINGLE) {
+    // publish this workgroup's picks, then take a ticket
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+  }
+  const int32_t* picks = SINGLE ? spick : topk_idx;
+
+  // ---- group the T*k picks by expert --------------------------------------
+  // wave 0 ranks the experts: lane L holds experts L*epl .. L*epl+epl-1, so
+  // (lane, j) order is id order and ballot popcounts give the slot position
+  // of every touched expert (heavy ones, >= 16 tokens, first, then the
+  // light ones, each run in increasing id); pair ranges follow expert id
+  // order after the shared expert's [0, T).
+  for (int e = tid; e <= E; e += blockDim.x) {
+    cnt[e] = (e == E) ? (has_shared ? T : 0) : 0;
+    fill[e] = 0;
+  }
+  __syncthreads();
+  for (int p = tid; p < T * k; p += blockDim.x) atomicAdd(&cnt[picks[p]], 1);
+  __syncthreads();
+  const int base = has_shared ? 1 : 0;
+  if (wave == 0) {
+    constexpr int EPL = PER;                          // experts per lane, at most
+    const int epl = (E + kWave - 1) / kWave;          // E <= 64 * PER
+    const unsigned long long bel = (1ull << lane) - 1ull;
+    int c[EPL];
+    int nh = 0, nl = 0, hb = 0, lb = 0;      // totals; touched experts below this lane
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * epl + j;
+      c[j] = (j < epl && e < E) ? cnt[e] : 0;
+      const unsigned long long mh = __ballot(c[j] >= 16);
+      const unsigned long long ml = __ballot(c[j] > 0 && c[j] < 16);
+      nh += __popcll(mh);
+      nl += __popcll(ml);
+      hb += __popcll(mh & bel);
+      lb += __popcll(ml & bel);
+    }
+    // pair offsets in expert-id order: this lane's exclusive prefix of the
+    // per-lane pair totals, one ballot per bit of the total (< 2^15)
+    int tot = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) tot += c[j];
+    int pref = has_shared ? T : 0;
+#pragma unroll
+    for (int bit = 0; bit < 15; ++bit) pref += __popcll(__ballot((tot >> bit) & 1) & bel) << bit;
+    int ho = 0, lo = 0;                       // this lane's touched experts so far
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      if (c[j] > 0) {
+        const int e = lane * epl + j;
+        const bool heavy = c[j] >= 16;
+        const int pos = base + (heavy ? hb + ho : nh + lb + lo);
+        slots[pos] = int4{e, pref, c[j], 0};
+        eoff[e] = pref;
+        if (heavy) ++ho; else ++lo;
+      }
+      pref += c[j];
+    }
+    const int n = base + nh + nl;
+    if (has_shared && lane == 0) slots[0] = int4{E, 0, T, 0};
+    for (int i = n + lane; i <= E; i += kWave) slots[i] = int4{-1, 0, 0, 0};
+    if (lane == 0) info[0] = n;
+  }
   // scatter the pairs
-  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   for (int p = tid; p < T * k; p += blockDim.x) {
-    const int e = topk_idx[p];
+    const int e = picks[p];
     const int tt = p / k;
-    pair_rows[eoff[e] + atomicAdd(&cnt[e], 1)] = tt * K1 + (p - tt * k);
+    pair_rows[eoff[e] + atomicAdd(&fill[e], 1)] = tt * K1 + (p - tt * k);
   }
   if (has_shared)
     for (int tt = tid; tt < T; tt += blockDim.x) pair_rows[tt] = tt * K1 + k;
@@ -309,14 +388,22 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
   const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
   router_kernel<<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, meta.ticket);
   const int nsel = (T + kSelWaves - 1) / kSelWaves;
-#define BDM_SELECT(P)                                                                           \
-  select_kernel<P><<<nsel, kSelWaves * 64, 0, s>>>(meta.logits, bias, T, E, k, renorm,         \
-                                                   has_shared, meta.topk_idx, meta.topk_w,     \
-                                                   meta.ticket, meta.slots, meta.pair_rows,    \
-                                                   meta.info, user_idx, user_w)
-  if (E <= 256) BDM_SELECT(4);
-  else if (E <= 512) BDM_SELECT(8);
-  else BDM_SELECT(16);
+#define BDM_SELECT(P)                                                                          \
+  if (T <= kSelOneMaxT)                                                                        \
+    select_kernel<P, kSelOneWaves, true><<<1, kSelOneWaves * 64, 0, s>>>(                      \
+        meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
+        meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+  else                                                                                         \
+    select_kernel<P, kSelWaves, false><<<nsel, kSelWaves * 64, 0, s>>>(                        \
+        meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
+        meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w)
+  if (E <= 256) {
+    BDM_SELECT(4);
+  } else if (E <= 512) {
+    BDM_SELECT(8);
+  } else {
+    BDM_SELECT(16);
+  }
 #undef BDM_SELECT
 }
 
