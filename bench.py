@@ -16,12 +16,13 @@ serving repeated weights, the timed steps rotate over --sets independent
 weight sets (router, experts, shared expert, head) and token blocks.
 
 Output: one JSON line (rank 0).  `value` is block-tokens/s of the whole
-step; the MoE layer alone and the head alone are reported beside it, each
-with its algorithmic HBM bytes (touched experts x 6,291,456 B; head
+step; the MoE layer alone (its launches back to back over the rotated sets)
+and the head alone are reported beside it, each with its algorithmic HBM bytes (touched experts x 6,291,456 B; head
 1,017,118,720 B) and the fraction of the 8 TB/s HBM peak.  The roofline
 entry is the head GEMM kernel (one launch per step, the largest single
-kernel), timed with HIP events recorded on the stream it runs on; its HBM
-traffic comes from the committed rocprofv3 counter summary when that was
+kernel): after the timed steps the same launches run back to back over the
+rotated sets between two HIP events recorded on the stream they run on; its
+HBM traffic comes from the committed rocprofv3 counter summary when that was
 taken on the current kernel source, else it is null.
 """
 from __future__ import annotations
@@ -130,13 +131,14 @@ def main():
         if ev is not None:
             ev[4].record()
 
-    # touched experts per set (routing of each set's first step input)
-    touched = []
+    # touched experts per set (routing of each set's step input)
+    touched, xns = [], []
     for r in range(args.sets):
         inp = sets[r][0]
-        bdm.bdm_rmsnorm(xs[r], xn, eps=1e-6)
+        xns.append(torch.empty_like(xn))
+        bdm.bdm_rmsnorm(xs[r], xns[r], eps=1e-6)
         y = torch.empty_like(xn)
-        bdm.bdm_moe_block_forward(xn, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, L.k,
+        bdm.bdm_moe_block_forward(xns[r], inp.w_router, inp.w_gate, inp.w_up, inp.w_down, L.k,
                                   ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
                                   y=y, topk_idx=idx, ws=moe_ws)
         torch.cuda.synchronize()
@@ -175,17 +177,44 @@ def main():
     torch.cuda.synchronize()
     ms_step_plain = start.elapsed_time(stop) / args.steps
 
+    # the head GEMM kernel alone: the same launches back to back over the
+    # rotated sets, two events on the stream they run on around all of them
+    # (per-call events inside a step add their own overhead to each call)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        r = i % args.sets
+        bdm.bdm_lm_head_stats(xo[r], heads[r], HS.mask_id, st_m, st_s, st_a)
+    stop.record()
+    torch.cuda.synchronize()
+    gemm_loop_us = start.elapsed_time(stop) * 1e3 / args.steps
+    # the MoE layer alone, the same way (each set's own normalised input)
+    ylay = torch.empty_like(xn)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        r = i % args.sets
+        kw = kw_sets[r]
+        bdm.bdm_moe_block_forward(xns[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                  kw["w_down"], L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                  ws_down=kw["ws_down"], residual=xs[r], y=ylay, topk_idx=idx,
+                                  ws=moe_ws)
+    stop.record()
+    torch.cuda.synchronize()
+    moe_loop_us = start.elapsed_time(stop) * 1e3 / args.steps
+
     u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
     moe_bytes = (u_mean + 1) * EXPERT_BYTES
-    moe_gbs = moe_bytes / (moe_us * 1e-6) / 1e9
+    moe_gbs = moe_bytes / (moe_loop_us * 1e-6) / 1e9
     head_gbs = HEAD_BYTES / (head_us * 1e-6) / 1e9
     value = T / (ms_step_plain * 1e-3)
 
-    gemm_gbs = HEAD_BYTES / (gemm_us * 1e-6) / 1e9
+    gemm_gbs = HEAD_BYTES / (gemm_loop_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": "head_tile_kernel (bdm_lm_head_stats)",
             "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": head_traffic(),
-            "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_us, 2)}
+            "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_loop_us, 2),
+            "launches_timed": args.steps, "us_per_launch_in_step": round(gemm_us, 2)}
 
     cpu = None
     if args.cpu_blocks > 0:
@@ -212,7 +241,8 @@ def main():
             "vocab": HS.V, "weight_sets_rotated": args.sets, "parallelism": "single GPU",
             "weight_layout": "mfma_tiles (packed once at load)" if args.layout else "row_major",
         },
-        "moe_layer": {"us": round(moe_us, 2), "block_tokens_per_s": round(T / (moe_us * 1e-6), 1),
+        "moe_layer": {"us": round(moe_loop_us, 2), "us_in_step": round(moe_us, 2),
+                      "block_tokens_per_s": round(T / (moe_loop_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
                       "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4)},
         "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),

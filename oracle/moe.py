@@ -108,14 +108,20 @@ def expert_ffn(x_row, w_gate_e, w_up_e, w_down_e) -> np.ndarray:
 
 
 def moe_block(x_bits, w_router, w_gate, w_up, w_down, k: int, ws_gate=None, ws_up=None,
-              ws_down=None, residual=None, bias=None, renorm: bool = True):
+              ws_down=None, residual=None, bias=None, renorm: bool = True, routing=None):
     """Steps 1-7 for a block.  Weight arguments are indexable by expert id
-    (numpy [E][..] uint16 arrays or lazy per-expert views).
+    (numpy [E][..] uint16 arrays or lazy per-expert views).  ``routing`` =
+    (idx, w, near_tie) replaces steps 2-4 (e.g. the block coreset selector's
+    routing, oracle.coreset); slots with id -1 hold no expert.
 
     Returns dict: y (uint16 bf16 bits [T][H]), y_f64 (the value before the
     final rounding), idx, w, logits, near_tie, counts ([E] tokens per expert),
     touched (number of distinct routed experts)."""
-    idx, w, l32, near = route(x_bits, w_router, k, bias, renorm)
+    if routing is None:
+        idx, w, l32, near = route(x_bits, w_router, k, bias, renorm)
+    else:
+        idx, w, near = (np.asarray(a) for a in routing)
+        l32 = router_logits(x_bits, w_router, bias)
     x = bf16.to_f64(x_bits)
     T, H = x.shape
     E = l32.shape[1]
@@ -126,11 +132,14 @@ def moe_block(x_bits, w_router, w_gate, w_up, w_down, k: int, ws_gate=None, ws_u
         acc = np.zeros(H, dtype=np.float64)
         for j in range(k):
             e = int(idx[t, j])
+            if e < 0:
+                continue
             acc += w[t, j] * expert_ffn(x[t], w_gate[e], w_up[e], w_down[e])
         if ws_gate is not None:
             acc += expert_ffn(x[t], ws_gate, ws_up, ws_down)
         out[t] += acc
-    counts = np.bincount(idx.reshape(-1), minlength=E)
+    picks = idx.reshape(-1)
+    counts = np.bincount(picks[picks >= 0], minlength=E)
     return {
         "y": bf16.from_f64(out),
         "y_f64": out,

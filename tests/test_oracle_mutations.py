@@ -8,6 +8,7 @@ fail.  The mistakes are planted in the oracle only, on the CPU.
 import numpy as np
 import pytest
 
+import oracle.coreset as C
 import oracle.head as H
 import oracle.moe as M
 import oracle.norm as N
@@ -101,7 +102,33 @@ def _rms_no_eps(x_bits, eps=1e-6, gamma=None):
     return bf16.from_f64(x / np.sqrt(np.mean(np.abs(x), axis=-1, keepdims=True)))
 
 
+def _mass_counts(p, first, E):
+    mass = np.zeros(E)
+    for t in range(first.shape[0]):
+        for e in first[t]:
+            mass[e] += 1.0
+    return mass
+
+
+def _cut_one_more(orig):
+    return lambda order, mass, top_p: min(len(order), orig(order, mass, top_p) + 1)
+
+
+def _order_ties_high(mass):
+    touched = np.flatnonzero(mass > 0)
+    return touched[np.lexsort((-touched, -mass[touched]))]
+
+
+def _order_ascending(mass):
+    touched = np.flatnonzero(mass > 0)
+    return touched[np.lexsort((touched, mass[touched]))]
+
+
 MUTANTS = {
+    "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
+    "coreset_cut_one_more": (C, "cut", _cut_one_more),
+    "coreset_mass_ties_high_id": (C, "mass_order", lambda o: _order_ties_high),
+    "coreset_order_ascending": (C, "mass_order", lambda o: _order_ascending),
     "silu_sign": (M, "silu", lambda o: _silu_sign),
     "gate_up_swapped": (M, "expert_ffn", lambda o: _ffn_swapped),
     "activation_not_rounded": (M, "expert_ffn", lambda o: _ffn_unrounded),
@@ -131,6 +158,11 @@ PINS = [
     lambda: P.test_head_matches_dense_brute_force_and_torch(0),
     P.test_rmsnorm_matches_torch_and_unit_rms,
     P.test_stack_tokens_independent_and_matches_chained_brute,
+    lambda: P.test_coreset_reproduces_page_simulation(3),
+    P.test_coreset_closed_form_identical_tokens,
+    P.test_coreset_equal_masses_keep_lower_id,
+    P.test_coreset_top_p_one_keeps_routing_and_tiny_top_p_keeps_one,
+    P.test_coreset_sets_nest_and_restrict_routing,
 ]
 
 

@@ -408,3 +408,113 @@ def test_stack_tokens_independent_and_matches_chained_brute():
         cur, _, _ = brute.moe_dense(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], s.k,
                                     h["ws_gate"], h["ws_up"], h["ws_down"], residual=cur)
     assert np.array_equal(cur, y)
+
+
+# --------------------------------------------------------------------------
+# Block coreset expert selector (files page, "The expert selection")
+# --------------------------------------------------------------------------
+
+# The page's simulation of the selector at top_p 0.9 on synthetic logits
+# (per-token N(0,1) noise plus a block-wide N(0,1) preference of the given
+# weight): experts touched before the selector, experts kept, and slots of a
+# token's 8 that are re-routed.  (union, kept, rerouted) per weight.
+PAGE_CORESET_SIM = {0: (163.4, 126.7, 1.1), 1: (79.0, 45.5, 1.2), 2: (40.8, 16.2, 1.6),
+                    3: (27.5, 8.6, 2.5)}
+
+
+@pytest.mark.parametrize("weight", [0, 1, 2, 3])
+def test_coreset_reproduces_page_simulation(weight):
+    from oracle import coreset
+    rng = np.random.default_rng(100 + weight)
+    union, kept, rer = coreset.simulate(weight, 400, rng)
+    pu, pk, pr = PAGE_CORESET_SIM[weight]
+    # the page's figures carry their own sampling error; 400 blocks here
+    assert abs(union - pu) <= (0.02 if weight < 2 else 0.04) * pu, (union, pu)
+    assert abs(kept - pk) <= (0.03 if weight < 2 else 0.07) * pk, (kept, pk)
+    assert abs(rer - pr) <= (0.12 if weight < 3 else 0.3), (rer, pr)
+
+
+def _identical_block(T, E, top, k):
+    """T identical tokens: logits `top` on experts 0..len(top)-1, -8 elsewhere."""
+    l = np.full((T, E), -8.0, dtype=np.float32)
+    l[:, :len(top)] = np.asarray(top, dtype=np.float32)
+    return l
+
+
+def test_coreset_closed_form_identical_tokens():
+    """Identical tokens with top logits 3, 2, 1, 0 and k = 4: the masses are
+    T times the softmax probabilities, so the cumulative shares of the kept
+    prefix are e^3, e^3+e^2, ... over e^3+e^2+e+1 (0.644, 0.881, 0.968, 1):
+    top_p 0.9 keeps 3 experts, 0.85 keeps 2, 0.5 keeps 1; each token then
+    routes to the kept experts with weights softmax over their logits."""
+    from oracle import coreset
+    E, T, k = 12, 8, 4
+    l = _identical_block(T, E, [3, 2, 1, 0], k)
+    e = np.exp(np.array([3.0, 2.0, 1.0, 0.0]))
+    share = np.cumsum(e) / e.sum()
+    assert share[1] < 0.9 <= share[2] and share[0] < 0.85 <= share[1]
+    for top_p, n in ((0.9, 3), (0.85, 2), (0.5, 1), (0.99, 4)):
+        r = coreset.coreset_route(l, k, top_p, block=T)
+        assert r["n_kept"][0] == n
+        assert list(r["kept"][0]) == list(range(n))
+        for t in range(T):
+            assert list(r["idx"][t, :n]) == list(range(n))
+            assert np.all(r["idx"][t, n:] == -1) and np.all(r["w"][t, n:] == 0)
+            np.testing.assert_allclose(r["w"][t, :n], e[:n] / e[:n].sum(), rtol=1e-6)
+        assert np.all(r["rerouted"] == k - n)
+
+
+def test_coreset_equal_masses_keep_lower_id():
+    """Two experts with equal logits in every token have equal masses; a cut
+    between them keeps the lower id."""
+    from oracle import coreset
+    l = _identical_block(4, 10, [1.0, 1.0], 2)
+    r = coreset.coreset_route(l, 2, 0.5, block=4)
+    assert list(r["kept"][0]) == [0]
+    assert np.all(r["idx"][:, 0] == 0) and np.all(r["idx"][:, 1] == -1)
+    np.testing.assert_allclose(r["w"][:, 0], 1.0)
+
+
+def test_coreset_top_p_one_keeps_routing_and_tiny_top_p_keeps_one():
+    from oracle import coreset
+    rng = np.random.default_rng(7)
+    l = rng.standard_normal((32, 64)).astype(np.float32)
+    k = 4
+    full = coreset.coreset_route(l, k, 1.0)
+    first = np.stack([moe.select_topk(l[t], k) for t in range(32)])
+    assert full["n_kept"][0] == len(np.unique(first))
+    assert np.array_equal(full["idx"], first)
+    p = moe.softmax(l)
+    for t in range(32):
+        ps = p[t, first[t]]
+        np.testing.assert_allclose(full["w"][t], ps / ps.sum(), rtol=1e-12)
+    assert np.all(full["rerouted"] == 0)
+    one = coreset.coreset_route(l, k, 1e-9)
+    top = coreset.block_coreset(l, k, 1e-9)["order"][0]
+    assert one["n_kept"][0] == 1 and one["kept"][0][0] == top
+    assert np.all(one["idx"][:, 0] == top) and np.all(one["idx"][:, 1:] == -1)
+    np.testing.assert_allclose(one["w"][:, 0], 1.0)
+
+
+def test_coreset_sets_nest_and_restrict_routing():
+    """Kept sets are prefixes of one mass order, so they nest as top_p
+    grows; every token's picks lie in its block's kept set, and a token
+    whose first-pass picks were all kept keeps its routing."""
+    from oracle import coreset
+    rng = np.random.default_rng(11)
+    pref = rng.standard_normal(128)
+    l = (rng.standard_normal((64, 128)) + 1.0 * pref[None, :]).astype(np.float32)
+    k = 8
+    prev = None
+    for top_p in (0.3, 0.6, 0.9, 0.99):
+        r = coreset.coreset_route(l, k, top_p, block=32)
+        for b in range(2):
+            kept = set(r["kept"][b].tolist())
+            if prev is not None:
+                assert prev[b] <= kept
+            for t in range(32 * b, 32 * b + 32):
+                picks = [e for e in r["idx"][t] if e >= 0]
+                assert set(picks) <= kept and len(picks) == min(k, len(kept))
+                if set(r["first"][t].tolist()) <= kept:
+                    assert list(r["idx"][t]) == list(r["first"][t])
+        prev = [set(r["kept"][b].tolist()) for b in range(2)]
