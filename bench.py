@@ -202,6 +202,32 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     moe_loop_us = start.elapsed_time(stop) * 1e3 / args.steps
+    # the same layer with the block coreset expert selector (top_p 0.9 over
+    # the 32-slot block), timed the same way; its bytes are the kept experts'
+    nk = torch.zeros((1,), dtype=torch.int32, device=dev)
+    kept = []
+    for r in range(args.sets):
+        kw = kw_sets[r]
+        bdm.bdm_moe_block_forward(xns[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                  kw["w_down"], L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                  ws_down=kw["ws_down"], residual=xs[r], y=ylay, ws=moe_ws,
+                                  coreset_top_p=0.9, coreset_block=T, n_kept=nk)
+        torch.cuda.synchronize()
+        kept.append(int(nk.item()))
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        r = i % args.sets
+        kw = kw_sets[r]
+        bdm.bdm_moe_block_forward(xns[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                  kw["w_down"], L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                  ws_down=kw["ws_down"], residual=xs[r], y=ylay, ws=moe_ws,
+                                  coreset_top_p=0.9, coreset_block=T, n_kept=nk)
+    stop.record()
+    torch.cuda.synchronize()
+    cs_us = start.elapsed_time(stop) * 1e3 / args.steps
+    kept_mean = float(np.mean([kept[i % args.sets] for i in range(args.steps)]))
+    cs_bytes = (kept_mean + 1) * EXPERT_BYTES
 
     u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
     moe_bytes = (u_mean + 1) * EXPERT_BYTES
@@ -245,6 +271,11 @@ def main():
                       "block_tokens_per_s": round(T / (moe_loop_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
                       "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4)},
+        "moe_layer_coreset_top_p_0.9": {
+            "us": round(cs_us, 2), "block_tokens_per_s": round(T / (cs_us * 1e-6), 1),
+            "kept_experts": round(kept_mean, 2), "bytes": int(cs_bytes),
+            "GB_s": round(cs_bytes / (cs_us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(cs_bytes / (cs_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},

@@ -31,6 +31,10 @@ _SIGS = {
     "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                        _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
                                        _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_moe_block_forward_coreset": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
+                                               _c_int, _c_float, _c_int, _vp, _vp, _vp, _c_int,
+                                               _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _c_size, _vp]),
     "bdm_head_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
                                     _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
@@ -183,10 +187,13 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_bias=None,
                           ws_gate=None, ws_up=None, ws_down=None, residual=None, y=None,
-                          topk_idx=None, topk_w=None, renorm: bool = True, ws=None, stream=None):
+                          topk_idx=None, topk_w=None, renorm: bool = True, ws=None, stream=None,
+                          coreset_top_p=None, coreset_block: int = 32, n_kept=None):
     """y = MoE layer over the block x (see include/bdmoe.h).  ``y`` may be
     ``residual`` (in-place residual add); a new tensor is made when None.
-    Expert weights may be row-major tensors or all `Packed`."""
+    Expert weights may be row-major tensors or all `Packed`.  With
+    ``coreset_top_p`` the block coreset selector runs first
+    (bdm_moe_block_forward_coreset; ``n_kept`` receives |kept| per block)."""
     T, H = x.shape
     E, I, _ = w_gate.shape
     dev = x.device
@@ -214,12 +221,22 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
     need = bdm_moe_workspace_bytes(T, H, I, E, k, has_shared)
     if ws is None:
         ws = workspace(need, dev)
-    st = load().bdm_moe_block_forward(
-        _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm), _ptr(w_gate),
-        _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), layout,
-        _ptr(residual), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
-        _stream(stream))
-    _raise("bdm_moe_block_forward", st)
+    if coreset_top_p is None:
+        st = load().bdm_moe_block_forward(
+            _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm),
+            _ptr(w_gate), _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up),
+            _ptr(ws_down), layout, _ptr(residual), _ptr(y), _ptr(topk_idx), _ptr(topk_w),
+            _ptr(ws), ws.numel(), _stream(stream))
+        _raise("bdm_moe_block_forward", st)
+        return y
+    nb = (T + coreset_block - 1) // max(1, coreset_block)
+    _check(n_kept, "n_kept", torch.int32, (nb,), dev)
+    st = load().bdm_moe_block_forward_coreset(
+        _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm),
+        float(coreset_top_p), int(coreset_block), _ptr(w_gate), _ptr(w_up), _ptr(w_down), I,
+        _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), layout, _ptr(residual), _ptr(y),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(n_kept), _ptr(ws), ws.numel(), _stream(stream))
+    _raise("bdm_moe_block_forward_coreset", st)
     return y
 
 

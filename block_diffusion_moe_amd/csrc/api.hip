@@ -40,6 +40,7 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
   char* logits = take(sizeof(float) * bdm::kRouterParts * T * E);
   char* topk_idx = take(sizeof(int32_t) * T * k);
   char* topk_w = take(sizeof(float) * T * k);
+  char* topk_p = take(sizeof(float) * T * k);
   char* ticket = take(sizeof(int32_t) * 4);
   char* info = take(sizeof(int32_t) * 4);
   char* slots = take(sizeof(int) * 4 * (E + 1));
@@ -50,6 +51,7 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
     m->logits = reinterpret_cast<float*>(logits);
     m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
     m->topk_w = reinterpret_cast<float*>(topk_w);
+    m->topk_p = reinterpret_cast<float*>(topk_p);
     m->ticket = reinterpret_cast<int32_t*>(ticket);
     m->info = reinterpret_cast<int32_t*>(info);
     m->slots = reinterpret_cast<int4*>(slots);
@@ -138,13 +140,14 @@ int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_shared, s
   return BDM_OK;
 }
 
-int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router,
-                          const float* router_bias, int E, int k, int renorm,
-                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                          int I, const uint16_t* ws_gate, const uint16_t* ws_up,
-                          const uint16_t* ws_down, int weight_layout, const uint16_t* residual,
-                          uint16_t* y, int32_t* topk_idx, float* topk_w, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+namespace {
+
+int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const float* router_bias,
+                int E, int k, int renorm, float top_p, int block, const uint16_t* w_gate,
+                const uint16_t* w_up, const uint16_t* w_down, int I, const uint16_t* ws_gate,
+                const uint16_t* ws_up, const uint16_t* ws_down, int weight_layout,
+                const uint16_t* residual, uint16_t* y, int32_t* topk_idx, float* topk_w,
+                int32_t* n_kept, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
     return BDM_ERR_INVALID_ARG;
   const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
@@ -171,11 +174,41 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
   moe_layout(T, H, I, E, k, has_shared, static_cast<char*>(workspace), &meta);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, meta, topk_idx,
-                     topk_w, s);
+  bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, top_p, block,
+                     meta, topk_idx, topk_w, n_kept, s);
   bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
                       ws_down, residual, y, meta, weight_layout, s);
   return last_hip_status();
+}
+
+}  // namespace
+
+int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router,
+                          const float* router_bias, int E, int k, int renorm,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int I, const uint16_t* ws_gate, const uint16_t* ws_up,
+                          const uint16_t* ws_down, int weight_layout, const uint16_t* residual,
+                          uint16_t* y, int32_t* topk_idx, float* topk_w, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
+                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, topk_idx, topk_w,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* w_router,
+                                  const float* router_bias, int E, int k, int renorm,
+                                  float top_p, int block_tokens, const uint16_t* w_gate,
+                                  const uint16_t* w_up, const uint16_t* w_down, int I,
+                                  const uint16_t* ws_gate, const uint16_t* ws_up,
+                                  const uint16_t* ws_down, int weight_layout,
+                                  const uint16_t* residual, uint16_t* y, int32_t* topk_idx,
+                                  float* topk_w, int32_t* n_kept, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
+  if (block_tokens < 1 || block_tokens > BDM_CORESET_MAX_BLOCK) return BDM_ERR_INVALID_ARG;
+  return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, top_p, block_tokens, w_gate,
+                     w_up, w_down, I, ws_gate, ws_up, ws_down, weight_layout, residual, y,
+                     topk_idx, topk_w, n_kept, workspace, workspace_bytes, stream);
 }
 
 int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {

@@ -234,6 +234,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(
 // of its k+1 row loads before summing them in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ypair, int H,
                                                       int k, int has_shared,
+                                                      const int32_t* __restrict__ topk_idx,
                                                       const float* __restrict__ topk_w,
                                                       const uint16_t* residual, uint16_t* y) {
   const int t = blockIdx.x;
@@ -241,6 +242,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (h0 >= H) return;
   const int K1 = k + 1;
   const float* yrow = ypair + static_cast<size_t>(t) * K1 * H + h0;
+  // every row load first (a slot the block coreset selector left empty, id
+  // -1, has a row in the workspace that is loaded and then ignored)
   float4 v[BDM_MAX_TOPK + 1][2];
 #pragma unroll
   for (int j = 0; j <= BDM_MAX_TOPK; ++j) {
@@ -261,11 +264,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   }
+  uint32_t used = 0u;
+#pragma unroll
+  for (int j = 0; j < BDM_MAX_TOPK; ++j)
+    if (j < k) used |= (topk_idx[t * k + j] >= 0 ? 1u : 0u) << j;
 #pragma unroll
   for (int j = 0; j <= BDM_MAX_TOPK; ++j) {
     const float yv[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w,
                          v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
-    if (j < k) {
+    if (j < k && ((used >> j) & 1u)) {
       const float wj = topk_w[t * k + j];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, yv[i], acc[i]);
@@ -312,7 +319,8 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
     down_kernel<32, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   }
-  combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_w, residual, y);
+  combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
+                                   residual, y);
 }
 
 }  // namespace bdm

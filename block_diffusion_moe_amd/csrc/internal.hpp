@@ -21,6 +21,7 @@ struct MoeMeta {
   float* logits;        // [4][T][E]     partial router logits (fp32), one per K-part
   int32_t* topk_idx;    // [T][k]        picks, decreasing weight
   float* topk_w;        // [T][k]        their weights
+  float* topk_p;        // [T][k]        first-pass probabilities (block coreset selector)
   int32_t* ticket;      // [1]           completion ticket of the select step
   int32_t* info;        // [4]           [0] number of touched expert groups
   int4* slots;          // [E+1]         {expert, offset, count, 0} per touched group, then -1
@@ -29,9 +30,12 @@ struct MoeMeta {
   float* ypair;         // [T*(k+1)][H]  fp32 expert outputs
 };
 
+// top_p > 0: block coreset selector over blocks of `block` tokens (n_kept
+// nullable, one count per block); top_p <= 0: plain top-k routing
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                   int k, int renorm, int has_shared, const MoeMeta& meta, int32_t* user_idx,
-                   float* user_w, hipStream_t s);
+                   int k, int renorm, int has_shared, float top_p, int block,
+                   const MoeMeta& meta, int32_t* user_idx, float* user_w, int32_t* n_kept,
+                   hipStream_t s);
 
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,

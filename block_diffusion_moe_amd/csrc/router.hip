@@ -160,9 +160,10 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ part, size
 // picks are gathered into lanes 0..k-1 (ds_permute), ranked there (larger
 // logit first, equal -> lower id) and moved to the lane of their rank.
 // Returns the j-th pick and weight in lane j (j < k).
-template <int PER>
+template <int PER, bool WANT_P = false>
 __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, int renorm,
-                                          int lane, int& sel_e, float& sel_w) {
+                                          int lane, int& sel_e, float& sel_w,
+                                          float* sel_p = nullptr) {
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = (lane + kWave * i < E) ? logit_key(v[i]) : 0u;
@@ -228,104 +229,58 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
   const float sel_v = (lane < k) ? key_logit(static_cast<uint32_t>(sk)) : -INFINITY;
   sel_e = (lane < k) ? se : 0;
   const float first_v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
-  // w_j = exp(l_j - l_max) / (sum over the picks when renormalised, else over all E)
+  // w_j = exp(l_j - l_max) / (sum over the picks when renormalised, else over
+  // all E); p_j (WANT_P) = exp(l_j - l_max) / sum over all E
   const float z = (lane < k) ? expf(sel_v - first_v) : 0.0f;
-  float den;
-  if (renorm) {
-    den = wave_sum(z);
-  } else {
+  float den_all = 0.0f;
+  if (WANT_P || !renorm) {
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + kWave * i;
       if (e < E) s += expf(v[i] - first_v);
     }
-    den = wave_sum(s);
+    den_all = wave_sum(s);
   }
-  sel_w = z / den;
+  sel_w = z / (renorm ? wave_sum(z) : den_all);
+  if (WANT_P) *sel_p = z / den_all;
 }
 
 constexpr int kSelWaves = 4;       // tokens per select workgroup (one wave each)
 constexpr int kSelOneWaves = 16;   // waves of the single-workgroup select (small blocks)
 constexpr int kSelOneMaxT = 16;    // largest block the single-workgroup select takes
 
-// Top-k of every token, then the grouping of the picks by expert for the
-// expert kernels:
+// Group the T*k picks by expert for the expert kernels (every thread of the
+// workgroup calls this; picks in LDS or global memory, -1 = no expert):
 //   slots[i] = {expert, offset, count, 0} for the i-th touched group -- the
 //              shared expert (group E, all T tokens) first, then routed
 //              experts with at least 16 tokens, then the others, each run in
 //              increasing id -- and {-1, 0, 0, 0} for i = n .. E;
 //   pair_rows[offset .. offset+count) = the (token, slot) rows t*(k+1)+j of
-//              the group's tokens (shared: t*(k+1)+k).
-// SINGLE: one workgroup of NW waves takes every token (wave w: tokens w,
-// w+NW, ...), keeps the picks in LDS and groups them itself.  Otherwise one
-// wave per token, NW tokens per workgroup, and the last workgroup to finish
-// (completion ticket) groups the picks read back from global memory.
-// The order inside a group is whatever the LDS atomics produce; every row's
-// result is computed independently of the others, so outputs do not depend
-// on it.
-template <int PER, int NW, bool SINGLE>
-__global__ __launch_bounds__(NW * 64) void select_kernel(
-    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
-    int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* ticket, int4* __restrict__ slots, int32_t* __restrict__ pair_rows,
-    int32_t* __restrict__ info, int32_t* __restrict__ user_idx, float* __restrict__ user_w) {
-  __shared__ int cnt[BDM_MAX_EXPERTS + 1];
-  __shared__ int eoff[BDM_MAX_EXPERTS + 1];
-  __shared__ int fill[BDM_MAX_EXPERTS + 1];
-  __shared__ int spick[SINGLE ? kSelOneMaxT * BDM_MAX_TOPK : 1];
-  __shared__ int s_last;
+//              the group's tokens (shared: t*(k+1)+k); the ranges follow
+//              expert id order after the shared expert's [0, T).
+// Wave 0 ranks the experts: lane L holds experts L*epl .. L*epl+epl-1, so
+// (lane, j) order is id order and ballot popcounts give every touched
+// expert's slot position.  The order inside a group is whatever the LDS
+// atomics produce; every row's result is computed on its own, so outputs do
+// not depend on it.
+template <int PER>
+__device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_shared, int* cnt,
+                            int* eoff, int* fill, int4* __restrict__ slots,
+                            int32_t* __restrict__ pair_rows, int32_t* __restrict__ info) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int K1 = k + 1;
-
-  // SINGLE: this wave's two tokens (w, w + NW) load their rows together
-  const int ta = SINGLE ? wave : blockIdx.x * NW + wave;
-  const int tb = SINGLE ? wave + NW : T;
-  const size_t zs = static_cast<size_t>(T) * E;
-  float va[PER], vb[PER];
-  if (ta < T) load_logits<PER>(part + static_cast<size_t>(ta) * E, zs, bias, E, lane, va);
-  if (SINGLE && tb < T) load_logits<PER>(part + static_cast<size_t>(tb) * E, zs, bias, E, lane, vb);
-#pragma unroll
-  for (int r = 0; r < (SINGLE ? 2 : 1); ++r) {
-    const int t = r == 0 ? ta : tb;
-    if (t < T) {
-      int sel_e;
-      float sel_w;
-      topk_pick<PER>(r == 0 ? va : vb, E, k, renorm, lane, sel_e, sel_w);
-      if (lane < k) {
-        topk_idx[t * k + lane] = sel_e;
-        topk_w[t * k + lane] = sel_w;
-        if (user_idx) user_idx[t * k + lane] = sel_e;
-        if (user_w) user_w[t * k + lane] = sel_w;
-        if (SINGLE) spick[t * k + lane] = sel_e;
-      }
-    }
-  }
-  if (!SINGLE) {
-    // publish this workgroup's picks, then take a ticket
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-  }
-  const int32_t* picks = SINGLE ? spick : topk_idx;
-
-  // ---- group the T*k picks by expert --------------------------------------
-  // wave 0 ranks the experts: lane L holds experts L*epl .. L*epl+epl-1, so
-  // (lane, j) order is id order and ballot popcounts give the slot position
-  // of every touched expert (heavy ones, >= 16 tokens, first, then the
-  // light ones, each run in increasing id); pair ranges follow expert id
-  // order after the shared expert's [0, T).
   for (int e = tid; e <= E; e += blockDim.x) {
     cnt[e] = (e == E) ? (has_shared ? T : 0) : 0;
     fill[e] = 0;
   }
   __syncthreads();
-  for (int p = tid; p < T * k; p += blockDim.x) atomicAdd(&cnt[picks[p]], 1);
+  for (int p = tid; p < T * k; p += blockDim.x) {
+    const int e = picks[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   const int base = has_shared ? 1 : 0;
   if (wave == 0) {
@@ -375,6 +330,7 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
   __syncthreads();
   for (int p = tid; p < T * k; p += blockDim.x) {
     const int e = picks[p];
+    if (e < 0 || e >= E) continue;
     const int tt = p / k;
     pair_rows[eoff[e] + atomicAdd(&fill[e], 1)] = tt * K1 + (p - tt * k);
   }
@@ -382,27 +338,246 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
     for (int tt = tid; tt < T; tt += blockDim.x) pair_rows[tt] = tt * K1 + k;
 }
 
+// Top-k of every token, then the grouping of the picks by expert.
+// SINGLE: one workgroup of NW waves takes every token (wave w: token w),
+// keeps the picks in LDS and groups them itself.  Otherwise one wave per
+// token, NW tokens per workgroup, and the last workgroup to finish
+// (completion ticket) groups the picks read back from global memory.
+// FIRST (block coreset selector, first pass): the picks and their
+// probabilities over all E (topk_p) only; no grouping.
+template <int PER, int NW, bool SINGLE, bool FIRST>
+__global__ __launch_bounds__(NW * 64) void select_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
+    int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ topk_p, int32_t* ticket, int4* __restrict__ slots,
+    int32_t* __restrict__ pair_rows, int32_t* __restrict__ info, int32_t* __restrict__ user_idx,
+    float* __restrict__ user_w) {
+  __shared__ int cnt[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
+  __shared__ int eoff[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
+  __shared__ int fill[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
+  __shared__ int spick[SINGLE ? kSelOneMaxT * BDM_MAX_TOPK : 1];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+
+  const int t = SINGLE ? wave : blockIdx.x * NW + wave;
+  if (t < T) {
+    float v[PER];
+    load_logits<PER>(part + static_cast<size_t>(t) * E, static_cast<size_t>(T) * E, bias, E,
+                     lane, v);
+    int sel_e;
+    float sel_w, sel_p;
+    topk_pick<PER, FIRST>(v, E, k, renorm, lane, sel_e, sel_w, &sel_p);
+    if (lane < k) {
+      topk_idx[t * k + lane] = sel_e;
+      if (FIRST) {
+        topk_p[t * k + lane] = sel_p;
+      } else {
+        topk_w[t * k + lane] = sel_w;
+        if (user_idx) user_idx[t * k + lane] = sel_e;
+        if (user_w) user_w[t * k + lane] = sel_w;
+        if (SINGLE) spick[t * k + lane] = sel_e;
+      }
+    }
+  }
+  if constexpr (FIRST) {
+    return;
+  } else {
+  if (!SINGLE) {
+    // publish this workgroup's picks, then take a ticket
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+  }
+  group_picks<PER>(SINGLE ? spick : topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots,
+                   pair_rows, info);
+  }
+}
+
+constexpr int kCsWaves = 16;       // waves of a coreset workgroup (one block of tokens)
+
+// Block coreset expert selector, one workgroup per block of B <= 32 tokens
+// (page "Clover-35B-A3B: how a diffusion model gets to 680 tokens a second,
+// read from its files", section "The expert selection"):
+//   mass_e  = sum over the block's tokens (in order) of the first-pass
+//             probability of every pick of e;
+//   order   = touched experts by mass, larger first (equal -> lower id);
+//   kept    = the shortest prefix whose cumulative mass (fp32, fixed order)
+//             reaches top_p times the total, at least one expert;
+//   re-route: each token's top-min(k, |kept|) over the kept experts (the
+//             others at -inf), weights as in the plain routing; the rest of
+//             its k slots hold -1 and weight 0.
+// Then the grouping, by the block's own workgroup when there is one block,
+// else by the last workgroup to finish (completion ticket).
+template <int PER>
+__global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
+    int renorm, float top_p, int B, int has_shared, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, const float* __restrict__ topk_p, int32_t* ticket,
+    int4* __restrict__ slots, int32_t* __restrict__ pair_rows, int32_t* __restrict__ info,
+    int32_t* __restrict__ user_idx, float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
+  __shared__ int cnt[BDM_MAX_EXPERTS + 1];
+  __shared__ int eoff[BDM_MAX_EXPERTS + 1];
+  __shared__ int fill[BDM_MAX_EXPERTS + 1];
+  __shared__ float mass[BDM_MAX_EXPERTS];
+  __shared__ float smass[BDM_MAX_EXPERTS];      // masses in mass order
+  __shared__ int rank_of[BDM_MAX_EXPERTS];      // position in mass order, -1 untouched
+  __shared__ int sidx[kCsWaves * 2 * BDM_MAX_TOPK];
+  __shared__ float sp[kCsWaves * 2 * BDM_MAX_TOPK];
+  __shared__ int s_ntouch, s_nkeep, s_last;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int t0 = blockIdx.x * B;
+  const int nb = min(B, T - t0);                // tokens of this block
+
+  // this wave's tokens (w, w + 16) load their logit rows first
+  const int ta = wave, tb = wave + kCsWaves;
+  const size_t zs = static_cast<size_t>(T) * E;
+  float va[PER], vb[PER];
+  if (ta < nb) load_logits<PER>(part + static_cast<size_t>(t0 + ta) * E, zs, bias, E, lane, va);
+  if (tb < nb) load_logits<PER>(part + static_cast<size_t>(t0 + tb) * E, zs, bias, E, lane, vb);
+  // the block's first-pass picks and probabilities
+  for (int i = tid; i < nb * k; i += blockDim.x) {
+    sidx[i] = topk_idx[t0 * k + i];
+    sp[i] = topk_p[t0 * k + i];
+  }
+  if (tid == 0) s_ntouch = 0;
+  __syncthreads();
+  // mass of expert e: its picks' probabilities in token order
+  for (int e = tid; e < E; e += blockDim.x) {
+    float m = 0.0f;
+    for (int i = 0; i < nb * k; ++i) m += (sidx[i] == e) ? sp[i] : 0.0f;
+    mass[e] = m;
+    if (m > 0.0f) atomicAdd(&s_ntouch, 1);
+  }
+  __syncthreads();
+  // rank in mass order (larger first, equal -> lower id)
+  for (int e = tid; e < E; e += blockDim.x) {
+    const float m = mass[e];
+    int r = -1;
+    if (m > 0.0f) {
+      r = 0;
+      for (int q = 0; q < E; ++q) {
+        const float mq = mass[q];
+        r += (mq > m || (mq == m && q < e)) ? 1 : 0;
+      }
+      smass[r] = m;
+    }
+    rank_of[e] = r;
+  }
+  __syncthreads();
+  // cumulative mass in order (lane L sums a contiguous chunk, then a fixed
+  // scan over lanes) and the cut
+  if (wave == 0) {
+    const int nt = s_ntouch;
+    const int per = (nt + kWave - 1) / kWave;
+    const int i0 = lane * per;
+    float loc = 0.0f;
+    for (int i = i0; i < min(i0 + per, nt); ++i) loc += smass[i];
+    float incl = loc;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    const float total = __shfl(incl, kWave - 1, kWave);
+    const float thr = top_p * total;
+    const float up = __shfl_up(incl, 1, kWave);
+    float cum = lane == 0 ? 0.0f : up;           // exclusive prefix of this chunk
+    int below = 0;
+    for (int i = i0; i < min(i0 + per, nt); ++i) {
+      cum += smass[i];
+      below += (cum < thr) ? 1 : 0;
+    }
+    below = wave_sum_i(below);
+    if (lane == 0) {
+      const int keep = min(max(below + 1, 1), nt);
+      s_nkeep = keep;
+      if (n_kept) n_kept[blockIdx.x] = keep;
+    }
+  }
+  __syncthreads();
+  // re-route every token of the block over the kept experts
+  const int keep = s_nkeep;
+  const int kk = min(k, keep);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int tl = r == 0 ? ta : tb;
+    if (tl < nb) {
+      float v[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane + kWave * i;
+        const int rk = (e < E) ? rank_of[e] : -1;
+        v[i] = (rk >= 0 && rk < keep) ? (r == 0 ? va[i] : vb[i]) : -INFINITY;
+      }
+      int sel_e;
+      float sel_w;
+      topk_pick<PER>(v, E, kk, renorm, lane, sel_e, sel_w);
+      if (lane < k) {
+        const int t = t0 + tl;
+        const int ee = lane < kk ? sel_e : -1;
+        const float ww = lane < kk ? sel_w : 0.0f;
+        topk_idx[t * k + lane] = ee;
+        topk_w[t * k + lane] = ww;
+        if (user_idx) user_idx[t * k + lane] = ee;
+        if (user_w) user_w[t * k + lane] = ww;
+        sidx[tl * k + lane] = ee;
+      }
+    }
+  }
+  if (gridDim.x == 1) {
+    __syncthreads();
+    group_picks<PER>(sidx, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
+    return;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  group_picks<PER>(topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
+}
+
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
-                   int k, int renorm, int has_shared, const MoeMeta& meta, int32_t* user_idx,
-                   float* user_w, hipStream_t s) {
+                   int k, int renorm, int has_shared, float top_p, int block,
+                   const MoeMeta& meta, int32_t* user_idx, float* user_w, int32_t* n_kept,
+                   hipStream_t s) {
   const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
   router_kernel<<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, meta.ticket);
   const int nsel = (T + kSelWaves - 1) / kSelWaves;
+  const bool core = top_p > 0.0f;
+  const int ncs = core ? (T + block - 1) / block : 0;
 #define BDM_SELECT(P)                                                                          \
-  if (T <= kSelOneMaxT)                                                                        \
-    select_kernel<P, kSelOneWaves, true><<<1, kSelOneWaves * 64, 0, s>>>(                      \
+  if (core) {                                                                                  \
+    select_kernel<P, kSelWaves, false, true><<<nsel, kSelWaves * 64, 0, s>>>(                  \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
-  else                                                                                         \
-    select_kernel<P, kSelWaves, false><<<nsel, kSelWaves * 64, 0, s>>>(                        \
+        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+    coreset_kernel<P><<<ncs, kCsWaves * 64, 0, s>>>(                                           \
+        meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,           \
+        meta.topk_w, meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info,          \
+        user_idx, user_w, n_kept);                                                             \
+  } else if (T <= kSelOneMaxT) {                                                               \
+    select_kernel<P, kSelOneWaves, true, false><<<1, kSelOneWaves * 64, 0, s>>>(               \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w)
+        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+  } else {                                                                                     \
+    select_kernel<P, kSelWaves, false, false><<<nsel, kSelWaves * 64, 0, s>>>(                 \
+        meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
+        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+  }
   if (E <= 256) {
-    BDM_SELECT(4);
+    BDM_SELECT(4)
   } else if (E <= 512) {
-    BDM_SELECT(8);
+    BDM_SELECT(8)
   } else {
-    BDM_SELECT(16);
+    BDM_SELECT(16)
   }
 #undef BDM_SELECT
 }

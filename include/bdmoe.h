@@ -78,6 +78,7 @@ extern "C" {
 #define BDM_MAX_INTER    1024   /* I, multiple of 32 */
 #define BDM_MAX_EXPERTS  1024   /* E */
 #define BDM_MAX_TOPK       16   /* k, 1 <= k <= E */
+#define BDM_CORESET_MAX_BLOCK 32 /* tokens per block of the coreset selector */
 
 /* Library version as 10000*major + 100*minor + patch. */
 BDM_API int bdm_version(void);
@@ -151,6 +152,51 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           int weight_layout,
                           const uint16_t* residual, uint16_t* y,
                           int32_t* topk_idx, float* topk_w,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bdm_moe_block_forward_coreset -- the same layer with the block coreset
+ * expert selector in front of the experts.
+ *
+ * [files] "The expert selection": for a block, every token's top-8 routing
+ * probabilities are added up per expert, the experts are sorted by that
+ * total, the smallest set whose share of the total reaches top_p is kept
+ * (never fewer than the top expert), and no token of the block may route
+ * outside it; [files] "What Clover is": the selector is on with top_p 0.9.
+ *
+ * For every block of block_tokens consecutive rows of x (the last one may be
+ * shorter), with p_t = softmax(l_t) over all E and S_t the first-pass picks
+ * of bdm_moe_block_forward:
+ *   mass_e = sum over the block's tokens, in order, of p_t[e] for e in S_t
+ *            (fp32)
+ *   order  = experts with mass > 0, larger mass first (equal: lower id)
+ *   kept   = the shortest prefix of order whose cumulative mass (fp32, in
+ *            that order) reaches top_p * total mass; at least one expert
+ *   S'_t   = the min(k, |kept|) kept experts with the largest l_t (equal:
+ *            lower id); w'_t as in bdm_moe_block_forward with the logits of
+ *            the other experts at -inf; slots past |S'_t| hold expert -1
+ *            and weight 0 and contribute nothing
+ * and then y as in bdm_moe_block_forward with S', w'.
+ *
+ * Arguments as in bdm_moe_block_forward, plus
+ *   top_p         in (0, 1]; 1 keeps every touched expert
+ *   block_tokens  tokens per block, 1 .. BDM_CORESET_MAX_BLOCK (32)
+ *   n_kept        [ceil(T / block_tokens)] int32 device array or NULL:
+ *                 receives |kept| per block
+ *   topk_idx/topk_w receive S', w' (-1 / 0 in the empty slots)
+ * Workspace: bdm_moe_workspace_bytes for the same sizes.  Errors as in
+ * bdm_moe_block_forward; top_p or block_tokens out of range ->
+ * BDM_ERR_INVALID_ARG.
+ */
+BDM_API int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H,
+                          const float* w_router, const float* router_bias, int E, int k,
+                          int renorm, float top_p, int block_tokens,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int I,
+                          const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                          int weight_layout,
+                          const uint16_t* residual, uint16_t* y,
+                          int32_t* topk_idx, float* topk_w, int32_t* n_kept,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
                            "bdm_moe_block_forward", "bdm_head_workspace_bytes",
                            "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
                            "bdm_pack_weights", "bdm_head_stat_parts", "bdm_lm_head_stats",
-                           "bdm_unmask_from_stats"])
+                           "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -184,3 +184,20 @@ def test_calibration_library_exports():
     assert f(None, _fake(1 << 20), 16384, None) == -1
     assert f(_fake(1 << 20), _fake(1 << 21), 16000, None) == -1
     assert f(_fake(1 << 20), _fake(1 << 20), 16384, None) == -1
+
+
+def test_coreset_validation(lib):
+    A = _fake(1 << 20)
+    size = 1 << 30
+
+    def call(top_p=0.9, block=32, T=32):
+        return lib.bdm_moe_block_forward_coreset(
+            A, T, 2048, A, None, 256, 8, 1, top_p, block, A, A, A, 512, A, A, A, 0, None, A,
+            None, None, None, A, size, None)
+    assert call(top_p=0.0) == -1
+    assert call(top_p=-0.5) == -1
+    assert call(top_p=1.5) == -1
+    assert call(top_p=float("nan")) == -1
+    assert call(block=0) == -1
+    assert call(block=33) == -1
+    assert call(T=2000) == -2
