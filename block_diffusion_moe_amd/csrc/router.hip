@@ -343,8 +343,8 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
 // keeps the picks in LDS and groups them itself.  Otherwise one wave per
 // token, NW tokens per workgroup, and the last workgroup to finish
 // (completion ticket) groups the picks read back from global memory.
-// FIRST (block coreset selector, first pass): the picks and their
-// probabilities over all E (topk_p) only; no grouping.
+// FIRST (first pass of the block coreset selector): the picks, their
+// weights and their probabilities over all E (topk_p) only; no grouping.
 template <int PER, int NW, bool SINGLE, bool FIRST>
 __global__ __launch_bounds__(NW * 64) void select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
@@ -371,40 +371,136 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
     topk_pick<PER, FIRST>(v, E, k, renorm, lane, sel_e, sel_w, &sel_p);
     if (lane < k) {
       topk_idx[t * k + lane] = sel_e;
-      if (FIRST) {
-        topk_p[t * k + lane] = sel_p;
-      } else {
-        topk_w[t * k + lane] = sel_w;
-        if (user_idx) user_idx[t * k + lane] = sel_e;
-        if (user_w) user_w[t * k + lane] = sel_w;
-        if (SINGLE) spick[t * k + lane] = sel_e;
-      }
+      topk_w[t * k + lane] = sel_w;
+      if (FIRST) topk_p[t * k + lane] = sel_p;
+      if (!FIRST && user_idx) user_idx[t * k + lane] = sel_e;
+      if (!FIRST && user_w) user_w[t * k + lane] = sel_w;
+      if (SINGLE) spick[t * k + lane] = sel_e;
     }
   }
-  if constexpr (FIRST) {
-    return;
-  } else {
-  if (!SINGLE) {
-    // publish this workgroup's picks, then take a ticket
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-  }
-  group_picks<PER>(SINGLE ? spick : topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots,
-                   pair_rows, info);
+  if constexpr (!FIRST) {
+    if (!SINGLE) {
+      // publish this workgroup's picks, then take a ticket
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
+      __syncthreads();
+      if (!s_last) return;
+      __threadfence();
+    }
+    group_picks<PER>(SINGLE ? spick : topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots,
+                     pair_rows, info);
   }
 }
 
 constexpr int kCsWaves = 16;       // waves of a coreset workgroup (one block of tokens)
 
+// Re-route one token over the kept experts, given its first-pass picks (lane
+// j < k holds pick j in `fe`, decreasing logit) and its logit row v.  The
+// kept first-pass picks stay first, in their order (they are the token's
+// largest logits); the remaining min(k, keep) - (kept first-pass picks)
+// slots take the largest logits among kept experts that were not picked
+// (wave argmax rounds, equal -> lower id).  Weights as in topk_pick over the
+// kept experts.  Lane s < k returns slot s (-1 / 0 past min(k, keep)).
+template <int PER>
+__device__ __forceinline__ void reroute_pick(const float (&v)[PER], int fe, const int* rank_of,
+                                             int keep, int E, int k, int renorm, int lane,
+                                             int& sel_e, float& sel_w) {
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const bool fkeep = lane < k && fe >= 0 && rank_of[fe] >= 0 && rank_of[fe] < keep;
+  const unsigned long long km = __ballot(fkeep);
+  const int nfk = __popcll(km);
+  const int kk = min(k, keep);
+  // which of this lane's experts are first-pass picks, which are kept
+  uint32_t picked = 0u, allowed = 0u;
+#pragma unroll
+  for (int q = 0; q < BDM_MAX_TOPK; ++q) {
+    if (q < k) {
+      const int eq = __builtin_amdgcn_readlane(fe, q);
+      if ((eq & (kWave - 1)) == lane) picked |= 1u << (eq / kWave);
+    }
+  }
+  float cv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    const int r = e < E ? rank_of[e] : -1;
+    const bool ok = r >= 0 && r < keep;
+    allowed |= (ok ? 1u : 0u) << i;
+    cv[i] = (ok && !((picked >> i) & 1u)) ? v[i] : -INFINITY;
+  }
+  // the new picks: lane r (< nnew) receives the r-th one
+  const int nnew = kk - nfk;
+  int ne = -1;
+  float nv = -INFINITY;
+  for (int r = 0; r < nnew; ++r) {
+    float bv = -INFINITY;
+    int be = INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + kWave * i;
+      if (cv[i] > bv || (cv[i] == bv && cv[i] != -INFINITY && e < be)) {
+        bv = cv[i];
+        be = e;
+      }
+    }
+    wave_argmax(bv, be);
+    if (lane == r) {
+      ne = be;
+      nv = bv;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + kWave * i == be) cv[i] = -INFINITY;
+  }
+  // logit of this lane's first-pass pick (from the lane that holds it)
+  const int src = (fe >= 0 ? fe : 0) & (kWave - 1);
+  float fv = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float x = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(v[i])));
+    if (fe >= 0 && fe / kWave == i) fv = x;
+  }
+  // slots: kept first-pass picks (pushed to their compact position), then
+  // the new ones (pulled from lanes 0 .. nnew-1)
+  const int dst = fkeep ? __popcll(km & below) : kWave - 1;
+  const int pe = __builtin_amdgcn_ds_permute(dst * 4, fe);
+  const float pv = __int_as_float(__builtin_amdgcn_ds_permute(dst * 4, __float_as_int(fv)));
+  const int from = (lane >= nfk && lane < kk) ? lane - nfk : 0;
+  const int qe = __builtin_amdgcn_ds_bpermute(from * 4, ne);
+  const float qv = __int_as_float(__builtin_amdgcn_ds_bpermute(from * 4, __float_as_int(nv)));
+  float sel_v = -INFINITY;
+  sel_e = -1;
+  if (lane < nfk) {
+    sel_e = pe;
+    sel_v = pv;
+  } else if (lane < kk) {
+    sel_e = qe;
+    sel_v = qv;
+  }
+  const float first_v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
+  const float z = (lane < kk) ? expf(sel_v - first_v) : 0.0f;
+  float den;
+  if (renorm) {
+    den = wave_sum(z);
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((allowed >> i) & 1u) s += expf(v[i] - first_v);
+    den = wave_sum(s);
+  }
+  sel_w = (lane < kk) ? z / den : 0.0f;
+}
+
 // Block coreset expert selector, one workgroup per block of B <= 32 tokens
 // (page "Clover-35B-A3B: how a diffusion model gets to 680 tokens a second,
 // read from its files", section "The expert selection"):
-//   mass_e  = sum over the block's tokens (in order) of the first-pass
-//             probability of every pick of e;
+//   first pass (select_kernel FIRST): every token's top-k, weights and the
+//             picks' probabilities over all E;
+//   mass_e  = sum over the block's tokens of the probabilities of the picks
+//             of e (fp32; four partial sums over token ranges, added in a
+//             fixed order);
 //   order   = touched experts by mass, larger first (equal -> lower id);
 //   kept    = the shortest prefix whose cumulative mass (fp32, fixed order)
 //             reaches top_p times the total, at least one expert;
@@ -420,54 +516,111 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     float* __restrict__ topk_w, const float* __restrict__ topk_p, int32_t* ticket,
     int4* __restrict__ slots, int32_t* __restrict__ pair_rows, int32_t* __restrict__ info,
     int32_t* __restrict__ user_idx, float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
+  constexpr int kParts = 4;                     // partial sums per expert mass
   __shared__ int cnt[BDM_MAX_EXPERTS + 1];
   __shared__ int eoff[BDM_MAX_EXPERTS + 1];
   __shared__ int fill[BDM_MAX_EXPERTS + 1];
-  __shared__ float mass[BDM_MAX_EXPERTS];
+  __shared__ __align__(16) float mass[BDM_MAX_EXPERTS];
+  __shared__ float mpart[kParts][BDM_MAX_EXPERTS];
   __shared__ float smass[BDM_MAX_EXPERTS];      // masses in mass order
   __shared__ int rank_of[BDM_MAX_EXPERTS];      // position in mass order, -1 untouched
-  __shared__ int sidx[kCsWaves * 2 * BDM_MAX_TOPK];
-  __shared__ float sp[kCsWaves * 2 * BDM_MAX_TOPK];
+  __shared__ __align__(16) int sidx[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
+  __shared__ __align__(16) float sp[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
+  __shared__ float sw[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
   __shared__ int s_ntouch, s_nkeep, s_last;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int t0 = blockIdx.x * B;
   const int nb = min(B, T - t0);                // tokens of this block
+  const int E16 = (E + 15) & ~15;
+  const int nbk = nb * k;
+  const int nbk16 = (nbk + 15) & ~15;
 
-  // this wave's tokens (w, w + 16) load their logit rows first
+  // this wave's tokens (w, w + 16): logit rows for the re-route; the block's
+  // first-pass picks (padded with id -1 to a multiple of 16), weights and
+  // probabilities
   const int ta = wave, tb = wave + kCsWaves;
   const size_t zs = static_cast<size_t>(T) * E;
   float va[PER], vb[PER];
   if (ta < nb) load_logits<PER>(part + static_cast<size_t>(t0 + ta) * E, zs, bias, E, lane, va);
   if (tb < nb) load_logits<PER>(part + static_cast<size_t>(t0 + tb) * E, zs, bias, E, lane, vb);
-  // the block's first-pass picks and probabilities
-  for (int i = tid; i < nb * k; i += blockDim.x) {
-    sidx[i] = topk_idx[t0 * k + i];
-    sp[i] = topk_p[t0 * k + i];
+  for (int i = tid; i < nbk16; i += blockDim.x) {
+    const bool in = i < nbk;
+    sidx[i] = in ? topk_idx[t0 * k + i] : -1;
+    sp[i] = in ? topk_p[t0 * k + i] : 0.0f;
+    sw[i] = in ? topk_w[t0 * k + i] : 0.0f;
   }
+  for (int e = tid; e < E16; e += blockDim.x) mass[e] = 0.0f;
   if (tid == 0) s_ntouch = 0;
   __syncthreads();
-  // mass of expert e: its picks' probabilities in token order
-  for (int e = tid; e < E; e += blockDim.x) {
+  // mass: kParts threads per expert, each over a contiguous range of the
+  // picks (in token order), then the partial sums in part order
+  const int nparts = (static_cast<int>(blockDim.x) / E16 >= kParts) ? kParts : 1;
+  const int chunk = ((nbk16 / 16 + nparts - 1) / nparts) * 16;
+  for (int w = tid; w < E * nparts; w += blockDim.x) {
+    const int e = w % E;
+    const int pp = w / E;
+    const int i1 = min(nbk16, (pp + 1) * chunk);
     float m = 0.0f;
-    for (int i = 0; i < nb * k; ++i) m += (sidx[i] == e) ? sp[i] : 0.0f;
+    for (int i0 = pp * chunk; i0 < i1; i0 += 16) {
+      int4 id[4];
+      float4 pv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        id[u] = *reinterpret_cast<const int4*>(sidx + i0 + 4 * u);
+        pv[u] = *reinterpret_cast<const float4*>(sp + i0 + 4 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m += (id[u].x == e) ? pv[u].x : 0.0f;
+        m += (id[u].y == e) ? pv[u].y : 0.0f;
+        m += (id[u].z == e) ? pv[u].z : 0.0f;
+        m += (id[u].w == e) ? pv[u].w : 0.0f;
+      }
+    }
+    mpart[pp][e] = m;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    float m = mpart[0][e];
+    for (int pp = 1; pp < nparts; ++pp) m += mpart[pp][e];
     mass[e] = m;
+    cnt[e] = 0;
     if (m > 0.0f) atomicAdd(&s_ntouch, 1);
   }
   __syncthreads();
-  // rank in mass order (larger first, equal -> lower id)
+  // rank in mass order (larger first, equal -> lower id): kParts threads
+  // per expert count over quarters of the experts; masses past E are 0
+  const int qchunk = ((E16 / 16 + nparts - 1) / nparts) * 16;
+  for (int w = tid; w < E * nparts; w += blockDim.x) {
+    const int e = w % E;
+    const int pp = w / E;
+    const float m = mass[e];
+    if (m > 0.0f) {
+      int r = 0;
+      const int q1 = min(E16, (pp + 1) * qchunk);
+      for (int q0 = pp * qchunk; q0 < q1; q0 += 16) {
+        float4 mv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mv[u] = *reinterpret_cast<const float4*>(mass + q0 + 4 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + 4 * u;
+          r += (mv[u].x > m || (mv[u].x == m && q < e)) ? 1 : 0;
+          r += (mv[u].y > m || (mv[u].y == m && q + 1 < e)) ? 1 : 0;
+          r += (mv[u].z > m || (mv[u].z == m && q + 2 < e)) ? 1 : 0;
+          r += (mv[u].w > m || (mv[u].w == m && q + 3 < e)) ? 1 : 0;
+        }
+      }
+      atomicAdd(&cnt[e], r);                    // integer counts: any order
+    }
+  }
+  __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const float m = mass[e];
-    int r = -1;
-    if (m > 0.0f) {
-      r = 0;
-      for (int q = 0; q < E; ++q) {
-        const float mq = mass[q];
-        r += (mq > m || (mq == m && q < e)) ? 1 : 0;
-      }
-      smass[r] = m;
-    }
+    const int r = (m > 0.0f) ? cnt[e] : -1;
+    if (r >= 0) smass[r] = m;
     rank_of[e] = r;
   }
   __syncthreads();
@@ -502,32 +655,31 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     }
   }
   __syncthreads();
-  // re-route every token of the block over the kept experts
+  // re-route every token of the block over the kept experts; a token whose
+  // first-pass picks are all kept keeps them and (renormalised) their
+  // weights, which is what the re-route would compute
   const int keep = s_nkeep;
-  const int kk = min(k, keep);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int tl = r == 0 ? ta : tb;
     if (tl < nb) {
-      float v[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = lane + kWave * i;
-        const int rk = (e < E) ? rank_of[e] : -1;
-        v[i] = (rk >= 0 && rk < keep) ? (r == 0 ? va[i] : vb[i]) : -INFINITY;
-      }
+      const int fe = lane < k ? sidx[tl * k + lane] : -1;
+      const bool fkeep = lane < k && fe >= 0 && rank_of[fe] >= 0 && rank_of[fe] < keep;
       int sel_e;
       float sel_w;
-      topk_pick<PER>(v, E, kk, renorm, lane, sel_e, sel_w);
+      if (renorm && __popcll(__ballot(fkeep)) == k) {
+        sel_e = fe;
+        sel_w = lane < k ? sw[tl * k + lane] : 0.0f;
+      } else {
+        reroute_pick<PER>(r == 0 ? va : vb, fe, rank_of, keep, E, k, renorm, lane, sel_e, sel_w);
+      }
       if (lane < k) {
         const int t = t0 + tl;
-        const int ee = lane < kk ? sel_e : -1;
-        const float ww = lane < kk ? sel_w : 0.0f;
-        topk_idx[t * k + lane] = ee;
-        topk_w[t * k + lane] = ww;
-        if (user_idx) user_idx[t * k + lane] = ee;
-        if (user_w) user_w[t * k + lane] = ww;
-        sidx[tl * k + lane] = ee;
+        topk_idx[t * k + lane] = sel_e;
+        topk_w[t * k + lane] = sel_w;
+        if (user_idx) user_idx[t * k + lane] = sel_e;
+        if (user_w) user_w[t * k + lane] = sel_w;
+        sidx[tl * k + lane] = sel_e;            // this wave's own entries only
       }
     }
   }
