@@ -21,6 +21,11 @@ factor is reported for comparison only.
         writes a markdown summary with a per-kernel table; its first lines are
         `<!-- key = value -->` records (source digest, traffic of the head GEMM
         kernel) that bench.py reads back.
+    python -m block_diffusion_moe_amd.traffic mfma --dir DIR --out FILE [--command TEXT]
+        per-kernel matrix-core activity from one counter pass of
+        SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16
+        and GRBM_GUI_ACTIVE: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+        (GRBM_GUI_ACTIVE x CUs x 4 SIMDs).
 """
 from __future__ import annotations
 
@@ -140,6 +145,36 @@ def summarize(a):
     print("\n".join(out))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "GRBM_GUI_ACTIVE")
+
+
+def mfma(a):
+    agg = read_counters(a.dir)
+    names = sorted({n for n, _ in agg if "bdm" in n})
+    out = ["# Matrix-core (MFMA) activity per kernel (rocprofv3 counters)", ""]
+    if a.command:
+        out += ["Made by:", "", "```", a.command, "```", ""]
+    out += [f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {a.cus} CUs x 4 SIMDs); "
+            "means per dispatch.", "",
+            "| kernel | dispatches | GRBM_GUI_ACTIVE | SQ_BUSY_CYCLES | SQ_VALU_MFMA_BUSY_CYCLES "
+            "| SQ_INSTS_VALU_MFMA_MOPS_BF16 | MFMA busy |",
+            "|---|---:|---:|---:|---:|---:|---:|"]
+    for n in names:
+        v = {c: agg.get((n, c), []) for c in MFMA_COUNTERS}
+        if not all(v.values()):
+            continue
+        m = {c: sum(x) / len(x) for c, x in v.items()}
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, m["GRBM_GUI_ACTIVE"] * a.cus * 4)
+        out.append(f"| `{n}` | {len(v['GRBM_GUI_ACTIVE'])} | {m['GRBM_GUI_ACTIVE']:.4g} | "
+                   f"{m['SQ_BUSY_CYCLES']:.4g} | {m['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | "
+                   f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} | {100 * busy:.2f}% |")
+    out.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(out))
+    print("\n".join(out))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -148,9 +183,16 @@ def main(argv=None):
     for k in ("fetch", "write", "cal_fetch", "cal_write", "out"):
         s.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     s.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("--dir", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--cus", type=int, default=256)
+    m.add_argument("--command", default="")
     a = p.parse_args(argv)
     if a.cmd == "copy":
         copy_kernel()
+    elif a.cmd == "mfma":
+        mfma(a)
     else:
         summarize(a)
 

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.coreset as C
+import oracle.denoise as D
 import oracle.head as H
 import oracle.moe as M
 import oracle.norm as N
@@ -124,7 +125,23 @@ def _order_ascending(mass):
     return touched[np.lexsort((touched, mass[touched]))]
 
 
+def _step_no_final_norm(tokens, embed_bits, layers, head_bits, k, mask_id, threshold=0.95,
+                        eps=1e-6):
+    import oracle.stack as S
+    tokens = np.asarray(tokens, dtype=np.int64)
+    y, near = S.stack_forward(np.asarray(embed_bits)[tokens], layers, k, eps)
+    out = H.head_unmask(y, head_bits, tokens, mask_id, threshold)
+    out["near_route"] = near.any(axis=0)
+    return out
+
+
+def _loop_one_step(orig):
+    return lambda *a, **kw: orig(*a, **dict(kw, max_steps=1))
+
+
 MUTANTS = {
+    "denoise_no_final_norm": (D, "denoise_step", lambda o: _step_no_final_norm),
+    "denoise_stops_after_one_step": (D, "denoise_block", _loop_one_step),
     "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
     "coreset_cut_one_more": (C, "cut", _cut_one_more),
     "coreset_mass_ties_high_id": (C, "mass_order", lambda o: _order_ties_high),
@@ -163,6 +180,9 @@ PINS = [
     P.test_coreset_equal_masses_keep_lower_id,
     P.test_coreset_top_p_one_keeps_routing_and_tiny_top_p_keeps_one,
     P.test_coreset_sets_nest_and_restrict_routing,
+    P.test_denoise_loop_terminates_commits_and_never_revisits,
+    P.test_denoise_step_is_its_parts_composed,
+    P.test_denoise_confident_block_finishes_in_one_step,
 ]
 
 

@@ -518,3 +518,67 @@ def test_coreset_sets_nest_and_restrict_routing():
                 if set(r["first"][t].tolist()) <= kept:
                     assert list(r["idx"][t]) == list(r["first"][t])
         prev = [set(r["kept"][b].tolist()) for b in range(2)]
+
+
+# --------------------------------------------------------------------------
+# The denoise loop (files page, "How it writes")
+# --------------------------------------------------------------------------
+
+def _tiny_model(seed=0, L=3, V=96, H=64, E=8, I=32, k=2):
+    rng = np.random.default_rng(seed)
+    b = lambda *s, sd=0.02: bf16.from_f64(rng.standard_normal(s) * sd)  # noqa: E731
+    layers = [{"w_router": (rng.standard_normal((E, H)) * 0.2).astype(np.float32),
+               "w_gate": b(E, I, H), "w_up": b(E, I, H), "w_down": b(E, H, I),
+               "ws_gate": b(I, H), "ws_up": b(I, H), "ws_down": b(H, I)} for _ in range(L)]
+    return layers, b(V, H, sd=1.0), b(V, H, sd=0.3)
+
+
+def test_denoise_loop_terminates_commits_and_never_revisits():
+    from oracle import denoise
+    layers, emb, wh = _tiny_model()
+    T, mask = 8, 5
+    tokens = np.full(T, mask)
+    tokens[3] = 17                              # one slot already committed
+    final, commits = denoise.denoise_block(tokens, emb, layers, wh, 2, mask, 0.95)
+    assert 1 <= len(commits) <= T - 1
+    assert all(c >= 1 for c in commits) and sum(commits) == T - 1
+    assert not (final == mask).any() and final[3] == 17
+    # the same loop one step at a time: each step's commits stay committed
+    cur = tokens.copy()
+    for c in commits:
+        out = denoise.denoise_step(cur, emb, layers, wh, 2, mask, 0.95)
+        done = cur != mask
+        assert np.array_equal(out["tokens"][done], cur[done])
+        assert out["n_committed"] == c
+        cur = out["tokens"]
+    assert np.array_equal(cur, final)
+    # an unmasked block takes no step
+    f2, c2 = denoise.denoise_block(final, emb, layers, wh, 2, mask, 0.95)
+    assert c2 == [] and np.array_equal(f2, final)
+
+
+def test_denoise_step_is_its_parts_composed():
+    from oracle import denoise
+    layers, emb, wh = _tiny_model(seed=1)
+    tokens = np.array([5, 5, 9, 5, 5, 40, 5, 5])
+    out = denoise.denoise_step(tokens, emb, layers, wh, 2, 5, 0.95)
+    x = emb[tokens]
+    for lw in layers:
+        xn = norm.rmsnorm(x, 1e-6)
+        x = moe.moe_block(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"], 2,
+                          lw["ws_gate"], lw["ws_up"], lw["ws_down"], residual=x)["y"]
+    ref = head.head_unmask(norm.rmsnorm(x, 1e-6), wh, tokens, 5, 0.95)
+    assert np.array_equal(out["tokens"], ref["tokens"])
+    np.testing.assert_allclose(out["conf"], ref["conf"], rtol=0, atol=0)
+
+
+def test_denoise_confident_block_finishes_in_one_step():
+    """A threshold no probability can miss (0 < conf always) commits every
+    masked slot in the first step; a threshold above 1 commits one per step."""
+    from oracle import denoise
+    layers, emb, wh = _tiny_model(seed=2)
+    tokens = np.full(6, 3)
+    final, commits = denoise.denoise_block(tokens, emb, layers, wh, 2, 3, 0.0)
+    assert commits == [6] and not (final == 3).any()
+    final, commits = denoise.denoise_block(tokens, emb, layers, wh, 2, 3, 1.5)
+    assert commits == [1] * 6
