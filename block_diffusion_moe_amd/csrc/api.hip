@@ -248,7 +248,7 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   bdm::launch_head_stats(h, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s, parts.a,
                          parts.grid, parts.grid, s);
   bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
-                     fallback, tokens, argmax, conf, n_committed, s);
+                     fallback, tokens, argmax, conf, n_committed, nullptr, s);
   return last_hip_status();
 }
 
@@ -293,8 +293,127 @@ int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum, const in
   if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
   (void)hipGetLastError();
   bdm::launch_unmask(stat_max, stat_sum, stat_arg, T, parts, stat_stride, mask_id, threshold,
-                     fallback, tokens, argmax, conf, n_committed, static_cast<hipStream_t>(stream));
+                     fallback, tokens, argmax, conf, n_committed, nullptr,
+                     static_cast<hipStream_t>(stream));
   return last_hip_status();
+}
+
+// Workspace of the denoise loop: the MoE layer's, the head's partials, the
+// block's hidden state and its normalised copy, two step counters.
+size_t denoise_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
+                      bdm::MoeMeta* meta, bdm::HeadParts* parts, uint16_t** x, uint16_t** xn,
+                      int32_t** counters) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  const size_t nm = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
+  char* m = take(nm);
+  const size_t nh = head_layout(T, nullptr, nullptr);
+  char* h = take(nh);
+  char* xa = take(sizeof(uint16_t) * static_cast<size_t>(T) * H);
+  char* xb = take(sizeof(uint16_t) * static_cast<size_t>(T) * H);
+  char* c = take(sizeof(int32_t) * 4);
+  if (base) {
+    moe_layout(T, H, I, E, k, has_shared, m, meta);
+    head_layout(T, h, parts);
+    *x = reinterpret_cast<uint16_t*>(xa);
+    *xn = reinterpret_cast<uint16_t*>(xb);
+    *counters = reinterpret_cast<int32_t*>(c);
+  }
+  return off;
+}
+
+int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
+                                size_t* bytes) {
+  if (!bytes) return BDM_ERR_INVALID_ARG;
+  const int st = check_moe_shape(T, H, I, E, k, has_shared);
+  if (st != BDM_OK) return st;
+  *bytes = denoise_layout(T, H, I, E, k, has_shared, nullptr, nullptr, nullptr, nullptr, nullptr,
+                          nullptr);
+  return BDM_OK;
+}
+
+int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
+                      const bdm_moe_layer* layers, int L, int E, int k, int I, int renorm,
+                      const uint16_t* w_head, int weight_layout, int32_t mask_id, float threshold,
+                      int max_steps, int* steps_taken, int32_t* commits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!tokens || !w_embed || !w_head || !steps_taken || !workspace || (L > 0 && !layers))
+    return BDM_ERR_INVALID_ARG;
+  if (L < 0 || max_steps < 0 || (renorm != 0 && renorm != 1)) return BDM_ERR_INVALID_ARG;
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+    return BDM_ERR_INVALID_ARG;
+  if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
+    return BDM_ERR_INVALID_ARG;
+  int has_shared = 1;
+  for (int l = 0; l < L; ++l) {
+    const bdm_moe_layer& w = layers[l];
+    if (!w.w_router || !w.w_gate || !w.w_up || !w.w_down) return BDM_ERR_INVALID_ARG;
+    const int ns = (w.ws_gate != nullptr) + (w.ws_up != nullptr) + (w.ws_down != nullptr);
+    if (ns != 0 && ns != 3) return BDM_ERR_INVALID_ARG;
+    if (l == 0) has_shared = ns == 3;
+    else if ((ns == 3) != (has_shared == 1)) return BDM_ERR_INVALID_ARG;
+    if (!aligned16(w.w_router) || !aligned16(w.w_gate) || !aligned16(w.w_up) ||
+        !aligned16(w.w_down) ||
+        (ns == 3 && (!aligned16(w.ws_gate) || !aligned16(w.ws_up) || !aligned16(w.ws_down))))
+      return BDM_ERR_INVALID_ARG;
+  }
+  int st = check_moe_shape(T, H, I, E, k, has_shared);
+  if (st != BDM_OK) return st;
+  st = check_head_shape(T, H, V);
+  if (st != BDM_OK) return st;
+  if (mask_id < 0 || mask_id >= V) return BDM_ERR_INVALID_ARG;
+  if (!aligned16(w_embed) || !aligned16(w_head) ||
+      (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return BDM_ERR_INVALID_ARG;
+  const size_t need = denoise_layout(T, H, I, E, k, has_shared, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr);
+  if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
+  int cus = 0;
+  st = device_setup(&cus);
+  if (st != BDM_OK) return st;
+
+  bdm::MoeMeta meta;
+  bdm::HeadParts parts;
+  uint16_t *x = nullptr, *xn = nullptr;
+  int32_t* cnt = nullptr;
+  denoise_layout(T, H, I, E, k, has_shared, static_cast<char*>(workspace), &meta, &parts, &x, &xn,
+                 &cnt);
+  parts.grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int steps = 0;
+  *steps_taken = 0;
+  while (steps < max_steps) {
+    bdm::launch_embed(tokens, T, w_embed, V, H, x, s);
+    for (int l = 0; l < L; ++l) {
+      const bdm_moe_layer& w = layers[l];
+      bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
+      bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared, 0.0f, 0,
+                         meta, nullptr, nullptr, nullptr, s);
+      bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
+                          w.ws_up, w.ws_down, x, x, meta, weight_layout, s);
+    }
+    bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
+    bdm::launch_head_stats(xn, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s,
+                           parts.a, parts.grid, parts.grid, s);
+    bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
+                       1, tokens, nullptr, nullptr, cnt, cnt + 1, s);
+    int32_t host[2] = {0, 0};
+    if (hipMemcpyAsync(host, cnt, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return BDM_ERR_HIP;
+    st = last_hip_status();
+    if (st != BDM_OK) return st;
+    if (commits) commits[steps] = host[0];
+    ++steps;
+    *steps_taken = steps;
+    if (host[1] <= 0 || host[0] <= 0) break;      // nothing masked is left
+  }
+  return BDM_OK;
 }
 
 int bdm_packed_weight_elems(long rows, int cols, size_t* n) {

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
     int T, int nparts, int pstride, int32_t mask_id, float threshold, int fallback,
     int32_t* tokens,
     int32_t* __restrict__ argmax_out, float* __restrict__ conf_out,
-    int32_t* __restrict__ n_committed) {
+    int32_t* __restrict__ n_committed, int32_t* __restrict__ n_left) {
   extern __shared__ float smem[];
   float* sconf = smem;                                   // [T]
   int* sarg = reinterpret_cast<int*>(smem + T);         // [T]
@@ -287,12 +287,13 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   // Commit rule, one wave.  Best masked row for the fallback: largest conf,
   // equal -> lowest position.
   const int lane = tid;
-  int ncommit = 0;
+  int ncommit = 0, nmasked = 0;
   float best_c = -INFINITY;
   int best_t = INT32_MAX;
   for (int t0 = 0; t0 < T; t0 += kWave) {
     const int t = t0 + lane;
     int commit = 0;
+    nmasked += wave_sum_i((t < T && stok[t] == mask_id) ? 1 : 0);
     if (t < T && stok[t] == mask_id) {
       const float cf = sconf[t];
       if (cf >= threshold) commit = 1;
@@ -310,6 +311,7 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
     ncommit = 1;
   }
   if (lane == 0 && n_committed) *n_committed = ncommit;
+  if (lane == 0 && n_left) *n_left = nmasked - ncommit;
 }
 
 // the k-batch must divide H/32 (always even), else batches of 2 k-steps
@@ -340,10 +342,11 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
 
 void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
                    int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
-                   int32_t* argmax, float* conf, int32_t* n_committed, hipStream_t s) {
+                   int32_t* argmax, float* conf, int32_t* n_committed, int32_t* n_left,
+                   hipStream_t s) {
   head_merge_kernel<<<1, 1024, static_cast<size_t>(T) * 12, s>>>(
       pm, ps, pa, T, parts, pstride, mask_id, threshold, fallback, tokens, argmax, conf,
-      n_committed);
+      n_committed, n_left);
 }
 
 int head_prepare() {

@@ -61,9 +61,15 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
                        int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
                        int pstride, int grid, hipStream_t s);
 
+// n_left (nullable): masked rows that remain after the rule
 void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
                    int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
-                   int32_t* argmax, float* conf, int32_t* n_committed, hipStream_t s);
+                   int32_t* argmax, float* conf, int32_t* n_committed, int32_t* n_left,
+                   hipStream_t s);
+
+// x[t] = w_embed[tokens[t]] (ids clamped to [0, V)), bf16 rows of H
+void launch_embed(const int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
+                  uint16_t* x, hipStream_t s);
 
 void launch_pack(const uint16_t* src, long R, int K, uint16_t* dst, hipStream_t s);
 

@@ -200,6 +200,66 @@ BDM_API int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bdm_moe_layer -- the device weights of one MoE layer for bdm_denoise_block
+ * (the arrays of bdm_moe_block_forward; router_bias and the ws_* trio may be
+ * NULL, the trio all or none and the same choice in every layer).
+ */
+typedef struct bdm_moe_layer {
+  const float* w_router;       /* [E][H] fp32 */
+  const float* router_bias;    /* [E] fp32 or NULL */
+  const uint16_t* w_gate;      /* [E][I][H] bf16 */
+  const uint16_t* w_up;        /* [E][I][H] bf16 */
+  const uint16_t* w_down;      /* [E][H][I] bf16 */
+  const uint16_t* ws_gate;     /* [I][H] bf16 or NULL */
+  const uint16_t* ws_up;       /* [I][H] bf16 or NULL */
+  const uint16_t* ws_down;     /* [H][I] bf16 or NULL */
+} bdm_moe_layer;
+
+/*
+ * bdm_denoise_workspace_bytes -- workspace size for bdm_denoise_block (host
+ * arithmetic; same validation as bdm_moe_workspace_bytes).
+ */
+BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int has_shared,
+                                        size_t* bytes);
+
+/*
+ * bdm_denoise_block -- the denoise loop over one block.
+ *
+ * [files] "How it writes": a block starts masked; each step runs the model
+ * over the whole block, takes every slot's most likely token and its
+ * probability with the mask logit at -inf, commits every still-masked slot
+ * that reaches the threshold (else the single most confident one), and the
+ * loop repeats until no slot is masked; committed slots stay as they are.
+ * The model here is the expert part of the stack only (pre-norm):
+ *   x = w_embed[tokens];  for each layer: x = bf16(x + MoE(RMSNorm(x)));
+ *   h = RMSNorm(x);  tokens = unmask(head(h))        (RMSNorm eps 1e-6, gamma 1)
+ * with MoE = bdm_moe_block_forward, the head and rule = bdm_lm_head_unmask
+ * with the fallback on.
+ *
+ * Arguments
+ *   tokens      [T] int32 device, in/out: the block (mask_id = masked slot)
+ *   w_embed     [V][H] bf16 device, row-major: embedding rows
+ *   layers      HOST array of L bdm_moe_layer (device pointers inside)
+ *   E, k, I, renorm   as in bdm_moe_block_forward, the same for every layer
+ *   w_head      [V][H] bf16 device: the untied head
+ *   weight_layout     layout of every expert matrix and of w_head
+ *   mask_id, threshold   as in bdm_lm_head_unmask
+ *   max_steps   steps at most (the loop also stops when no slot is masked)
+ *   steps_taken HOST int: steps run
+ *   commits     HOST [max_steps] int32 or NULL: slots committed per step
+ *   workspace   bdm_denoise_workspace_bytes(T, H, I, E, k, has_shared)
+ * Synchronous: after each step the host waits for the step on `stream` and
+ * reads two counters.  Errors as in bdm_moe_block_forward and
+ * bdm_lm_head_unmask; BDM_ERR_HIP if a step fails.
+ */
+BDM_API int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
+                              const bdm_moe_layer* layers, int L, int E, int k, int I,
+                              int renorm, const uint16_t* w_head, int weight_layout,
+                              int32_t mask_id, float threshold, int max_steps,
+                              int* steps_taken, int32_t* commits, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * bdm_head_workspace_bytes -- workspace size for bdm_lm_head_unmask.
  *   bytes: HOST pointer.  Pure host arithmetic.
  */

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
                            "bdm_moe_block_forward", "bdm_head_workspace_bytes",
                            "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
                            "bdm_pack_weights", "bdm_head_stat_parts", "bdm_lm_head_stats",
-                           "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset"])
+                           "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset",
+                           "bdm_denoise_workspace_bytes", "bdm_denoise_block"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -201,3 +202,41 @@ def test_coreset_validation(lib):
     assert call(block=0) == -1
     assert call(block=33) == -1
     assert call(T=2000) == -2
+
+
+def test_denoise_validation(lib):
+    from block_diffusion_moe_amd.binding import MoeLayerC
+    A = _fake(1 << 20)
+    lay = (MoeLayerC * 2)()
+    for i in range(2):
+        for f, _ in MoeLayerC._fields_:
+            setattr(lay[i], f, 1 << 20)
+        lay[i].router_bias = None
+    steps = ctypes.c_int(-1)
+    size = 1 << 30
+
+    def call(**kw):
+        a = dict(tokens=A, T=32, emb=A, V=248320, H=2048, layers=lay, L=2, E=256, k=8, I=512,
+                 renorm=1, head=A, layout=0, mask=151669, thr=0.95, steps=32)
+        a.update(kw)
+        return lib.bdm_denoise_block(a["tokens"], a["T"], a["emb"], a["V"], a["H"], a["layers"],
+                                     a["L"], a["E"], a["k"], a["I"], a["renorm"], a["head"],
+                                     a["layout"], a["mask"], a["thr"], a["steps"],
+                                     ctypes.byref(steps), None, A, size, None)
+    assert call(tokens=None) == -1
+    assert call(mask=248320) == -1
+    assert call(steps=-1) == -1
+    assert call(layout=2) == -1
+    assert call(thr=float("inf")) == -1
+    assert call(T=2000) == -2
+    assert call(H=2000) == -2
+    lay[1].ws_gate = None                       # shared trio broken in one layer
+    assert call() == -1
+    lay[1].ws_up = None
+    lay[1].ws_down = None                       # layers disagree on the shared expert
+    assert call() == -1
+    size_t = ctypes.c_size_t(0)
+    assert lib.bdm_denoise_workspace_bytes(32, 2048, 512, 256, 8, 1, ctypes.byref(size_t)) == 0
+    m = ctypes.c_size_t(0)
+    assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 1, ctypes.byref(m)) == 0
+    assert size_t.value > m.value

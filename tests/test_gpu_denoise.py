@@ -1,0 +1,148 @@
+"""GPU parity of the denoise loop (bdm_denoise_block) against oracle.denoise.
+
+Tiny model: every step of the GPU loop is checked against the oracle step on
+the GPU's own current tokens (teacher forcing; decisions exact away from a
+routing near tie, an argmax near tie, a threshold near call or a fallback
+near tie), and the whole loop equals those single steps bit for bit.  The
+40-layer Clover-shaped stack with the full head: the loop's invariants (at
+most T steps, at least one commit per step, committed slots unchanged,
+nothing masked at the end), and its first step equals the library's single
+calls composed by hand, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import denoise as oden
+from tests.conftest import gpu_available
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def bdm():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_diffusion_moe_amd as b
+    b.load()
+    return b
+
+
+def _layers(shape, seeds, device):
+    out = []
+    for sd in seeds:
+        wr, wg, wu, wd, sg, su, sdn, _ = synth.moe_weights(shape, sd, device)
+        out.append({"w_router": wr, "w_gate": wg, "w_up": wu, "w_down": wd, "ws_gate": sg,
+                    "ws_up": su, "ws_down": sdn})
+    return out
+
+
+def _host_layers(layers):
+    return [{"w_router": lw["w_router"].cpu().numpy(),
+             **{n: synth.bf16_bits(lw[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate",
+                                                     "ws_up", "ws_down")}} for lw in layers]
+
+
+def _embed(V, H, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(900 + seed)
+    return torch.randn((V, H), generator=g, device=device).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("threshold", [0.95, 0.0, 0.02])
+def test_denoise_tiny_teacher_forced(bdm, threshold):
+    say(f"case denoise tiny threshold={threshold}")
+    s = synth.MoEShape(T=8, H=64, E=16, I=32, k=2)
+    V, mask = 512, 0
+    layers = _layers(s, (11, 12, 13), DEV)
+    emb = _embed(V, s.H, 1, DEV)
+    w_head = synth.head_weights(synth.HeadShape(T=8, H=64, V=V, mask_id=mask), 5, device=DEV)
+    w_head = (w_head.float() * 30.0).to(torch.bfloat16)      # sharper rows: some commit
+    hl, eb, hb = _host_layers(layers), synth.bf16_bits(emb), synth.bf16_bits(w_head)
+    tok0 = torch.full((s.T,), mask, dtype=torch.int32, device=DEV)
+    tok0[2] = 7
+    cur = tok0.clone()
+    history = []
+    while (cur == mask).any():
+        before = cur.cpu().numpy().astype(np.int64)
+        steps, commits = bdm.bdm_denoise_block(cur, emb, layers, w_head, s.k, mask, threshold,
+                                               max_steps=1)
+        torch.cuda.synchronize()
+        after = cur.cpu().numpy().astype(np.int64)
+        o = oden.denoise_step(before, eb, hl, hb, s.k, mask, threshold)
+        assert steps == 1 and commits[0] >= 1
+        excl = o["near_route"] | o["near_tie"] | o["near_threshold"]
+        keep = ~excl
+        assert np.array_equal(after[before != mask], before[before != mask])
+        if not excl.any() and not o["fallback_tie"]:
+            assert np.array_equal(after, o["tokens"]), (after, o["tokens"])
+            assert commits[0] == o["n_committed"]
+        else:
+            assert np.array_equal(after[keep], o["tokens"][keep])
+        history.append(commits[0])
+        assert len(history) <= s.T
+    say(f"  commits per step {history}")
+    # the whole loop at once gives the same block, bit for bit
+    full = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(full, emb, layers, w_head, s.k, mask, threshold)
+    torch.cuda.synchronize()
+    assert commits == history and steps == len(history)
+    assert torch.equal(full, cur)
+    if threshold == 0.0:
+        assert history == [s.T - 1]
+
+
+def test_denoise_clover_stack_invariants_and_first_step(bdm):
+    """40 Clover-shaped layers, the 248,320-row head, packed weights."""
+    s = synth.LAYER
+    HS = synth.HEAD
+    say("case denoise 40-layer stack + head")
+    layers = _layers(s, range(100, 100 + synth.STACK_LAYERS), DEV)
+    pk = bdm.bdm_pack_weights
+    players = [{**{n: lw[n] for n in ("w_router",)},
+                **{n: pk(lw[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up",
+                                          "ws_down")}} for lw in layers]
+    del layers
+    torch.cuda.empty_cache()
+    emb = _embed(HS.V, s.H, 2, DEV)
+    w_head = pk(synth.head_weights(HS, 0, device=DEV))
+    torch.cuda.synchronize()
+    say("  weights ready")
+    tok0 = torch.full((s.T,), HS.mask_id, dtype=torch.int32, device=DEV)
+    tok0[[0, 9, 20]] = torch.tensor([11, 12, 13], dtype=torch.int32, device=DEV)
+    # first step by hand from the single calls
+    x = emb[tok0.long()].contiguous()
+    xn = torch.empty_like(x)
+    ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(s.T, s.H, s.I, s.E, s.k, True), DEV)
+    for lw in players:
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        bdm.bdm_moe_block_forward(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"],
+                                  s.k, ws_gate=lw["ws_gate"], ws_up=lw["ws_up"],
+                                  ws_down=lw["ws_down"], residual=x, y=x, ws=ws)
+    bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+    ref = tok0.clone()
+    nc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bdm.bdm_lm_head_unmask(xn, w_head, HS.mask_id, 0.95, True, ref, n_committed=nc)
+    one = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(one, emb, players, w_head, s.k, HS.mask_id, 0.95,
+                                           max_steps=1)
+    torch.cuda.synchronize()
+    assert steps == 1 and commits == [int(nc.item())]
+    assert torch.equal(one, ref)
+    # the whole loop
+    tok = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(tok, emb, players, w_head, s.k, HS.mask_id, 0.95)
+    torch.cuda.synchronize()
+    say(f"  {steps} steps, commits {commits}")
+    masked0 = int((tok0 == HS.mask_id).sum())
+    assert 1 <= steps <= masked0 and all(c >= 1 for c in commits) and sum(commits) == masked0
+    assert not (tok == HS.mask_id).any()
+    done = tok0 != HS.mask_id
+    assert torch.equal(tok[done], tok0[done])
+    assert int(tok.min()) >= 0 and int(tok.max()) < HS.V
+    del players, w_head, emb
+    torch.cuda.empty_cache()
