@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--cpu-blocks", type=int, default=4,
                    help="weight sets whose blocks the CPU oracle cycles over for cpu_baseline, "
                         "at least 10 s of oracle time (0: skip)")
+    p.add_argument("--stack-layers", type=int, default=40,
+                   help="layers of the denoise-loop stack measured beside the step (0: skip)")
     p.add_argument("--layout", type=int, default=1,
                    help="weight layout: 1 = packed MFMA tiles (packed once, untimed), 0 = row-major")
     return p.parse_args()
@@ -242,6 +244,10 @@ def main():
             "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_loop_us, 2),
             "launches_timed": args.steps, "us_per_launch_in_step": round(gemm_us, 2)}
 
+    stack = None
+    if args.stack_layers > 0:
+        stack = stack_step(bdm, synth, torch, np, dev, args, L, HS)
+
     cpu = None
     if args.cpu_blocks > 0:
         cpu = cpu_baseline(sets[:args.cpu_blocks])
@@ -279,6 +285,7 @@ def main():
         "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
+        "denoise_step_stack": stack,
         "rmsnorm_us": round(norm_us, 2),
         "ms_per_step_with_events": round(ms_step, 4),
         "wall_s_timed": round(wall, 3),
@@ -286,6 +293,74 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def stack_step(bdm, synth, torch, np, dev, args, L, HS):
+    """One denoise step of the loop driver over a stack of Clover-shaped
+    layers (bdm_denoise_block with max_steps 1: embedding, per layer RMSNorm +
+    MoE, final RMSNorm, head + unmask, and the per-step host read of the
+    counters) from the same initial block, repeated; bytes = every layer's
+    touched experts (this step's routing) + the head."""
+    nl = args.stack_layers
+    print(f"[bench] generating the {nl}-layer stack", file=sys.stderr, flush=True)
+    layers = []
+    for l in range(nl):
+        wr, wg, wu, wd, sg, su, sd, _ = synth.moe_weights(L, 100 + l, dev)
+        pk = bdm.bdm_pack_weights
+        layers.append({"w_router": wr, "w_gate": pk(wg), "w_up": pk(wu), "w_down": pk(wd),
+                       "ws_gate": pk(sg), "ws_up": pk(su), "ws_down": pk(sd)})
+        del wg, wu, wd, sg, su, sd
+    g = torch.Generator(device=dev)
+    g.manual_seed(902)
+    emb = torch.randn((HS.V, L.H), generator=g, device=dev).to(torch.bfloat16)
+    w_head = bdm.bdm_pack_weights(synth.head_weights(HS, 0, device=dev))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # a block late in its loop: 31 committed tokens (distinct seeded ids) and
+    # one masked slot, so the 32 rows differ (an all-masked block has 32
+    # identical rows and touches only k experts per layer)
+    gt = torch.Generator(device="cpu")
+    gt.manual_seed(903)
+    ids = torch.randperm(HS.V - 1, generator=gt)[:L.T]
+    ids = ids + (ids >= HS.mask_id).long()                  # never the mask id
+    tok0 = ids.to(torch.int32).to(dev)
+    tok0[L.T // 2] = HS.mask_id
+    # this step's routing per layer (untimed), for the bytes
+    x = emb[tok0.long()].contiguous()
+    xn = torch.empty_like(x)
+    idx = torch.empty((L.T, L.k), dtype=torch.int32, device=dev)
+    ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(L.T, L.H, L.I, L.E, L.k, True), dev)
+    touched = 0
+    for lw in layers:
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        bdm.bdm_moe_block_forward(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"],
+                                  L.k, ws_gate=lw["ws_gate"], ws_up=lw["ws_up"],
+                                  ws_down=lw["ws_down"], residual=x, y=x, topk_idx=idx, ws=ws)
+        torch.cuda.synchronize()
+        touched += int(torch.unique(idx).numel())
+    dws = bdm.workspace(bdm.bdm_denoise_workspace_bytes(L.T, L.H, L.I, L.E, L.k, True), dev)
+    tok = tok0.clone()
+    bdm.bdm_denoise_block(tok, emb, layers, w_head, L.k, HS.mask_id, 0.95, max_steps=1, ws=dws)
+    reps = 5
+    times = []
+    for _ in range(reps):
+        tok.copy_(tok0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        bdm.bdm_denoise_block(tok, emb, layers, w_head, L.k, HS.mask_id, 0.95, max_steps=1,
+                              ws=dws)
+        times.append(time.perf_counter() - t0)
+    ms = 1e3 * float(np.median(times))
+    nbytes = (touched + nl) * EXPERT_BYTES + HEAD_BYTES
+    out = {"layers": nl, "ms": round(ms, 3), "block_tokens_per_s": round(L.T / (ms * 1e-3), 1),
+           "touched_experts_all_layers": touched, "bytes": int(nbytes),
+           "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "block": "31 committed tokens (distinct seeded ids) + 1 masked slot",
+           "timing": f"host wall clock of bdm_denoise_block(max_steps=1), median of {reps}"}
+    del layers, emb, w_head
+    torch.cuda.empty_cache()
+    return out
 
 
 def head_traffic():
