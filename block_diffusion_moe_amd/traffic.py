@@ -24,8 +24,9 @@ factor is reported for comparison only.
     python -m block_diffusion_moe_amd.traffic mfma --dir DIR --out FILE [--command TEXT]
         per-kernel matrix-core activity from one counter pass of
         SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16
-        and GRBM_GUI_ACTIVE: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
-        (GRBM_GUI_ACTIVE x CUs x 4 SIMDs).
+        and GRBM_GUI_ACTIVE: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over
+        every SIMD) / (GRBM_GUI_ACTIVE / XCDs (it is summed over the XCDs) x
+        CUs x 4 SIMDs); MFMA flop per launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.
 """
 from __future__ import annotations
 
@@ -155,20 +156,24 @@ def mfma(a):
     out = ["# Matrix-core (MFMA) activity per kernel (rocprofv3 counters)", ""]
     if a.command:
         out += ["Made by:", "", "```", a.command, "```", ""]
-    out += [f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {a.cus} CUs x 4 SIMDs); "
-            "means per dispatch.", "",
+    out += [f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {a.xcds} XCDs x {a.cus} "
+            "CUs x 4 SIMDs) (both counters are sums over the chip: the busy cycles over every "
+            "SIMD, GUI_ACTIVE over the XCDs); MFMA flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.  "
+            "Means per dispatch.", "",
             "| kernel | dispatches | GRBM_GUI_ACTIVE | SQ_BUSY_CYCLES | SQ_VALU_MFMA_BUSY_CYCLES "
-            "| SQ_INSTS_VALU_MFMA_MOPS_BF16 | MFMA busy |",
-            "|---|---:|---:|---:|---:|---:|---:|"]
+            "| SQ_INSTS_VALU_MFMA_MOPS_BF16 | MFMA flop | MFMA busy |",
+            "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for n in names:
         v = {c: agg.get((n, c), []) for c in MFMA_COUNTERS}
         if not all(v.values()):
             continue
         m = {c: sum(x) / len(x) for c, x in v.items()}
-        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, m["GRBM_GUI_ACTIVE"] * a.cus * 4)
+        cycles = m["GRBM_GUI_ACTIVE"] / a.xcds
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, cycles * a.cus * 4)
         out.append(f"| `{n}` | {len(v['GRBM_GUI_ACTIVE'])} | {m['GRBM_GUI_ACTIVE']:.4g} | "
                    f"{m['SQ_BUSY_CYCLES']:.4g} | {m['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | "
-                   f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} | {100 * busy:.2f}% |")
+                   f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} | "
+                   f"{512 * m['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} | {100 * busy:.2f}% |")
     out.append("")
     with open(a.out, "w") as fh:
         fh.write("\n".join(out))
@@ -187,6 +192,7 @@ def main(argv=None):
     m.add_argument("--dir", required=True)
     m.add_argument("--out", required=True)
     m.add_argument("--cus", type=int, default=256)
+    m.add_argument("--xcds", type=int, default=8)
     m.add_argument("--command", default="")
     a = p.parse_args(argv)
     if a.cmd == "copy":
