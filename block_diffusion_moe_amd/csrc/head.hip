@@ -239,6 +239,115 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   }
 }
 
+// Cooperative variant for H % 256 == 0 (KSW = H / 256 k-steps per wave):
+// the 8 waves of a workgroup stream every 16-row group together, wave w the
+// k-steps [w*KSW, (w+1)*KSW), with that slice of the hidden rows held in its
+// registers for the whole run.  The 8 partial products of a group meet in
+// LDS and are summed in wave order, and each (token, column) of the group is
+// folded into the online-softmax state of one lane (token 4w + lane/16,
+// column lane%16).  The workgroup takes one contiguous run of groups; its
+// waves move in step (one barrier per group), and the loads of the next two
+// groups are in flight while a group is reduced.  Loads past the run read
+// the hidden rows instead (valid, L2-resident, ignored), so no load sits
+// behind a branch.
+template <int KSW>
+__global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
+    const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
+    int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
+    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride) {
+  static_assert(kHeadWaves == 8 && kHeadTokChunk == 32, "one token row of 4 per wave");
+  __shared__ float part[2][kHeadWaves][2][4][kWave];          // 32 KB
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const long ngroups = (V + 15) / 16;
+  const long G0 = static_cast<long>(blockIdx.x) * ngroups / gridDim.x;
+  const long G1 = static_cast<long>(blockIdx.x + 1) * ngroups / gridDim.x;
+  const int n = static_cast<int>(G1 - G0);
+  const int s0 = wave * KSW;
+
+  // weight fragments of group gi (n <= gi: the hidden rows, never used)
+  auto wfrag = [&](long gi) -> FragPtr {
+    if (gi >= G1) return FragPtr{h + c * 8, 0};
+    if (layout == BDM_LAYOUT_MFMA_TILES) return frag_ptr(w, gi * 16, H, lane, layout);
+    long v = gi * 16 + c;
+    v = v < V ? v : V - 1;
+    return FragPtr{w + v * H + g * 8, 32};
+  };
+  auto load = [&](long gi, u32x4(&b)[KSW]) {
+    const FragPtr f = wfrag(gi);
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) b[s] = ld16_stream(f.p + (s0 + s) * f.step);
+  };
+  u32x4 ba[KSW], bb[KSW];
+  load(G0, ba);
+  load(G0 + 1, bb);
+  // this wave's slice of the hidden rows (rows >= ntok are zero)
+  u32x4 a0[KSW], a1[KSW];
+  {
+    const bool ok0 = c < ntok, ok1 = 16 + c < ntok;
+    const uint16_t* r0 = h + static_cast<size_t>(tok0 + (ok0 ? c : 0)) * H + g * 8;
+    const uint16_t* r1 = h + static_cast<size_t>(tok0 + (ok1 ? 16 + c : 0)) * H + g * 8;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      const u32x4 x0 = ld16(r0 + (s0 + s) * 32);
+      const u32x4 x1 = ld16(r1 + (s0 + s) * 32);
+      a0[s] = ok0 ? x0 : u32x4{0u, 0u, 0u, 0u};
+      a1[s] = ok1 ? x1 : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // the (token, column) this lane folds: token ot, column c
+  const int ot = 4 * wave + g;
+  const int omt = ot >> 4, oq = (ot >> 2) & 3, oi = ot & 3;
+  SoftStat st = softstat_empty();
+
+  auto step = [&](int j, u32x4(&b)[KSW]) {
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      acc0 = mfma_bf16(a0[s], b[s], acc0);
+      acc1 = mfma_bf16(a1[s], b[s], acc1);
+    }
+    load(G0 + j + 2, b);
+    float* pp = &part[j & 1][wave][0][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pp[(0 * 4 + i) * kWave + lane] = acc0[i];
+      pp[(1 * 4 + i) * kWave + lane] = acc1[i];
+    }
+    __syncthreads();
+    float l = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kHeadWaves; ++wv) l += part[j & 1][wv][omt][oi][16 * oq + c];
+    const int v = static_cast<int>((G0 + j) * 16) + c;
+    if (!(v < V && v + voff != mask_id)) l = -INFINITY;
+    const float nm = fmaxf(st.m, l);
+    const float sc = (st.m == nm) ? 1.0f : expf(st.m - nm);
+    const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
+    st.a = (l > st.m) ? v + voff : st.a;
+    st.s = st.s * sc + add;
+    st.m = nm;
+  };
+  int j = 0;
+  for (; j + 1 < n; j += 2) {
+    step(j, ba);
+    step(j + 1, bb);
+  }
+  if (j < n) step(j, ba);
+
+  // the 16 columns of a token sit in one DPP row; each token in one wave
+  const SoftStat r = row_merge_stat(st);
+  if (c == 0 && ot < ntok) {
+    const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
+    pm[o] = r.m;
+    ps[o] = r.s;
+    pa[o] = r.a;
+  }
+}
+
 // One workgroup.  16 threads (one DPP row) per token merge that token's
 // partials (all loads issued first), the row reduction finishes the merge,
 // and one wave applies the commit rule over the block.
@@ -328,11 +437,25 @@ static HeadKernel head_kernel_for(int H) {
   return kHeadKernels[(u == kHeadU ? 0 : 2) + (even ? 0 : 1)];
 }
 
+static HeadKernel coop_kernel_for(int H) {
+  switch (H / 256) {
+    case 1: return &head_coop_kernel<1>;
+    case 2: return &head_coop_kernel<2>;
+    case 4: return &head_coop_kernel<4>;
+    case 8: return &head_coop_kernel<8>;
+    default: return nullptr;
+  }
+}
+
 void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V, int voff,
                        int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
                        int pstride, int grid, hipStream_t s) {
-  const size_t lds = head_lds_bytes(H);
-  auto kern = head_kernel_for(H);
+#ifndef BDM_HEAD_COOP
+#define BDM_HEAD_COOP 1
+#endif
+  HeadKernel coop = (BDM_HEAD_COOP && H % 256 == 0) ? coop_kernel_for(H) : nullptr;
+  const size_t lds = coop ? 0 : head_lds_bytes(H);
+  HeadKernel kern = coop ? coop : head_kernel_for(H);
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
     kern<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,

@@ -45,7 +45,10 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
 
 // Head: partial softmax statistics per (token, vocabulary tile).
 constexpr int kHeadTokChunk = 32;    // tokens per head pass
-constexpr int kHeadWaves = 8;        // waves per head workgroup
+#ifndef BDM_HEAD_WAVES
+#define BDM_HEAD_WAVES 8
+#endif
+constexpr int kHeadWaves = BDM_HEAD_WAVES;   // waves per head workgroup
 
 struct HeadParts {
   int grid;     // head workgroups (one per CU)
