@@ -37,7 +37,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0
-PMC_SUMMARY = os.path.join(HERE, "profiles", "head_tile_kernel_clover_head.traffic.md")
+PMC_SUMMARY = os.path.join(HERE, "profiles", "head_coop_kernel_clover_head.traffic.md")
 EXPERT_BYTES = 3 * 2048 * 512 * 2        # gate + up + down, bf16
 HEAD_BYTES = 248320 * 2048 * 2
 
@@ -238,7 +238,7 @@ def main():
     value = T / (ms_step_plain * 1e-3)
 
     gemm_gbs = HEAD_BYTES / (gemm_loop_us * 1e-6) / 1e9
-    roof = {"bound": "hbm", "kernel": "head_tile_kernel (bdm_lm_head_stats)",
+    roof = {"bound": "hbm", "kernel": "head_coop_kernel (bdm_lm_head_stats)",
             "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": head_traffic(),
             "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_loop_us, 2),
@@ -364,7 +364,7 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
 
 
 def head_traffic():
-    """HBM bytes per head_tile_kernel launch from the committed counter summary
+    """HBM bytes per head GEMM launch from the committed counter summary
     (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing or
     was taken on other kernel sources."""
     try:

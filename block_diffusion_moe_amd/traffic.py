@@ -40,7 +40,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-HEAD_KERNEL = "head_tile_kernel"
+HEAD_KERNELS = ("head_coop_kernel", "head_tile_kernel")   # the head GEMM (either variant)
 HEAD_SOURCES = ("head.hip", "device.hpp", "internal.hpp")
 
 
@@ -124,7 +124,7 @@ def summarize(a):
         fb = f_fac * 1024.0 * sum(fv) / len(fv)
         wb = w_fac * 1024.0 * sum(wv) / len(wv)
         rows.append((n, len(fv), fb, wb))
-        if n.split("::")[-1].startswith(HEAD_KERNEL):
+        if n.split("::")[-1].startswith(HEAD_KERNELS):
             head_bytes = fb + wb if head_bytes is None else max(head_bytes, fb + wb)
     out = [f"<!-- source_sha256 = {kernel_source_digest()} -->"]
     if head_bytes is not None:
