@@ -146,8 +146,9 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
                 int E, int k, int renorm, float top_p, int block, const uint16_t* w_gate,
                 const uint16_t* w_up, const uint16_t* w_down, int I, const uint16_t* ws_gate,
                 const uint16_t* ws_up, const uint16_t* ws_down, int weight_layout,
-                const uint16_t* residual, uint16_t* y, int32_t* topk_idx, float* topk_w,
-                int32_t* n_kept, void* workspace, size_t workspace_bytes, void* stream) {
+                const uint16_t* residual, uint16_t* y, uint16_t* y_norm, int32_t* topk_idx,
+                float* topk_w, int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                void* stream) {
   if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
     return BDM_ERR_INVALID_ARG;
   const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
@@ -160,10 +161,15 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
   if (st != BDM_OK) return st;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
       !aligned16(w_down) || !aligned16(y) || (residual && !aligned16(residual)) ||
+      (y_norm && !aligned16(y_norm)) ||
       (has_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down))) ||
       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return BDM_ERR_INVALID_ARG;
   if (static_cast<const void*>(x) == static_cast<const void*>(y)) return BDM_ERR_INVALID_ARG;
+  if (y_norm && (static_cast<const void*>(y_norm) == static_cast<const void*>(y) ||
+                 static_cast<const void*>(y_norm) == static_cast<const void*>(x) ||
+                 static_cast<const void*>(y_norm) == static_cast<const void*>(residual)))
+    return BDM_ERR_INVALID_ARG;
   const size_t need = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
   if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
 
@@ -177,7 +183,7 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
   bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, top_p, block,
                      meta, topk_idx, topk_w, n_kept, s);
   bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
-                      ws_down, residual, y, meta, weight_layout, s);
+                      ws_down, residual, y, y_norm, meta, weight_layout, s);
   return last_hip_status();
 }
 
@@ -188,11 +194,11 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int I, const uint16_t* ws_gate, const uint16_t* ws_up,
                           const uint16_t* ws_down, int weight_layout, const uint16_t* residual,
-                          uint16_t* y, int32_t* topk_idx, float* topk_w, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          uint16_t* y, uint16_t* y_norm, int32_t* topk_idx, float* topk_w,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
-                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, topk_idx, topk_w,
-                     nullptr, workspace, workspace_bytes, stream);
+                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, topk_idx,
+                     topk_w, nullptr, workspace, workspace_bytes, stream);
 }
 
 int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* w_router,
@@ -201,13 +207,13 @@ int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* 
                                   const uint16_t* w_up, const uint16_t* w_down, int I,
                                   const uint16_t* ws_gate, const uint16_t* ws_up,
                                   const uint16_t* ws_down, int weight_layout,
-                                  const uint16_t* residual, uint16_t* y, int32_t* topk_idx,
-                                  float* topk_w, int32_t* n_kept, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
+                                  int32_t* topk_idx, float* topk_w, int32_t* n_kept,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
   if (block_tokens < 1 || block_tokens > BDM_CORESET_MAX_BLOCK) return BDM_ERR_INVALID_ARG;
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, top_p, block_tokens, w_gate,
-                     w_up, w_down, I, ws_gate, ws_up, ws_down, weight_layout, residual, y,
+                     w_up, w_down, I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm,
                      topk_idx, topk_w, n_kept, workspace, workspace_bytes, stream);
 }
 
@@ -389,15 +395,16 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
   *steps_taken = 0;
   while (steps < max_steps) {
     bdm::launch_embed(tokens, T, w_embed, V, H, x, s);
+    bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
+    // each layer's combine also writes RMSNorm of its output: the next
+    // layer's input, after the last layer the final norm
     for (int l = 0; l < L; ++l) {
       const bdm_moe_layer& w = layers[l];
-      bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
       bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared, 0.0f, 0,
                          meta, nullptr, nullptr, nullptr, s);
       bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
-                          w.ws_up, w.ws_down, x, x, meta, weight_layout, s);
+                          w.ws_up, w.ws_down, x, x, xn, meta, weight_layout, s);
     }
-    bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
     bdm::launch_head_stats(xn, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s,
                            parts.a, parts.grid, parts.grid, s);
     bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,

@@ -197,4 +197,21 @@ __device__ __forceinline__ SoftStat row_merge_stat(SoftStat v) {
   return v;
 }
 
+// RMSNorm scale of one row held as 8 consecutive fp32 values per thread
+// (thread i: elements 8i .. 8i+7; threads past the row hold zeros) in a
+// 256-thread workgroup: 1 / sqrt(mean(x^2) + eps), summed in a fixed order
+// (per thread, DPP within the wave, then the 4 waves pairwise).  `part`: 4
+// floats of LDS.  Every thread of the workgroup must call it.
+__device__ __forceinline__ float row_rms_scale(const float (&v)[8], float eps, int H,
+                                               float* part) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x % kWave) == 0) part[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  return 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+}
+
 }  // namespace bdm

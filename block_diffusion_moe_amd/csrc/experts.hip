@@ -236,12 +236,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int k, int has_shared,
                                                       const int32_t* __restrict__ topk_idx,
                                                       const float* __restrict__ topk_w,
-                                                      const uint16_t* residual, uint16_t* y) {
+                                                      const uint16_t* residual, uint16_t* y,
+                                                      uint16_t* y_norm) {
+  __shared__ float part[4];
   const int t = blockIdx.x;
   const int h0 = threadIdx.x * 8;
-  if (h0 >= H) return;
+  const bool on = h0 < H;
+  if (!on && !y_norm) return;
   const int K1 = k + 1;
-  const float* yrow = ypair + static_cast<size_t>(t) * K1 * H + h0;
+  const float* yrow = ypair + static_cast<size_t>(t) * K1 * H + (on ? h0 : 0);
   // every row load first (a slot the block coreset selector left empty, id
   // -1, has a row in the workspace that is loaded and then ignored)
   float4 v[BDM_MAX_TOPK + 1][2];
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   float acc[8];
   if (residual) {
-    const u32x4 r = ld16(residual + static_cast<size_t>(t) * H + h0);
+    const u32x4 r = ld16(residual + static_cast<size_t>(t) * H + (on ? h0 : 0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] = __uint_as_float(r[i] << 16);
@@ -286,14 +289,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int i = 0; i < 4; ++i)
     o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
            (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
-  *reinterpret_cast<u32x4*>(y + static_cast<size_t>(t) * H + h0) = o;
+  if (!on) o = u32x4{0u, 0u, 0u, 0u};
+  if (y_norm) {
+    // the next layer's RMSNorm of this row (eps 1e-6, unit gamma), the same
+    // arithmetic as the RMSNorm kernel on the stored bf16 values
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(o[j] << 16);
+      v[2 * j + 1] = __uint_as_float(o[j] & 0xffff0000u);
+    }
+    const float r = row_rms_scale(v, 1e-6f, H, part);
+    if (on) {
+      u32x4 q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j] * r)) |
+               (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1] * r)) << 16);
+      *reinterpret_cast<u32x4*>(y_norm + static_cast<size_t>(t) * H + h0) = q;
+    }
+  }
+  if (on) *reinterpret_cast<u32x4*>(y + static_cast<size_t>(t) * H + h0) = o;
 }
 
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int layout,
-                    hipStream_t s) {
+                    const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
+                    const MoeMeta& meta, int layout, hipStream_t s) {
   // upper bound on touched groups; workgroups past the actual list exit at once
   const int groups = (T * k < E ? T * k : E) + (has_shared ? 1 : 0);
   const int P = T * (k + 1);
@@ -320,7 +343,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                                              meta.pair_rows, meta.ypair);
   }
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
-                                   residual, y);
+                                   residual, y, y_norm);
 }
 
 }  // namespace bdm

@@ -40,8 +40,8 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
-                    const uint16_t* residual, uint16_t* y, const MoeMeta& meta, int layout,
-                    hipStream_t s);
+                    const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
+                    const MoeMeta& meta, int layout, hipStream_t s);
 
 // Head: partial softmax statistics per (token, vocabulary tile).
 constexpr int kHeadTokChunk = 32;    // tokens per head pass

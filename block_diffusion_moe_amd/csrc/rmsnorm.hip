@@ -20,14 +20,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, const f
     v[2 * j] = __uint_as_float(raw[j] << 16);
     v[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
   }
-  float ss = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
-  ss = wave_sum(ss);
-  if ((threadIdx.x % kWave) == 0) part[threadIdx.x / kWave] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  const float r = row_rms_scale(v, eps, H, part);
   if (!on) return;
   u32x4 o;
 #pragma unroll

@@ -135,6 +135,10 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *                and ws_down as [H][I] (the router stays fp32 row-major)
  *   residual     [T][H] bf16 or NULL; may be the same pointer as y
  *   y            [T][H] bf16        output
+ *   y_norm       [T][H] bf16 or NULL: also receives RMSNorm(y) (eps 1e-6,
+ *                unit gamma; bit for bit what bdm_rmsnorm gives on y), the
+ *                next layer's input in a pre-norm stack; must not alias x, y
+ *                or residual
  *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
  *   topk_w       [T][k] fp32 or NULL    receives w_t
  *   workspace, workspace_bytes: see bdm_moe_workspace_bytes
@@ -150,7 +154,7 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           int I,
                           const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                           int weight_layout,
-                          const uint16_t* residual, uint16_t* y,
+                          const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
                           int32_t* topk_idx, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream);
 
@@ -195,7 +199,7 @@ BDM_API int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H,
                           int I,
                           const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                           int weight_layout,
-                          const uint16_t* residual, uint16_t* y,
+                          const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
                           int32_t* topk_idx, float* topk_w, int32_t* n_kept,
                           void* workspace, size_t workspace_bytes, void* stream);
 

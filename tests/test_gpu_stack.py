@@ -63,16 +63,21 @@ def test_stack_40_layers_teacher_forced(bdm):
     wts = torch.empty((s.T, s.k), dtype=torch.float32, device=DEV)
     ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(s.T, s.H, s.I, s.E, s.k, True), DEV)
     rec = []
-    for inp, W in layers:
+    fused = torch.empty_like(x)
+    bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+    for l, (inp, W) in enumerate(layers):
         x_in = x.clone()
-        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
         xn_in = xn.clone()
+        # the layer also writes RMSNorm of its output (the next layer's input)
         bdm.bdm_moe_block_forward(xn, inp.w_router, W[0], W[1], W[2], s.k, ws_gate=W[3],
                                   ws_up=W[4], ws_down=W[5], residual=x, y=x, topk_idx=idx,
-                                  topk_w=wts, ws=ws)
+                                  topk_w=wts, ws=ws, y_norm=fused)
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.view(torch.int16), xn.view(torch.int16)), f"layer {l} y_norm"
         rec.append((x_in, xn_in, x.clone(), idx.clone(), wts.clone()))
     torch.cuda.synchronize()
-    say("  stack ran on the GPU")
+    say("  stack ran on the GPU (fused RMSNorm == bdm_rmsnorm bit for bit at every layer)")
     final = synth.bf16_bits(x).astype(np.float64)
     assert np.all(np.isfinite(final))
     tokens = np.sort(np.random.default_rng(4).choice(s.T, 4, replace=False))
