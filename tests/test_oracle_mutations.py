@@ -10,6 +10,7 @@ import pytest
 
 import oracle.coreset as C
 import oracle.denoise as D
+import oracle.verify as VF
 import oracle.head as H
 import oracle.moe as M
 import oracle.norm as N
@@ -139,7 +140,22 @@ def _loop_one_step(orig):
     return lambda *a, **kw: orig(*a, **dict(kw, max_steps=1))
 
 
+def _bound_max(entropy, ratio=0.9, delta=0.6):
+    return np.maximum(ratio, delta * np.exp(-np.asarray(entropy, dtype=np.float64)))
+
+
+def _bound_plus_h(entropy, ratio=0.9, delta=0.6):
+    return np.minimum(ratio, delta * np.exp(np.asarray(entropy, dtype=np.float64)))
+
+
+def _count_all(accept):
+    return int(np.sum(accept))
+
+
 MUTANTS = {
+    "verify_bound_max": (VF, "bound", lambda o: _bound_max),
+    "verify_bound_sign": (VF, "bound", lambda o: _bound_plus_h),
+    "verify_counts_every_accept": (VF, "accept_prefix", lambda o: _count_all),
     "denoise_no_final_norm": (D, "denoise_step", lambda o: _step_no_final_norm),
     "denoise_stops_after_one_step": (D, "denoise_block", _loop_one_step),
     "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
@@ -183,6 +199,9 @@ PINS = [
     P.test_denoise_loop_terminates_commits_and_never_revisits,
     P.test_denoise_step_is_its_parts_composed,
     P.test_denoise_confident_block_finishes_in_one_step,
+    P.test_verify_bound_matches_page_points,
+    P.test_verify_entropy_and_probabilities_closed_form,
+    P.test_verify_threshold_decision_and_prefix,
 ]
 
 

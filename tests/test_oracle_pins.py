@@ -582,3 +582,72 @@ def test_denoise_confident_block_finishes_in_one_step():
     assert commits == [6] and not (final == 3).any()
     final, commits = denoise.denoise_block(tokens, emb, layers, wh, 2, 3, 1.5)
     assert commits == [1] * 6
+
+
+# --------------------------------------------------------------------------
+# Self-speculative verify epilogue (files page, "Two ways to run it")
+# --------------------------------------------------------------------------
+
+def test_verify_bound_matches_page_points():
+    """The page's prose: with the defaults the ratio never binds; the bound is
+    0.6 for a certain model (H = 0) and 0.22 at one nat."""
+    from oracle import verify
+    assert verify.bound(0.0) == pytest.approx(0.6)
+    assert verify.bound(1.0) == pytest.approx(0.2207, abs=5e-5)
+    assert np.all(verify.bound(np.linspace(0, 10, 101)) <= 0.6)
+    # a larger delta lets the ratio bind at low entropy
+    assert verify.bound(0.0, delta=3.0) == pytest.approx(0.9)
+    assert verify.bound(2.0, delta=3.0) == pytest.approx(3.0 * math.exp(-2.0))
+
+
+def _rows_with_logits(rows, H=32):
+    """bf16 hidden rows e_0 .. and an identity-like head so that the logits of
+    row t are exactly rows[t] (vocabulary = H)."""
+    V = H
+    w = np.zeros((V, H), dtype=np.float64)
+    w[np.arange(V), np.arange(V)] = 1.0
+    h = np.zeros((len(rows), H), dtype=np.float64)
+    for t, r in enumerate(rows):
+        h[t, :len(r)] = r
+    return bf16.from_f64(h), bf16.from_f64(w)
+
+
+def test_verify_entropy_and_probabilities_closed_form():
+    """Logits with n equal maxima and the rest at -30 (bf16-exact): H = ln n,
+    p = 1/n, so at the defaults p >= 0.6/n is always accepted (the page's
+    remark that a lenient bound accepts nearly everything); one dominant
+    logit gives H ~ 0 and the bound 0.6."""
+    from oracle import verify
+    rows = [[2.0] * n + [-30.0] * (32 - n) for n in (1, 2, 4, 8)] + [[0.0] * 32]
+    hb, wb = _rows_with_logits(rows)
+    cand = [0, 1, 3, 7]
+    o = verify.verify(hb, wb, cand, "threshold")
+    np.testing.assert_allclose(o["entropy"][:4], np.log([1, 2, 4, 8]), atol=1e-9)
+    np.testing.assert_allclose(o["p_cand"], [1, 1 / 2, 1 / 4, 1 / 8], rtol=1e-9)
+    assert o["n_accepted"] == 4 and o["tokens"][4] == 0      # bonus: argmax of the last row
+    # exact rule: only the argmax (lowest id among equal maxima) is kept
+    e = verify.verify(hb, wb, cand, "exact")
+    assert list(e["accept"]) == [True, False, False, False] and e["n_accepted"] == 1
+    assert list(e["tokens"][:2]) == [0, 0] and np.all(e["tokens"][2:] == -1)
+
+
+def test_verify_threshold_decision_and_prefix():
+    """Two-outcome rows with p = sigmoid(d) for the candidate: accepted iff
+    p >= 0.6 e^-H(p); a rejection hides every later acceptance."""
+    from oracle import verify
+
+    def row(d):
+        return [d, 0.0] + [-60.0] * 30
+
+    def rule(p):
+        H = -(p * math.log(p) + (1 - p) * math.log(1 - p))
+        return p >= 0.6 * math.exp(-H)
+    ds = [4.0, 2.0, 0.0, -1.0, -2.0]
+    hb, wb = _rows_with_logits([row(d) for d in ds] + [row(3.0)])
+    o = verify.verify(hb, wb, [0] * 5, "threshold")
+    ps = [1 / (1 + math.exp(-d)) for d in ds]
+    np.testing.assert_allclose(o["p_cand"], ps, rtol=1e-6)
+    assert list(o["accept"]) == [rule(p) for p in ps]
+    r = verify.accept_prefix(o["accept"])
+    assert o["n_accepted"] == r and r < 5
+    assert list(o["tokens"][:r]) == [0] * r and o["tokens"][r] == o["argmax"][r]
