@@ -642,12 +642,13 @@ def test_verify_threshold_decision_and_prefix():
     def rule(p):
         H = -(p * math.log(p) + (1 - p) * math.log(1 - p))
         return p >= 0.6 * math.exp(-H)
-    ds = [4.0, 2.0, 0.0, -1.0, -2.0]
+    ds = [4.0, 2.0, -1.0, 0.0, 4.0]             # accepted, accepted, rejected, accepted, accepted
     hb, wb = _rows_with_logits([row(d) for d in ds] + [row(3.0)])
     o = verify.verify(hb, wb, [0] * 5, "threshold")
     ps = [1 / (1 + math.exp(-d)) for d in ds]
     np.testing.assert_allclose(o["p_cand"], ps, rtol=1e-6)
-    assert list(o["accept"]) == [rule(p) for p in ps]
-    r = verify.accept_prefix(o["accept"])
-    assert o["n_accepted"] == r and r < 5
-    assert list(o["tokens"][:r]) == [0] * r and o["tokens"][r] == o["argmax"][r]
+    assert [rule(p) for p in ps] == [True, True, False, True, True]
+    assert list(o["accept"]) == [True, True, False, True, True]
+    assert o["n_accepted"] == 2
+    # the boundary token: row 2's most likely token (column 1: d = -1 < 0)
+    assert list(o["tokens"]) == [0, 0, 1, -1, -1, -1]
