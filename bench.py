@@ -231,6 +231,27 @@ def main():
     kept_mean = float(np.mean([kept[i % args.sets] for i in range(args.steps)]))
     cs_bytes = (kept_mean + 1) * EXPERT_BYTES
 
+    # the self-speculative verify epilogue over the same head: 32 candidates +
+    # the boundary row, threshold rule (0.9, 0.6), back to back like the GEMM
+    hv = [torch.cat([xo[r], xo[r][:1]]).contiguous() for r in range(args.sets)]
+    cv = [tokens[r].clone() for r in range(args.sets)]
+    vws = bdm.workspace(bdm.bdm_head_verify_workspace_bytes(T + 1, H, HS.V), dev)
+    vtok = torch.empty((T + 1,), dtype=torch.int32, device=dev)
+    vna = torch.empty((1,), dtype=torch.int32, device=dev)
+    for r in range(args.sets):
+        bdm.bdm_lm_head_verify(hv[r], heads[r], cv[r], "threshold", 0.9, 0.6, tokens_out=vtok,
+                               n_accepted=vna, ws=vws)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        r = i % args.sets
+        bdm.bdm_lm_head_verify(hv[r], heads[r], cv[r], "threshold", 0.9, 0.6, tokens_out=vtok,
+                               n_accepted=vna, ws=vws)
+    stop.record()
+    torch.cuda.synchronize()
+    verify_us = start.elapsed_time(stop) * 1e3 / args.steps
+    verify_gbs = HEAD_BYTES / (verify_us * 1e-6) / 1e9
+
     u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
     moe_bytes = (u_mean + 1) * EXPERT_BYTES
     moe_gbs = moe_bytes / (moe_loop_us * 1e-6) / 1e9
@@ -285,6 +306,9 @@ def main():
         "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
+        "head_verify_33_rows": {"us": round(verify_us, 2), "bytes": HEAD_BYTES,
+                                "GB_s": round(verify_gbs, 1),
+                                "frac_of_peak": round(verify_gbs / PEAK_HBM_GBS, 4)},
         "denoise_step_stack": stack,
         "rmsnorm_us": round(norm_us, 2),
         "ms_per_step_with_events": round(ms_step, 4),

@@ -44,6 +44,11 @@ _SIGS = {
                                    _vp]),
     "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
                                     _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_head_verify_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int,
+                                                 ctypes.POINTER(_c_size)]),
+    "bdm_lm_head_verify": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_int,
+                                    _c_float, _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _c_size, _vp]),
     "bdm_head_stat_parts": (_c_int, [ctypes.POINTER(_c_int)]),
     "bdm_lm_head_stats": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                                    ctypes.c_int32, _vp, _vp, _vp, _c_int, _vp]),
@@ -334,6 +339,54 @@ def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool
                                    _stream(stream))
     _raise("bdm_lm_head_unmask", st)
     return tokens
+
+
+BDM_VERIFY_EXACT = 0
+BDM_VERIFY_THRESHOLD = 1
+_VERIFY_RULES = {"exact": BDM_VERIFY_EXACT, "threshold": BDM_VERIFY_THRESHOLD}
+
+
+def bdm_head_verify_workspace_bytes(T1, H, V) -> int:
+    n = _c_size()
+    _raise("bdm_head_verify_workspace_bytes",
+           load().bdm_head_verify_workspace_bytes(T1, H, V, ctypes.byref(n)))
+    return n.value
+
+
+def bdm_lm_head_verify(h, w_head, cand, rule: str = "threshold", ratio: float = 0.9,
+                       delta: float = 0.6, tokens_out=None, n_accepted=None, accept=None,
+                       argmax=None, p_cand=None, entropy=None, ws=None, stream=None):
+    """Verify epilogue over T1 = len(cand) + 1 causal hidden rows.  Returns
+    (tokens_out [T1] int32, n_accepted [1] int32), both device tensors."""
+    T1, H = h.shape
+    V = w_head.shape[0]
+    dev = h.device
+    if rule not in _VERIFY_RULES:
+        raise ValueError(f"rule must be one of {sorted(_VERIFY_RULES)}")
+    _check(h, "h", torch.bfloat16, (T1, H))
+    _check(w_head, "w_head", torch.bfloat16, (V, H), dev)
+    _check(cand, "cand", torch.int32, (T1 - 1,), dev)
+    if tokens_out is None:
+        tokens_out = torch.empty(T1, dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(tokens_out, "tokens_out", torch.int32, (T1,), dev)
+    _check(n_accepted, "n_accepted", torch.int32, (1,), dev)
+    _check(accept, "accept", torch.int32, (T1 - 1,), dev)
+    _check(argmax, "argmax", torch.int32, (T1,), dev)
+    _check(p_cand, "p_cand", torch.float32, (T1 - 1,), dev)
+    _check(entropy, "entropy", torch.float32, (T1,), dev)
+    need = bdm_head_verify_workspace_bytes(T1, H, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    layout = BDM_LAYOUT_MFMA_TILES if isinstance(w_head, Packed) else BDM_LAYOUT_ROW_MAJOR
+    st = load().bdm_lm_head_verify(_ptr(h), T1, H, _ptr(w_head), V, layout,
+                                   _ptr(cand) if T1 > 1 else None, _VERIFY_RULES[rule],
+                                   float(ratio), float(delta), _ptr(tokens_out),
+                                   _ptr(n_accepted), _ptr(accept), _ptr(argmax), _ptr(p_cand),
+                                   _ptr(entropy), _ptr(ws), ws.numel(), _stream(stream))
+    _raise("bdm_lm_head_verify", st)
+    return tokens_out, n_accepted
 
 
 def bdm_head_stat_parts() -> int:

@@ -89,6 +89,46 @@ size_t head_layout(int T, char* base, bdm::HeadParts* p) {
   return off;
 }
 
+// Verify epilogue partials: (m, s, a) as the head's plus q and lc.
+struct VerifyParts {
+  float* m;
+  float* s;
+  int32_t* a;
+  float* q;
+  float* lc;
+};
+
+size_t verify_layout(int T1, char* base, VerifyParts* p) {
+  const size_t n = static_cast<size_t>(T1) * kHeadMaxGrid;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  char* m = take(sizeof(float) * n);
+  char* s = take(sizeof(float) * n);
+  char* a = take(sizeof(int32_t) * n);
+  char* q = take(sizeof(float) * n);
+  char* lc = take(sizeof(float) * n);
+  if (p) {
+    p->m = reinterpret_cast<float*>(m);
+    p->s = reinterpret_cast<float*>(s);
+    p->a = reinterpret_cast<int32_t*>(a);
+    p->q = reinterpret_cast<float*>(q);
+    p->lc = reinterpret_cast<float*>(lc);
+  }
+  return off;
+}
+
+int check_verify_shape(int T1, int H, int V) {
+  if (T1 < 1 || H < 1 || V < 2) return BDM_ERR_INVALID_ARG;
+  if (T1 > BDM_MAX_TOKENS || H % 64 != 0) return BDM_ERR_UNSUPPORTED_SHAPE;
+  const int ks = H / 256;
+  if (H % 256 != 0 || (ks != 1 && ks != 2 && ks != 4 && ks != 8)) return BDM_ERR_UNSUPPORTED_SHAPE;
+  return BDM_OK;
+}
+
 // Per-device cache: compute-unit count and one-time kernel set-up.  Filled on
 // the first call made with that device current; -1 marks a failed set-up.
 constexpr int kMaxDevices = 64;
@@ -255,6 +295,48 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
                          parts.grid, parts.grid, s);
   bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
                      fallback, tokens, argmax, conf, n_committed, nullptr, s);
+  return last_hip_status();
+}
+
+int bdm_head_verify_workspace_bytes(int T1, int H, int V, size_t* bytes) {
+  if (!bytes) return BDM_ERR_INVALID_ARG;
+  const int st = check_verify_shape(T1, H, V);
+  if (st != BDM_OK) return st;
+  *bytes = verify_layout(T1, nullptr, nullptr);
+  return BDM_OK;
+}
+
+int bdm_lm_head_verify(const uint16_t* h, int T1, int H, const uint16_t* w_head, int V,
+                       int weight_layout, const int32_t* cand, int rule, float ratio, float delta,
+                       int32_t* tokens_out, int32_t* n_accepted, int32_t* accept, int32_t* argmax,
+                       float* p_cand, float* entropy, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!h || !w_head || !tokens_out || !n_accepted || !workspace) return BDM_ERR_INVALID_ARG;
+  if (T1 > 1 && !cand) return BDM_ERR_INVALID_ARG;
+  int st = check_verify_shape(T1, H, V);
+  if (st != BDM_OK) return st;
+  if (rule != BDM_VERIFY_EXACT && rule != BDM_VERIFY_THRESHOLD) return BDM_ERR_INVALID_ARG;
+  if (!(ratio == ratio) || !(delta == delta) || ratio == INFINITY || delta == INFINITY ||
+      ratio == -INFINITY || delta == -INFINITY)
+    return BDM_ERR_INVALID_ARG;
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+    return BDM_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w_head) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return BDM_ERR_INVALID_ARG;
+  const size_t need = verify_layout(T1, nullptr, nullptr);
+  if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
+  int cus = 0;
+  st = device_setup(&cus);
+  if (st != BDM_OK) return st;
+  VerifyParts p;
+  verify_layout(T1, static_cast<char*>(workspace), &p);
+  const int grid = cus < kHeadMaxGrid ? cus : kHeadMaxGrid;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  bdm::launch_head_verify_stats(h, T1, H, w_head, V, weight_layout, cand, T1 - 1, p.m, p.s, p.a,
+                                p.q, p.lc, grid, grid, s);
+  bdm::launch_verify_merge(p.m, p.s, p.a, p.q, p.lc, T1, grid, grid, cand, V, rule, ratio, delta,
+                           tokens_out, n_accepted, accept, argmax, p_cand, entropy, s);
   return last_hip_status();
 }
 

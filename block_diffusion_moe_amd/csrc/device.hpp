@@ -197,6 +197,64 @@ __device__ __forceinline__ SoftStat row_merge_stat(SoftStat v) {
   return v;
 }
 
+// Online statistics of a logit row for the verify epilogue: max m, s = sum
+// exp(l - m), q = sum exp(l - m) (l - m) (entropy = log s - q / s), argmax a
+// (lowest index on ties) and the candidate's logit lc (-inf until seen).
+struct VStat {
+  float m;
+  float s;
+  float q;
+  int a;
+  float lc;
+};
+
+__device__ __forceinline__ VStat vstat_empty() { return {-INFINITY, 0.0f, 0.0f, INT32_MAX, -INFINITY}; }
+
+// Associative merge (deterministic for a fixed merge tree).  A side with
+// m = -inf holds no element and contributes nothing.
+__device__ __forceinline__ VStat vstat_merge(VStat x, VStat y) {
+  VStat r;
+  r.m = fmaxf(x.m, y.m);
+  r.lc = fmaxf(x.lc, y.lc);
+  if (r.m == -INFINITY) {
+    r.s = 0.0f;
+    r.q = 0.0f;
+    r.a = min(x.a, y.a);
+    return r;
+  }
+  float s = 0.0f, q = 0.0f;
+  if (x.m != -INFINITY) {
+    const float d = x.m - r.m, e = expf(d);
+    s += x.s * e;
+    q += e * (x.q + d * x.s);
+  }
+  if (y.m != -INFINITY) {
+    const float d = y.m - r.m, e = expf(d);
+    s += y.s * e;
+    q += e * (y.q + d * y.s);
+  }
+  r.s = s;
+  r.q = q;
+  if (x.m > y.m) r.a = x.a;
+  else if (y.m > x.m) r.a = y.a;
+  else r.a = min(x.a, y.a);
+  return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ VStat dpp_vstat(VStat v) {
+  return {dpp_f<CTRL>(v.m), dpp_f<CTRL>(v.s), dpp_f<CTRL>(v.q), dpp_i<CTRL>(v.a),
+          dpp_f<CTRL>(v.lc)};
+}
+
+__device__ __forceinline__ VStat row_merge_vstat(VStat v) {
+  v = vstat_merge(v, dpp_vstat<kDppXor1>(v));
+  v = vstat_merge(v, dpp_vstat<kDppXor2>(v));
+  v = vstat_merge(v, dpp_vstat<kDppHalfMirror>(v));
+  v = vstat_merge(v, dpp_vstat<kDppMirror>(v));
+  return v;
+}
+
 // RMSNorm scale of one row held as 8 consecutive fp32 values per thread
 // (thread i: elements 8i .. 8i+7; threads past the row hold zeros) in a
 // 256-thread workgroup: 1 / sqrt(mean(x^2) + eps), summed in a fixed order

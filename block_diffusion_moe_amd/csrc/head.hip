@@ -250,11 +250,13 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 // groups are in flight while a group is reduced.  Loads past the run read
 // the hidden rows instead (valid, L2-resident, ignored), so no load sits
 // behind a branch.
-template <int KSW>
+template <int KSW, bool VERIFY>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
     int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
-    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride) {
+    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride,
+    const int32_t* __restrict__ cand, int ncand, float* __restrict__ pq,
+    float* __restrict__ plc) {
   static_assert(kHeadWaves == 8 && kHeadTokChunk == 32, "one token row of 4 per wave");
   __shared__ float part[2][kHeadWaves][2][4][kWave];          // 32 KB
 
@@ -303,6 +305,10 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   const int ot = 4 * wave + g;
   const int omt = ot >> 4, oq = (ot >> 2) & 3, oi = ot & 3;
   SoftStat st = softstat_empty();
+  VStat vs = vstat_empty();
+  // VERIFY: the candidate token of this lane's row (-1: none)
+  int mycand = -1;
+  if (VERIFY) mycand = (tok0 + ot < ncand && ot < ntok) ? cand[tok0 + ot] : -1;
 
   auto step = [&](int j, u32x4(&b)[KSW]) {
     f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -324,12 +330,28 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     for (int wv = 0; wv < kHeadWaves; ++wv) l += part[j & 1][wv][omt][oi][16 * oq + c];
     const int v = static_cast<int>((G0 + j) * 16) + c;
     if (!(v < V && v + voff != mask_id)) l = -INFINITY;
-    const float nm = fmaxf(st.m, l);
-    const float sc = (st.m == nm) ? 1.0f : expf(st.m - nm);
-    const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
-    st.a = (l > st.m) ? v + voff : st.a;
-    st.s = st.s * sc + add;
-    st.m = nm;
+    if constexpr (VERIFY) {
+      // q += exp(l - m)(l - m) under the same rescaling as s
+      const float nm = fmaxf(vs.m, l);
+      if (nm != -INFINITY) {
+        const float d = vs.m - nm;                     // <= 0; -inf while empty
+        const float sc = (vs.m == -INFINITY) ? 0.0f : expf(d);
+        const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
+        vs.q = (vs.m == -INFINITY ? 0.0f : sc * (vs.q + d * vs.s)) +
+               (l == -INFINITY ? 0.0f : add * (l - nm));
+        vs.s = vs.s * sc + add;
+        vs.a = (l > vs.m) ? v + voff : vs.a;
+        vs.m = nm;
+      }
+      if (v + voff == mycand) vs.lc = l;
+    } else {
+      const float nm = fmaxf(st.m, l);
+      const float sc = (st.m == nm) ? 1.0f : expf(st.m - nm);
+      const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
+      st.a = (l > st.m) ? v + voff : st.a;
+      st.s = st.s * sc + add;
+      st.m = nm;
+    }
   };
   int j = 0;
   for (; j + 1 < n; j += 2) {
@@ -339,12 +361,24 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   if (j < n) step(j, ba);
 
   // the 16 columns of a token sit in one DPP row; each token in one wave
-  const SoftStat r = row_merge_stat(st);
-  if (c == 0 && ot < ntok) {
-    const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
-    pm[o] = r.m;
-    ps[o] = r.s;
-    pa[o] = r.a;
+  if constexpr (VERIFY) {
+    const VStat r = row_merge_vstat(vs);
+    if (c == 0 && ot < ntok) {
+      const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
+      pm[o] = r.m;
+      ps[o] = r.s;
+      pa[o] = r.a;
+      pq[o] = r.q;
+      plc[o] = r.lc;
+    }
+  } else {
+    const SoftStat r = row_merge_stat(st);
+    if (c == 0 && ot < ntok) {
+      const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
+      pm[o] = r.m;
+      ps[o] = r.s;
+      pa[o] = r.a;
+    }
   }
 }
 
@@ -423,6 +457,81 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   if (lane == 0 && n_left) *n_left = nmasked - ncommit;
 }
 
+// Verify epilogue ([files] "Two ways to run it"), one workgroup: merge the
+// statistics of each of the T1 rows (16 threads per row, fixed tree), then
+// accept_t (t < T1 - 1) by the rule, r = the accepted prefix, and the
+// round's tokens: candidates 0..r-1, the most likely token of row r, -1 after.
+//   rule 0 (exact):     cand_t == argmax_t
+//   rule 1 (threshold): p_t(cand_t) >= min(ratio, delta * exp(-H_t)),
+//                       p = exp(lc - m) / s, H = log s - q / s
+__global__ __launch_bounds__(1024) void verify_merge_kernel(
+    const float* __restrict__ pm, const float* __restrict__ ps, const int32_t* __restrict__ pa,
+    const float* __restrict__ pq, const float* __restrict__ plc, int T1, int nparts, int pstride,
+    const int32_t* __restrict__ cand, int V, int rule, float ratio, float delta,
+    int32_t* __restrict__ tokens_out, int32_t* __restrict__ n_accepted,
+    int32_t* __restrict__ accept_out, int32_t* __restrict__ argmax_out,
+    float* __restrict__ pcand_out, float* __restrict__ entropy_out) {
+  extern __shared__ int vsm[];
+  int* sacc = vsm;                 // [T1]
+  int* sarg = vsm + T1;            // [T1]
+  const int tid = threadIdx.x;
+  const int sub = tid & 15;
+  for (int t0 = 0; t0 < T1; t0 += blockDim.x >> 4) {
+    const int t = t0 + (tid >> 4);
+    const bool on = t < T1;          // row-uniform
+    const size_t base = static_cast<size_t>(on ? t : 0) * pstride;
+    VStat st = vstat_empty();
+    for (int i = sub; i < nparts; i += 16) {
+      if (on) st = vstat_merge(st, VStat{pm[base + i], ps[base + i], pq[base + i], pa[base + i],
+                                         plc[base + i]});
+    }
+    st = row_merge_vstat(st);
+    if (on && sub == 0) {
+      const float ent = logf(st.s) - st.q / st.s;
+      const float pc = expf(st.lc - st.m) / st.s;
+      int acc = 0;
+      if (t < T1 - 1) {
+        const int c = cand[t];
+        acc = (c < 0 || c >= V) ? 0
+              : (rule == 0)     ? (c == st.a ? 1 : 0)
+                                : (pc >= fminf(ratio, delta * expf(-ent)) ? 1 : 0);
+        if (accept_out) accept_out[t] = acc;
+        if (pcand_out) pcand_out[t] = pc;
+      }
+      sacc[t] = acc;
+      sarg[t] = st.a;
+      if (argmax_out) argmax_out[t] = st.a;
+      if (entropy_out) entropy_out[t] = ent;
+    }
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  // the accepted prefix: the first rejected row (row T1-1 never accepts)
+  const int lane = tid;
+  int first = T1 - 1;
+  for (int t0 = 0; t0 < T1; t0 += kWave) {
+    const int t = t0 + lane;
+    const unsigned long long rej = __ballot(t < T1 && !sacc[t]);
+    if (rej) {
+      first = t0 + __builtin_ctzll(rej);
+      break;
+    }
+  }
+  for (int t = lane; t < T1; t += kWave)
+    tokens_out[t] = t < first ? cand[t] : (t == first ? sarg[t] : -1);
+  if (lane == 0) *n_accepted = first;
+}
+
+void launch_verify_merge(const float* pm, const float* ps, const int32_t* pa, const float* pq,
+                         const float* plc, int T1, int parts, int pstride, const int32_t* cand,
+                         int V, int rule, float ratio, float delta, int32_t* tokens_out,
+                         int32_t* n_accepted, int32_t* accept_out, int32_t* argmax_out,
+                         float* pcand_out, float* entropy_out, hipStream_t s) {
+  verify_merge_kernel<<<1, 1024, static_cast<size_t>(T1) * 8, s>>>(
+      pm, ps, pa, pq, plc, T1, parts, pstride, cand, V, rule, ratio, delta, tokens_out, n_accepted,
+      accept_out, argmax_out, pcand_out, entropy_out);
+}
+
 // the k-batch must divide H/32 (always even), else batches of 2 k-steps
 using HeadKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int, int32_t, int, int,
                             float*, float*, int32_t*, int);
@@ -437,12 +546,17 @@ static HeadKernel head_kernel_for(int H) {
   return kHeadKernels[(u == kHeadU ? 0 : 2) + (even ? 0 : 1)];
 }
 
-static HeadKernel coop_kernel_for(int H) {
+using CoopKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int, int32_t, int,
+                            int, float*, float*, int32_t*, int, const int32_t*, int, float*,
+                            float*);
+
+template <bool VERIFY>
+static CoopKernel coop_kernel_for(int H) {
   switch (H / 256) {
-    case 1: return &head_coop_kernel<1>;
-    case 2: return &head_coop_kernel<2>;
-    case 4: return &head_coop_kernel<4>;
-    case 8: return &head_coop_kernel<8>;
+    case 1: return &head_coop_kernel<1, VERIFY>;
+    case 2: return &head_coop_kernel<2, VERIFY>;
+    case 4: return &head_coop_kernel<4, VERIFY>;
+    case 8: return &head_coop_kernel<8, VERIFY>;
     default: return nullptr;
   }
 }
@@ -453,13 +567,29 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
 #ifndef BDM_HEAD_COOP
 #define BDM_HEAD_COOP 1
 #endif
-  HeadKernel coop = (BDM_HEAD_COOP && H % 256 == 0) ? coop_kernel_for(H) : nullptr;
+  CoopKernel coop = (BDM_HEAD_COOP && H % 256 == 0) ? coop_kernel_for<false>(H) : nullptr;
+  HeadKernel tile = head_kernel_for(H);
   const size_t lds = coop ? 0 : head_lds_bytes(H);
-  HeadKernel kern = coop ? coop : head_kernel_for(H);
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
-    kern<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
-                                            pstride);
+    if (coop)
+      coop<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
+                                            pstride, nullptr, 0, nullptr, nullptr);
+    else
+      tile<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps,
+                                              pa, pstride);
+  }
+}
+
+void launch_head_verify_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V,
+                              int layout, const int32_t* cand, int ncand, float* pm, float* ps,
+                              int32_t* pa, float* pq, float* plc, int pstride, int grid,
+                              hipStream_t s) {
+  CoopKernel k = coop_kernel_for<true>(H);
+  for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
+    const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
+    k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, 0, layout, -1, t0, n, pm, ps, pa, pstride,
+                                       cand, ncand, pq, plc);
   }
 }
 

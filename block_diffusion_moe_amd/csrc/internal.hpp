@@ -74,6 +74,18 @@ void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, i
 void launch_embed(const int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
                   uint16_t* x, hipStream_t s);
 
+// the verify epilogue: statistics with the entropy term and the candidates'
+// logits (H % 256 == 0), then the merge and the accept rule
+void launch_head_verify_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V,
+                              int layout, const int32_t* cand, int ncand, float* pm, float* ps,
+                              int32_t* pa, float* pq, float* plc, int pstride, int grid,
+                              hipStream_t s);
+void launch_verify_merge(const float* pm, const float* ps, const int32_t* pa, const float* pq,
+                         const float* plc, int T1, int parts, int pstride, const int32_t* cand,
+                         int V, int rule, float ratio, float delta, int32_t* tokens_out,
+                         int32_t* n_accepted, int32_t* accept_out, int32_t* argmax_out,
+                         float* pcand_out, float* entropy_out, hipStream_t s);
+
 void launch_pack(const uint16_t* src, long R, int K, uint16_t* dst, hipStream_t s);
 
 void launch_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H,

@@ -347,6 +347,55 @@ BDM_API int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum,
                                   int32_t* n_committed, void* stream);
 
 /*
+ * bdm_lm_head_verify -- the verify epilogue of self-speculative decoding
+ * ([files] "Two ways to run it"): the diffusion pass proposed T = T1 - 1
+ * candidate tokens; the same model run causally over them gave T1 final
+ * hidden states (row t predicts position t, row T the position after the
+ * last candidate).  This call streams the head once over all T1 rows and
+ * keeps the longest accepted prefix of candidates plus one new token:
+ *
+ *   l_t      = fp32 logits h_t . w_head^T over all V rows (never stored;
+ *              no row is excluded: the causal pass has no mask token)
+ *   p_t      = softmax(l_t); argmax_t = argmax_v l_t (equal: lowest id)
+ *   H_t      = -sum_v p_t,v log p_t,v (nats)
+ *   accept_t (t < T):
+ *     rule BDM_VERIFY_EXACT:     cand[t] == argmax_t
+ *     rule BDM_VERIFY_THRESHOLD: p_t(cand[t]) >= min(ratio, delta * exp(-H_t))
+ *                                (the page gives ratio 0.9, delta 0.6)
+ *   r        = number of leading accepted candidates (0 <= r <= T)
+ *   tokens_out[0..r-1] = cand[0..r-1]; tokens_out[r] = argmax_r;
+ *   tokens_out[r+1..T] = -1; *n_accepted = r  (r + 1 tokens this round)
+ *
+ * Arguments
+ *   h            [T1][H] bf16     causal-pass final hidden states
+ *   w_head       [V][H] bf16      head, row-major or packed (weight_layout)
+ *   cand         [T1-1] int32     DEVICE candidates (NULL allowed when T1 == 1);
+ *                                 an id outside [0, V) is never accepted
+ *   rule         BDM_VERIFY_EXACT or BDM_VERIFY_THRESHOLD
+ *   ratio, delta finite bound parameters (used by the threshold rule)
+ *   tokens_out   [T1] int32 DEVICE; n_accepted: DEVICE int32*
+ *   accept       [T1-1] int32 or NULL  (1 accepted, 0 rejected, every t)
+ *   argmax       [T1] int32 or NULL
+ *   p_cand       [T1-1] fp32 or NULL   p_t(cand[t]) (0 for an id outside [0, V))
+ *   entropy      [T1] fp32 or NULL     H_t
+ * Workspace: bdm_head_verify_workspace_bytes(T1, H, V).  Limits: 1 <= T1 <=
+ * 1024, H in {256, 512, 1024, 2048}, V >= 2.  All outputs are written on the
+ * stream; nothing is read back to the host.
+ */
+#define BDM_VERIFY_EXACT      0
+#define BDM_VERIFY_THRESHOLD  1
+#define BDM_VERIFY_RATIO_DEFAULT 0.9f
+#define BDM_VERIFY_DELTA_DEFAULT 0.6f
+
+BDM_API int bdm_head_verify_workspace_bytes(int T1, int H, int V, size_t* bytes);
+
+BDM_API int bdm_lm_head_verify(const uint16_t* h, int T1, int H, const uint16_t* w_head, int V,
+                               int weight_layout, const int32_t* cand, int rule, float ratio,
+                               float delta, int32_t* tokens_out, int32_t* n_accepted,
+                               int32_t* accept, int32_t* argmax, float* p_cand, float* entropy,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bdm_packed_weight_elems -- size of the packed copy of a [rows][cols] bf16
  * matrix: ceil(rows/16)*16*cols elements (rows padded to a multiple of 16).
  *   n: HOST pointer.  cols must be a multiple of 32.  Pure host arithmetic.

@@ -26,6 +26,10 @@ candidate):
    c_0 .. c_{r-1} and then a_r (the most likely token at the boundary: the
    greedy reading of the new token).
 
+Parity of the bound's formula is pinned only at what the page fixes (its two
+points and the ratio's role); the rest of the formula is the reading above:
+parity partly unpinned.
+
 Pins (tests/test_oracle_pins.py): the page's two points of the bound (0.6 at
 H = 0, 0.6/e = 0.2207 at H = 1 nat), constructed distributions of known
 entropy, the ratio binding only when delta e^-H exceeds it, a uniform

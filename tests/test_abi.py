@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
                            "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
                            "bdm_pack_weights", "bdm_head_stat_parts", "bdm_lm_head_stats",
                            "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset",
-                           "bdm_denoise_workspace_bytes", "bdm_denoise_block"])
+                           "bdm_denoise_workspace_bytes", "bdm_denoise_block",
+                           "bdm_head_verify_workspace_bytes", "bdm_lm_head_verify"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -245,3 +246,35 @@ def test_denoise_validation(lib):
     m = ctypes.c_size_t(0)
     assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 1, ctypes.byref(m)) == 0
     assert size_t.value > m.value
+
+
+def test_verify_validation(lib):
+    A = _fake(1 << 20)
+
+    def call(**kw):
+        a = dict(h=A, T1=33, H=2048, w=A, V=248320, lay=0, cand=A, rule=1, ratio=0.9,
+                 delta=0.6, tok=A, na=A, ws=A, wsb=1 << 30)
+        a.update(kw)
+        return lib.bdm_lm_head_verify(a["h"], a["T1"], a["H"], a["w"], a["V"], a["lay"],
+                                      a["cand"], a["rule"], a["ratio"], a["delta"], a["tok"],
+                                      a["na"], None, None, None, None, a["ws"], a["wsb"], None)
+    assert call(h=None) == -1
+    assert call(tok=None) == -1
+    assert call(na=None) == -1
+    assert call(cand=None) == -1
+    assert call(rule=2) == -1
+    assert call(ratio=float("nan")) == -1
+    assert call(delta=float("inf")) == -1
+    assert call(lay=3) == -1
+    assert call(T1=0) == -1
+    assert call(V=1) == -1
+    assert call(T1=1025) == -2
+    assert call(H=2112) == -2          # multiple of 64, not of 256
+    assert call(H=768) == -2           # multiple of 256 outside {256, 512, 1024, 2048}
+    assert call(wsb=16) == -3
+    n = ctypes.c_size_t(0)
+    assert lib.bdm_head_verify_workspace_bytes(33, 2048, 248320, ctypes.byref(n)) == 0
+    h = ctypes.c_size_t(0)
+    assert lib.bdm_head_workspace_bytes(33, 2048, 248320, ctypes.byref(h)) == 0
+    assert n.value > h.value
+    assert lib.bdm_head_verify_workspace_bytes(33, 768, 248320, ctypes.byref(n)) == -2

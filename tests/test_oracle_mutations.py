@@ -152,10 +152,29 @@ def _count_all(accept):
     return int(np.sum(accept))
 
 
+def _stats_bits(l32):
+    l = np.asarray(l32, dtype=np.float64)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(p > 0, p * np.log2(p), 0.0)
+    return np.argmax(l, axis=1).astype(np.int64), p, -plogp.sum(axis=1)
+
+
+def _verify_bonus_last_row(orig):
+    def f(*a, **kw):
+        o = orig(*a, **kw)
+        o["tokens"][o["n_accepted"]] = o["argmax"][-1]
+        return o
+    return f
+
+
 MUTANTS = {
     "verify_bound_max": (VF, "bound", lambda o: _bound_max),
     "verify_bound_sign": (VF, "bound", lambda o: _bound_plus_h),
     "verify_counts_every_accept": (VF, "accept_prefix", lambda o: _count_all),
+    "verify_entropy_in_bits": (VF, "stats", lambda o: _stats_bits),
+    "verify_bonus_from_last_row": (VF, "verify", _verify_bonus_last_row),
     "denoise_no_final_norm": (D, "denoise_step", lambda o: _step_no_final_norm),
     "denoise_stops_after_one_step": (D, "denoise_block", _loop_one_step),
     "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
