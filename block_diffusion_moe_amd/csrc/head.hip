@@ -241,24 +241,29 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 
 // Cooperative variant for H % 256 == 0 (KSW = H / 256 k-steps per wave):
 // the 8 waves of a workgroup stream every 16-row group together, wave w the
-// k-steps [w*KSW, (w+1)*KSW), with that slice of the hidden rows held in its
+// k-steps [w*KSW, (w+1)*KSW), with that slice of the hidden rows (MT tiles
+// of 16 rows: 32 or 64 rows per pass over the weights) held in its
 // registers for the whole run.  The 8 partial products of a group meet in
 // LDS and are summed in wave order, and each (token, column) of the group is
-// folded into the online-softmax state of one lane (token 4w + lane/16,
-// column lane%16).  The workgroup takes one contiguous run of groups; its
-// waves move in step (one barrier per group), and the loads of the next two
-// groups are in flight while a group is reduced.  Loads past the run read
-// the hidden rows instead (valid, L2-resident, ignored), so no load sits
-// behind a branch.
-template <int KSW, bool VERIFY>
+// folded into the online-softmax state of one lane (tokens 32f + 4w +
+// lane/16 for f < MT/2, column lane%16).  The workgroup takes one contiguous
+// run of groups; its waves move in step (one barrier per group), and the
+// loads of the next two groups are in flight while a group is reduced.
+// Loads past the run read the hidden rows instead (valid, L2-resident,
+// ignored), so no load sits behind a branch.
+//
+// VERIFY (the verify epilogue): no row is masked and the state is a VStat
+// (adds q = sum e^(l-m)(l-m) and the logit of the row's candidate cand[t]).
+template <int KSW, int MT, bool VERIFY>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
     int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
     float* __restrict__ ps, int32_t* __restrict__ pa, int pstride,
     const int32_t* __restrict__ cand, int ncand, float* __restrict__ pq,
     float* __restrict__ plc) {
-  static_assert(kHeadWaves == 8 && kHeadTokChunk == 32, "one token row of 4 per wave");
-  __shared__ float part[2][kHeadWaves][2][4][kWave];          // 32 KB
+  static_assert(kHeadWaves == 8 && (MT == 2 || MT == 4), "4 token rows of a tile per wave");
+  constexpr int NF = MT / 2;                                   // tokens folded per lane
+  __shared__ float part[2][kHeadWaves][MT][4][kWave];          // 16 KB per tile
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -288,69 +293,79 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   load(G0, ba);
   load(G0 + 1, bb);
   // this wave's slice of the hidden rows (rows >= ntok are zero)
-  u32x4 a0[KSW], a1[KSW];
-  {
-    const bool ok0 = c < ntok, ok1 = 16 + c < ntok;
-    const uint16_t* r0 = h + static_cast<size_t>(tok0 + (ok0 ? c : 0)) * H + g * 8;
-    const uint16_t* r1 = h + static_cast<size_t>(tok0 + (ok1 ? 16 + c : 0)) * H + g * 8;
+  u32x4 a[MT][KSW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const bool ok = 16 * mt + c < ntok;
+    const uint16_t* r = h + static_cast<size_t>(tok0 + (ok ? 16 * mt + c : 0)) * H + g * 8;
 #pragma unroll
     for (int s = 0; s < KSW; ++s) {
-      const u32x4 x0 = ld16(r0 + (s0 + s) * 32);
-      const u32x4 x1 = ld16(r1 + (s0 + s) * 32);
-      a0[s] = ok0 ? x0 : u32x4{0u, 0u, 0u, 0u};
-      a1[s] = ok1 ? x1 : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x = ld16(r + (s0 + s) * 32);
+      a[mt][s] = ok ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // the (token, column) this lane folds: token ot, column c
-  const int ot = 4 * wave + g;
-  const int omt = ot >> 4, oq = (ot >> 2) & 3, oi = ot & 3;
-  SoftStat st = softstat_empty();
-  VStat vs = vstat_empty();
-  // VERIFY: the candidate token of this lane's row (-1: none)
-  int mycand = -1;
-  if (VERIFY) mycand = (tok0 + ot < ncand && ot < ntok) ? cand[tok0 + ot] : -1;
+  // the (token, column) pairs this lane folds: tokens ot[f], column c
+  SoftStat st[NF];
+  VStat vs[NF];
+  int mycand[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int ot = 32 * f + 4 * wave + g;
+    st[f] = softstat_empty();
+    vs[f] = vstat_empty();
+    mycand[f] = -1;
+    if (VERIFY) mycand[f] = (tok0 + ot < ncand && ot < ntok) ? cand[tok0 + ot] : -1;
+  }
 
   auto step = [&](int j, u32x4(&b)[KSW]) {
-    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    f32x4 acc[MT];
 #pragma unroll
-    for (int s = 0; s < KSW; ++s) {
-      acc0 = mfma_bf16(a0[s], b[s], acc0);
-      acc1 = mfma_bf16(a1[s], b[s], acc1);
-    }
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSW; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
     load(G0 + j + 2, b);
     float* pp = &part[j & 1][wave][0][0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pp[(0 * 4 + i) * kWave + lane] = acc0[i];
-      pp[(1 * 4 + i) * kWave + lane] = acc1[i];
-    }
-    __syncthreads();
-    float l = 0.0f;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int wv = 0; wv < kHeadWaves; ++wv) l += part[j & 1][wv][omt][oi][16 * oq + c];
+      for (int i = 0; i < 4; ++i) pp[(mt * 4 + i) * kWave + lane] = acc[mt][i];
+    __syncthreads();
     const int v = static_cast<int>((G0 + j) * 16) + c;
-    if (!(v < V && v + voff != mask_id)) l = -INFINITY;
-    if constexpr (VERIFY) {
-      // q += exp(l - m)(l - m) under the same rescaling as s
-      const float nm = fmaxf(vs.m, l);
-      if (nm != -INFINITY) {
-        const float d = vs.m - nm;                     // <= 0; -inf while empty
-        const float sc = (vs.m == -INFINITY) ? 0.0f : expf(d);
+    const bool live = v < V && v + voff != mask_id;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int ot = 32 * f + 4 * wave + g;
+      const int omt = ot >> 4, oq = (ot >> 2) & 3, oi = ot & 3;
+      float l = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kHeadWaves; ++wv) l += part[j & 1][wv][omt][oi][16 * oq + c];
+      if (!live) l = -INFINITY;
+      if constexpr (VERIFY) {
+        // q += exp(l - m)(l - m) under the same rescaling as s
+        VStat& x = vs[f];
+        const float nm = fmaxf(x.m, l);
+        if (nm != -INFINITY) {
+          const float d = x.m - nm;                     // <= 0; -inf while empty
+          const float sc = (x.m == -INFINITY) ? 0.0f : expf(d);
+          const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
+          x.q = (x.m == -INFINITY ? 0.0f : sc * (x.q + d * x.s)) +
+                (l == -INFINITY ? 0.0f : add * (l - nm));
+          x.s = x.s * sc + add;
+          x.a = (l > x.m) ? v + voff : x.a;
+          x.m = nm;
+        }
+        if (v + voff == mycand[f]) x.lc = l;
+      } else {
+        SoftStat& x = st[f];
+        const float nm = fmaxf(x.m, l);
+        const float sc = (x.m == nm) ? 1.0f : expf(x.m - nm);
         const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
-        vs.q = (vs.m == -INFINITY ? 0.0f : sc * (vs.q + d * vs.s)) +
-               (l == -INFINITY ? 0.0f : add * (l - nm));
-        vs.s = vs.s * sc + add;
-        vs.a = (l > vs.m) ? v + voff : vs.a;
-        vs.m = nm;
+        x.a = (l > x.m) ? v + voff : x.a;
+        x.s = x.s * sc + add;
+        x.m = nm;
       }
-      if (v + voff == mycand) vs.lc = l;
-    } else {
-      const float nm = fmaxf(st.m, l);
-      const float sc = (st.m == nm) ? 1.0f : expf(st.m - nm);
-      const float add = (l == -INFINITY) ? 0.0f : expf(l - nm);
-      st.a = (l > st.m) ? v + voff : st.a;
-      st.s = st.s * sc + add;
-      st.m = nm;
     }
   };
   int j = 0;
@@ -361,23 +376,26 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   if (j < n) step(j, ba);
 
   // the 16 columns of a token sit in one DPP row; each token in one wave
-  if constexpr (VERIFY) {
-    const VStat r = row_merge_vstat(vs);
-    if (c == 0 && ot < ntok) {
-      const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
-      pm[o] = r.m;
-      ps[o] = r.s;
-      pa[o] = r.a;
-      pq[o] = r.q;
-      plc[o] = r.lc;
-    }
-  } else {
-    const SoftStat r = row_merge_stat(st);
-    if (c == 0 && ot < ntok) {
-      const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
-      pm[o] = r.m;
-      ps[o] = r.s;
-      pa[o] = r.a;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int ot = 32 * f + 4 * wave + g;
+    const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
+    if constexpr (VERIFY) {
+      const VStat r = row_merge_vstat(vs[f]);
+      if (c == 0 && ot < ntok) {
+        pm[o] = r.m;
+        ps[o] = r.s;
+        pa[o] = r.a;
+        pq[o] = r.q;
+        plc[o] = r.lc;
+      }
+    } else {
+      const SoftStat r = row_merge_stat(st[f]);
+      if (c == 0 && ot < ntok) {
+        pm[o] = r.m;
+        ps[o] = r.s;
+        pa[o] = r.a;
+      }
     }
   }
 }
@@ -481,9 +499,17 @@ __global__ __launch_bounds__(1024) void verify_merge_kernel(
     const bool on = t < T1;          // row-uniform
     const size_t base = static_cast<size_t>(on ? t : 0) * pstride;
     VStat st = vstat_empty();
-    for (int i = sub; i < nparts; i += 16) {
-      if (on) st = vstat_merge(st, VStat{pm[base + i], ps[base + i], pq[base + i], pa[base + i],
-                                         plc[base + i]});
+    for (int i0 = 0; i0 < nparts; i0 += 16 * 8) {
+      VStat part[8];                 // all loads of a batch issued before merging
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 16 + sub;
+        part[u] = (on && i < nparts) ? VStat{pm[base + i], ps[base + i], pq[base + i],
+                                             pa[base + i], plc[base + i]}
+                                     : vstat_empty();
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) st = vstat_merge(st, part[u]);
     }
     st = row_merge_vstat(st);
     if (on && sub == 0) {
@@ -550,16 +576,18 @@ using CoopKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int
                             int, float*, float*, int32_t*, int, const int32_t*, int, float*,
                             float*);
 
-template <bool VERIFY>
+template <int MT, bool VERIFY>
 static CoopKernel coop_kernel_for(int H) {
   switch (H / 256) {
-    case 1: return &head_coop_kernel<1, VERIFY>;
-    case 2: return &head_coop_kernel<2, VERIFY>;
-    case 4: return &head_coop_kernel<4, VERIFY>;
-    case 8: return &head_coop_kernel<8, VERIFY>;
+    case 1: return &head_coop_kernel<1, MT, VERIFY>;
+    case 2: return &head_coop_kernel<2, MT, VERIFY>;
+    case 4: return &head_coop_kernel<4, MT, VERIFY>;
+    case 8: return &head_coop_kernel<8, MT, VERIFY>;
     default: return nullptr;
   }
 }
+
+constexpr int kCoopChunk = 64;   // rows per pass of the cooperative kernel (MT = 4)
 
 void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V, int voff,
                        int layout, int32_t mask_id, float* pm, float* ps, int32_t* pa,
@@ -567,17 +595,21 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
 #ifndef BDM_HEAD_COOP
 #define BDM_HEAD_COOP 1
 #endif
-  CoopKernel coop = (BDM_HEAD_COOP && H % 256 == 0) ? coop_kernel_for<false>(H) : nullptr;
+  if (BDM_HEAD_COOP && H % 256 == 0 && coop_kernel_for<2, false>(H)) {
+    for (int t0 = 0; t0 < T; t0 += kCoopChunk) {
+      const int n = (T - t0) < kCoopChunk ? (T - t0) : kCoopChunk;
+      CoopKernel k = n <= 32 ? coop_kernel_for<2, false>(H) : coop_kernel_for<4, false>(H);
+      k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
+                                         pstride, nullptr, 0, nullptr, nullptr);
+    }
+    return;
+  }
   HeadKernel tile = head_kernel_for(H);
-  const size_t lds = coop ? 0 : head_lds_bytes(H);
+  const size_t lds = head_lds_bytes(H);
   for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
     const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
-    if (coop)
-      coop<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
-                                            pstride, nullptr, 0, nullptr, nullptr);
-    else
-      tile<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps,
-                                              pa, pstride);
+    tile<<<grid, kHeadWaves * 64, lds, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
+                                            pstride);
   }
 }
 
@@ -585,9 +617,9 @@ void launch_head_verify_stats(const uint16_t* h, int T, int H, const uint16_t* w
                               int layout, const int32_t* cand, int ncand, float* pm, float* ps,
                               int32_t* pa, float* pq, float* plc, int pstride, int grid,
                               hipStream_t s) {
-  CoopKernel k = coop_kernel_for<true>(H);
-  for (int t0 = 0; t0 < T; t0 += kHeadTokChunk) {
-    const int n = (T - t0) < kHeadTokChunk ? (T - t0) : kHeadTokChunk;
+  for (int t0 = 0; t0 < T; t0 += kCoopChunk) {
+    const int n = (T - t0) < kCoopChunk ? (T - t0) : kCoopChunk;
+    CoopKernel k = n <= 32 ? coop_kernel_for<2, true>(H) : coop_kernel_for<4, true>(H);
     k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, 0, layout, -1, t0, n, pm, ps, pa, pstride,
                                        cand, ncand, pq, plc);
   }

@@ -40,7 +40,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-HEAD_KERNELS = ("head_coop_kernel", "head_tile_kernel")   # the head GEMM (either variant)
+# the head GEMM of the unmask step (either variant; not the verify epilogue's
+# instance head_coop_kernel<KSW, true>)
+HEAD_KERNELS = ("head_coop_kernel", "head_tile_kernel")
 HEAD_SOURCES = ("head.hip", "device.hpp", "internal.hpp")
 
 
@@ -124,7 +126,9 @@ def summarize(a):
         fb = f_fac * 1024.0 * sum(fv) / len(fv)
         wb = w_fac * 1024.0 * sum(wv) / len(wv)
         rows.append((n, len(fv), fb, wb))
-        if n.split("::")[-1].startswith(HEAD_KERNELS):
+        short = n.split("::")[-1]
+        verify_variant = short.startswith("head_coop_kernel<") and short.endswith(", true>")
+        if short.startswith(HEAD_KERNELS) and not verify_variant:
             head_bytes = fb + wb if head_bytes is None else max(head_bytes, fb + wb)
     out = [f"<!-- source_sha256 = {kernel_source_digest()} -->"]
     if head_bytes is not None:

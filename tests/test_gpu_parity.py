@@ -304,6 +304,30 @@ def test_head_two_phase_and_vocab_shards(bdm, layout):
     compare_head((tok, am, cf, nc), o, blk.tokens.cpu().numpy())
 
 
+@pytest.mark.parametrize("T", [33, 64, 100])
+def test_head_wide_pass_equals_32_row_calls(bdm, T):
+    """Up to 64 rows share one pass over the head weights; every row's
+    partial statistics equal those of the same row computed in a call of at
+    most 32 rows, bit for bit (the per-row arithmetic does not change)."""
+    say(f"case head wide pass T={T}")
+    s = synth.HeadShape(T=T, H=2048, V=70001, mask_id=5)
+    W = synth.head_weights(s, 6, device=DEV)
+    blk = synth.head_block(s, W, block_seed=T, n_boost=8)
+    P = bdm.bdm_head_stat_parts()
+    for Wl in (W, bdm.bdm_pack_weights(W)):
+        wide = [torch.empty((T, P), dtype=dt, device=DEV)
+                for dt in (torch.float32, torch.float32, torch.int32)]
+        bdm.bdm_lm_head_stats(blk.h, Wl, s.mask_id, *wide)
+        narrow = [torch.empty_like(x) for x in wide]
+        for t0 in range(0, T, 32):
+            t1 = min(T, t0 + 32)
+            bdm.bdm_lm_head_stats(blk.h[t0:t1].contiguous(), Wl, s.mask_id,
+                                  *[x[t0:t1] for x in narrow])
+        torch.cuda.synchronize()
+        for x, z in zip(wide, narrow):
+            assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+
+
 def test_head_repeatable_bitwise(bdm):
     say("case head repeatability")
     s = synth.HeadShape(T=32, H=2048, V=65536, mask_id=3)
