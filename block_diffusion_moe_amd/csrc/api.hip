@@ -30,7 +30,6 @@ int check_moe_shape(int T, int H, int I, int E, int k, int has_shared) {
 size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
                   bdm::MoeMeta* m) {
   const size_t P = static_cast<size_t>(T) * (k + 1);
-  (void)has_shared;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -43,7 +42,7 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
   char* topk_p = take(sizeof(float) * T * k);
   char* ticket = take(sizeof(int32_t) * 4);
   char* info = take(sizeof(int32_t) * 4);
-  char* slots = take(sizeof(int) * 4 * (E + 1));
+  char* slots = take(sizeof(int) * 4 * bdm::moe_max_slots(T, E, k, has_shared));
   char* pair_rows = take(sizeof(int32_t) * P);
   char* act = take(sizeof(uint16_t) * P * I);
   char* ypair = take(sizeof(float) * P * H);

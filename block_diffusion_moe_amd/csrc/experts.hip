@@ -230,6 +230,250 @@ __global__ __launch_bounds__(256, 2) void down_kernel(
   }
 }
 
+// ---- many tokens per group (multi-block batches) ---------------------------
+// With many blocks in one call a touched expert serves tens of tokens, and a
+// work item (one slot: at most kSlotChunk = 64 tokens) holds all of them as
+// four 16-token MFMA row tiles.  Every weight byte is still read once per
+// slot, straight into registers, while the token rows are read once per
+// work item (not once per 16 weight rows).  Per element the arithmetic is
+// that of the kernels above (same K split, same summation order), so the
+// results are bit-identical to theirs.
+#ifndef BDM_WIDE_GU_GROUPS
+#define BDM_WIDE_GU_GROUPS 8
+#endif
+#ifndef BDM_WIDE_DN_GROUPS
+#define BDM_WIDE_DN_GROUPS 1
+#endif
+constexpr int kWideMt = 4;                             // 16-token row tiles per work item
+constexpr int kWideGuGroups = BDM_WIDE_GU_GROUPS;      // 16-column groups of I per gate/up item
+constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per wave in down
+
+// gate/up: work item = (slot, kWideGuGroups column groups).  The 8 waves
+// split K = H (KSW k-steps each) and hold their K-slice of the slot's token
+// rows in registers; the weights stream one 16-row group at a time,
+// alternating gate and up, each load issued two steps ahead (the gate and
+// up buffers ping-pong).  The 8 partial products of a group meet in LDS and
+// are summed in wave order; silu(g) * u is stored as bf16.
+template <int KSW>
+__global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
+    const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
+    const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
+    const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    uint16_t* __restrict__ act) {
+  static_assert(kGuWaves == 8, "8 waves split K");
+  constexpr int MT = kWideMt;
+  __shared__ float part[2][2][kGuWaves][MT][4][kWave];   // [gate/up][buffer]: 128 KB
+  __shared__ int srow[16 * MT];
+
+  const int ngi = I / 16;                                 // column groups of I
+  const int runs = (ngi + kWideGuGroups - 1) / kWideGuGroups;
+  const int4 slot = slots[blockIdx.x / runs];
+  const int e = slot.x;
+  const int off = slot.y;
+  const int m = slot.z < 16 * MT ? slot.z : 16 * MT;
+  if (!slot_ok(e, off, slot.z, E, P, ws_gate != nullptr)) return;
+  const int q0 = (blockIdx.x % runs) * kWideGuGroups;    // first column group
+  const int nq = (ngi - q0) < kWideGuGroups ? (ngi - q0) : kWideGuGroups;
+  const int K1 = k + 1;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int s0 = wave * KSW;
+
+  const uint16_t* wg = e == E ? ws_gate : w_gate;
+  const uint16_t* wu = e == E ? ws_up : w_up;
+  const long wrow = (e == E) ? 0 : static_cast<long>(e) * I;
+  // weights of column group q of this run; q >= nq: 16 bytes of token row
+  // 0 per lane instead (valid, cached, ignored)
+  auto load = [&](const uint16_t* W, int q, u32x4(&b)[KSW]) {
+    const FragPtr f = q < nq ? frag_ptr(W, wrow + 16L * (q0 + q), H, lane, layout)
+                             : FragPtr{x + c * 8, 0};
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) b[s] = ld16_stream(f.p + (s0 + s) * f.step);
+  };
+  // pair rows first, then the weight burst (in-order completion: the rows
+  // can be waited for without waiting for the weights)
+  const int prow = tid < 16 * MT ? clamp_row(pair_rows[off + (tid < m ? tid : 0)], P) : 0;
+  u32x4 bg[KSW], bu[KSW];
+  load(wg, 0, bg);
+  load(wu, 0, bu);
+  if (tid < 16 * MT) srow[tid] = prow;
+  __syncthreads();
+  // this wave's K-slice of the slot's token rows (rows >= m are zero)
+  u32x4 a[MT][KSW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = 16 * mt + c;
+    const bool ok = r < m;
+    const uint16_t* xr = x + static_cast<size_t>(srow[r] / K1) * H + g * 8;
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+      const u32x4 v = ld16(xr + (s0 + s) * 32);
+      a[mt][s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // the partial products of one matrix's group; each k-step of the same
+  // matrix's next group is requested as soon as this one has been used
+  auto partial = [&](u32x4(&b)[KSW], const uint16_t* W, int qn, float* pp) {
+    const FragPtr fn = qn < nq ? frag_ptr(W, wrow + 16L * (q0 + qn), H, lane, layout)
+                               : FragPtr{x + c * 8, 0};
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSW; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
+      b[s] = ld16_stream(fn.p + (s0 + s) * fn.step);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[(mt * 4 + i) * kWave + lane] = acc[mt][i];
+  };
+  for (int q = 0; q < nq; ++q) {
+    const int buf = q & 1;
+    partial(bg, wg, q + 1, &part[0][buf][wave][0][0][0]);
+    partial(bu, wu, q + 1, &part[1][buf][wave][0][0][0]);
+    __syncthreads();
+    // fold: 64 tokens x 16 columns, two per thread
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int o = tid + f * kGuWaves * kWave;
+      const int r = o >> 4, cc = o & 15;
+      const int mt = r >> 4, rr = r & 15;
+      const int ln = 16 * (rr >> 2) + cc, i = rr & 3;
+      float gs = part[0][buf][0][mt][i][ln], us = part[1][buf][0][mt][i][ln];
+#pragma unroll
+      for (int w = 1; w < kGuWaves; ++w) {
+        gs += part[0][buf][w][mt][i][ln];
+        us += part[1][buf][w][mt][i][ln];
+      }
+      if (r < m) {
+        const float av = gs / (1.0f + expf(-gs)) * us;
+        act[static_cast<size_t>(srow[r]) * I + 16 * (q0 + q) + cc] = f32_to_bf16(av);
+      }
+    }
+  }
+}
+
+// down: work item = (slot, 8 waves x kWideDnGroups groups of 16 rows of H).
+// The slot's activation rows are staged once in LDS in MFMA operand order
+// (tile (mt, s) = 64 lanes x 16 B, conflict-free reads); every wave then
+// owns its own 16-row groups over the whole K = I, their weights loaded
+// two groups ahead, and stores fp32 results per (token, slot) row.
+template <int KSMAX>
+#ifndef BDM_DN_WIDE_WAVES_PER_EU
+#define BDM_DN_WIDE_WAVES_PER_EU 4     // two workgroups per CU (<= 128 registers)
+#endif
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    BDM_DN_WIDE_WAVES_PER_EU, BDM_DN_WIDE_WAVES_PER_EU))) void down_wide_kernel(
+    const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
+    const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    float* __restrict__ ypair) {
+  constexpr int MT = kWideMt;
+  constexpr int NW = 8;
+  __shared__ u32x4 at[MT][KSMAX][kWave];               // 64 KB at KSMAX = 16
+  __shared__ int srow[16 * MT];
+
+  const int ngh = H / 16;
+  const int per = NW * kWideDnGroups;                  // groups per work item
+  const int runs = (ngh + per - 1) / per;
+  const int4 slot = slots[blockIdx.x / runs];
+  const int e = slot.x;
+  const int off = slot.y;
+  const int m = slot.z < 16 * MT ? slot.z : 16 * MT;
+  if (!slot_ok(e, off, slot.z, E, P, ws_down != nullptr)) return;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int KS = I / 32;
+  const int gbase = (blockIdx.x % runs) * per + wave * kWideDnGroups;
+
+  const uint16_t* W = e == E ? ws_down : w_down;
+  const long wrow = (e == E) ? 0 : static_cast<long>(e) * H;
+  // weights of this wave's group j; past its groups (or past H): 16 bytes of
+  // activation row 0 per lane instead (valid, cached, ignored)
+  auto wptr = [&](int j) -> FragPtr {
+    const int gi = gbase + j;
+    return (j < kWideDnGroups && gi < ngh) ? frag_ptr(W, wrow + 16L * gi, I, lane, layout)
+                                           : FragPtr{act + c * 8, 0};
+  };
+  auto ldk = [&](FragPtr f, int s) -> u32x4 {
+    const bool on = s < KS;
+    const u32x4 v = ld16_stream(f.p + (on ? s : 0) * f.step);
+    return on ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+  const int prow = tid < 16 * MT ? clamp_row(pair_rows[off + (tid < m ? tid : 0)], P) : 0;
+  u32x4 b[KSMAX];
+  {
+    const FragPtr f = wptr(0);
+#pragma unroll
+    for (int s = 0; s < KSMAX; ++s) b[s] = ldk(f, s);
+  }
+  if (tid < 16 * MT) srow[tid] = prow;
+  __syncthreads();
+  // stage the activation rows: chunk (r, s, gg) of 8 values -> tile
+  // (r / 16, s), lane (r % 16) + 16 gg; all loads first
+  constexpr int NCH = 16 * MT * KSMAX * 4 / (NW * kWave);
+  static_assert(NCH * NW * kWave == 16 * MT * KSMAX * 4, "whole chunks per thread");
+  constexpr int NB = NCH >= 4 ? 4 : NCH;           // chunks per batch
+  static_assert(NCH % NB == 0, "whole batches");
+#pragma unroll
+  for (int u0 = 0; u0 < NCH; u0 += NB) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int ch = tid + (u0 + u) * NW * kWave;
+      const int gg = ch & 3, s = (ch >> 2) % KSMAX, r = (ch >> 2) / KSMAX;
+      v[u] = ld16(act + static_cast<size_t>(srow[r]) * I + (s < KS ? s : 0) * 32 + gg * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int ch = tid + (u0 + u) * NW * kWave;
+      const int gg = ch & 3, s = (ch >> 2) % KSMAX, r = (ch >> 2) / KSMAX;
+      at[r >> 4][s][(r & 15) + 16 * gg] = (r < m && s < KS) ? v[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+
+  // each k-step of the next group is requested as soon as this group's
+  // k-step has been multiplied (one group per wave in flight, in order)
+  for (int j = 0; j < kWideDnGroups; ++j) {
+    const FragPtr fn = wptr(j + 1);
+    // an opaque zero: the operand reads stay inside the loop (hoisted out,
+    // the 64 tiles would take 256 registers)
+    int lz = lane;
+    asm volatile("" : "+v"(lz));
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSMAX; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(at[mt][s][lz], b[s], acc[mt]);
+      b[s] = ldk(fn, s);
+    }
+    const int gi = gbase + j;
+    if (gi < ngh) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * g + i;
+          if (r < m) ypair[static_cast<size_t>(srow[r]) * H + 16 * gi + c] = acc[mt][i];
+        }
+    }
+  }
+}
+
 // One workgroup per token; a thread owns 8 consecutive columns and issues all
 // of its k+1 row loads before summing them in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ypair, int H,
@@ -317,11 +561,37 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                     const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
                     const MoeMeta& meta, int layout, hipStream_t s) {
-  // upper bound on touched groups; workgroups past the actual list exit at once
-  const int groups = (T * k < E ? T * k : E) + (has_shared ? 1 : 0);
+  // upper bound on the slots; workgroups past the actual list exit at once
+  const int groups = moe_max_slots(T, E, k, has_shared);
   const int P = T * (k + 1);
   const dim3 gu(groups * (I / kGuCols)), dn(groups * (H / kDnRows));
   const int KS = H / 32;
+  const int KI = I / 32;
+#ifndef BDM_WIDE_MIN_T
+#define BDM_WIDE_MIN_T 384
+#endif
+  const int ksw = H / 256;
+  if (T >= BDM_WIDE_MIN_T && H % 256 == 0 && (ksw == 1 || ksw == 2 || ksw == 4 || ksw == 8) &&
+      KI <= 16) {
+    const int gu_runs = (I / 16 + kWideGuGroups - 1) / kWideGuGroups;
+    const int dn_runs = (H / 16 + 8 * kWideDnGroups - 1) / (8 * kWideDnGroups);
+    using GuWide = void (*)(const uint16_t*, int, int, int, int, int, int, const uint16_t*,
+                            const uint16_t*, const uint16_t*, const uint16_t*, const int4*,
+                            const int32_t*, uint16_t*);
+    const GuWide guw = ksw == 1   ? &gateup_wide_kernel<1>
+                       : ksw == 2 ? &gateup_wide_kernel<2>
+                       : ksw == 4 ? &gateup_wide_kernel<4>
+                                  : &gateup_wide_kernel<8>;
+    guw<<<groups * gu_runs, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up,
+                                                  ws_gate, ws_up, meta.slots, meta.pair_rows,
+                                                  meta.act);
+    down_wide_kernel<16><<<groups * dn_runs, 512, 0, s>>>(meta.act, H, I, E, P, layout, w_down,
+                                                          ws_down, meta.slots, meta.pair_rows,
+                                                          meta.ypair);
+    combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
+                                     residual, y, y_norm);
+    return;
+  }
   if (KS == kGuWaves * 8) {
     gateup_kernel<8, false><<<gu, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
                                                         ws_up, meta.slots, meta.pair_rows,
@@ -331,7 +601,6 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                                                        ws_up, meta.slots, meta.pair_rows,
                                                        meta.act);
   }
-  const int KI = I / 32;
   if (KI == 16) {
     down_kernel<16, false><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                               meta.pair_rows, meta.ypair);

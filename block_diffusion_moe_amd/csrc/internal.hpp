@@ -17,6 +17,21 @@ namespace bdm {
 // t*(k+1)+j holds the j-th pick of token t, row t*(k+1)+k its shared expert.
 constexpr int kRouterParts = 4;   // K-parts of the router GEMM (summed by select)
 
+// An expert work item serves at most kSlotChunk of its group's tokens; a
+// longer group (the shared expert, or a routed expert of a many-block batch)
+// takes several consecutive slots.  Upper bound on the slots of a T-token
+// layer: one per touched routed expert (<= min(T*k, E)), plus at most
+// floor(T*k / kSlotChunk) extra chunks over all routed experts (none unless
+// T > kSlotChunk: an expert holds a token at most once), plus the shared
+// expert's ceil(T / kSlotChunk).
+constexpr int kSlotChunk = 64;
+__host__ __device__ inline int moe_max_slots(int T, int E, int k, int has_shared) {
+  const int routed = T * k < E ? T * k : E;
+  const int extra = T > kSlotChunk ? (T * k) / kSlotChunk : 0;
+  const int shared = has_shared ? (T + kSlotChunk - 1) / kSlotChunk : 0;
+  return routed + extra + shared;
+}
+
 struct MoeMeta {
   float* logits;        // [4][T][E]     partial router logits (fp32), one per K-part
   int32_t* topk_idx;    // [T][k]        picks, decreasing weight

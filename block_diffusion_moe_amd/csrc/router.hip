@@ -33,24 +33,28 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
 }
 
 constexpr int kRtWaves = 4;     // waves per router workgroup
+constexpr int kRtWideTiles = 4; // token tiles per router workgroup in many-block calls
+constexpr int kRtWideMinT = 512;
 constexpr int kRtMaxKs = 4;     // k-steps per wave: H <= kRouterParts * 4 * 4 * 32 = 2048
 
 // Partial logits over one K-part: part[z][t][e] = sum_{h in part z} x[t][h] w[e][h].
 // The fp32 partials are summed (in part order) with the bias by the select
 // step.  Block (0,0,0) also clears the select step's completion ticket.
+// NTT token tiles of 32 per workgroup share one load and split of the
+// router weights (NTT > 1 for many-block calls).
+template <int NTT>
 __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* __restrict__ x,
                                                               int T, int H,
                                                               const float* __restrict__ wr, int E,
                                                               float* __restrict__ part,
                                                               int32_t* __restrict__ ticket) {
-  __shared__ f32x4 red[kRtWaves][2][kWave];
+  __shared__ f32x4 red[2][kRtWaves][2][kWave];
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *ticket = 0;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
   const int e0 = blockIdx.x * 16;
-  const int t0 = blockIdx.y * 32;
   const int z = blockIdx.z;
   const int KS = H / 32;
   const int ksp = (KS + kRouterParts - 1) / kRouterParts;       // k-steps of this part
@@ -60,11 +64,18 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
 
   const int er = (e0 + c) < E ? (e0 + c) : (E - 1);
   const float* wrow = wr + static_cast<size_t>(er) * H + g * 8;
-  const bool ok0 = (t0 + c) < T;
-  const bool ok1 = (t0 + 16 + c) < T;
-  const bool two = (t0 + 16) < T;
-  const uint16_t* x0 = x + static_cast<size_t>(ok0 ? t0 + c : 0) * H + g * 8;
-  const uint16_t* x1 = x + static_cast<size_t>(ok1 ? t0 + 16 + c : 0) * H + g * 8;
+  auto xload = [&](int t0, u32x4(&a0)[kRtMaxKs], u32x4(&a1)[kRtMaxKs]) {
+    const bool ok0 = (t0 + c) < T, ok1 = (t0 + 16 + c) < T;
+    const uint16_t* x0 = x + static_cast<size_t>(ok0 ? t0 + c : 0) * H + g * 8;
+    const uint16_t* x1 = x + static_cast<size_t>(ok1 ? t0 + 16 + c : 0) * H + g * 8;
+#pragma unroll
+    for (int q = 0; q < kRtMaxKs; ++q) {
+      const int s = (s0 + q < s1) ? s0 + q : 0;
+      const u32x4 v0 = ld16(x0 + s * 32), v1 = ld16(x1 + s * 32);
+      a0[q] = ok0 ? v0 : u32x4{0u, 0u, 0u, 0u};
+      a1[q] = ok1 ? v1 : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   // every load of this wave's K-slice first (clamped, no branches), then math
   float4 wa[kRtMaxKs], wb[kRtMaxKs];
@@ -74,51 +85,57 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
     const int s = (s0 + q < s1) ? s0 + q : 0;
     wa[q] = *reinterpret_cast<const float4*>(wrow + s * 32);
     wb[q] = *reinterpret_cast<const float4*>(wrow + s * 32 + 4);
-    a0[q] = ld16(x0 + s * 32);
-    a1[q] = ld16(x1 + s * 32);
   }
-  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  xload(blockIdx.y * NTT * 32, a0, a1);
+  u32x4 bh[kRtMaxKs], bm[kRtMaxKs], bl[kRtMaxKs];
 #pragma unroll
   for (int q = 0; q < kRtMaxKs; ++q) {
-    if (s0 + q < s1) {
-      const float wv[8] = {wa[q].x, wa[q].y, wa[q].z, wa[q].w, wb[q].x, wb[q].y, wb[q].z, wb[q].w};
-      uint16_t hi[8], mi[8], lo[8];
+    const float wv[8] = {wa[q].x, wa[q].y, wa[q].z, wa[q].w, wb[q].x, wb[q].y, wb[q].z, wb[q].w};
+    uint16_t hi[8], mi[8], lo[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split3(wv[j], hi[j], mi[j], lo[j]);
-      u32x4 bh, bm, bl;
+    for (int j = 0; j < 8; ++j) split3(wv[j], hi[j], mi[j], lo[j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bh[j] = static_cast<uint32_t>(hi[2 * j]) | (static_cast<uint32_t>(hi[2 * j + 1]) << 16);
-        bm[j] = static_cast<uint32_t>(mi[2 * j]) | (static_cast<uint32_t>(mi[2 * j + 1]) << 16);
-        bl[j] = static_cast<uint32_t>(lo[2 * j]) | (static_cast<uint32_t>(lo[2 * j + 1]) << 16);
-      }
-      const u32x4 z0 = ok0 ? a0[q] : u32x4{0u, 0u, 0u, 0u};
-      acc0 = mfma_bf16(z0, bh, acc0);
-      acc0 = mfma_bf16(z0, bm, acc0);
-      acc0 = mfma_bf16(z0, bl, acc0);
-      if (two) {
-        const u32x4 z1 = ok1 ? a1[q] : u32x4{0u, 0u, 0u, 0u};
-        acc1 = mfma_bf16(z1, bh, acc1);
-        acc1 = mfma_bf16(z1, bm, acc1);
-        acc1 = mfma_bf16(z1, bl, acc1);
-      }
+    for (int j = 0; j < 4; ++j) {
+      bh[q][j] = static_cast<uint32_t>(hi[2 * j]) | (static_cast<uint32_t>(hi[2 * j + 1]) << 16);
+      bm[q][j] = static_cast<uint32_t>(mi[2 * j]) | (static_cast<uint32_t>(mi[2 * j + 1]) << 16);
+      bl[q][j] = static_cast<uint32_t>(lo[2 * j]) | (static_cast<uint32_t>(lo[2 * j + 1]) << 16);
     }
   }
-  red[wave][0][lane] = acc0;
-  red[wave][1][lane] = acc1;
-  __syncthreads();
-  if (threadIdx.x < 2 * kWave) {
-    const int mt = threadIdx.x / kWave;
-    const int ln = threadIdx.x % kWave;
-    f32x4 sum = red[0][mt][ln];
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int t0 = (blockIdx.y * NTT + tt) * 32;
+    if (t0 >= T) break;                                  // workgroup-uniform
+    const bool two = (t0 + 16) < T;
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 1; w < kRtWaves; ++w) sum += red[w][mt][ln];
-    const int e = e0 + (ln & 15);
-    if (e < E) {
+    for (int q = 0; q < kRtMaxKs; ++q) {
+      if (s0 + q < s1) {
+        acc0 = mfma_bf16(a0[q], bh[q], acc0);
+        acc0 = mfma_bf16(a0[q], bm[q], acc0);
+        acc0 = mfma_bf16(a0[q], bl[q], acc0);
+        if (two) {
+          acc1 = mfma_bf16(a1[q], bh[q], acc1);
+          acc1 = mfma_bf16(a1[q], bm[q], acc1);
+          acc1 = mfma_bf16(a1[q], bl[q], acc1);
+        }
+      }
+    }
+    if (tt + 1 < NTT && t0 + 32 < T) xload(t0 + 32, a0, a1);   // next tile in flight
+    red[tt & 1][wave][0][lane] = acc0;
+    red[tt & 1][wave][1][lane] = acc1;
+    __syncthreads();
+    if (threadIdx.x < 2 * kWave) {
+      const int mt = threadIdx.x / kWave;
+      const int ln = threadIdx.x % kWave;
+      f32x4 sum = red[tt & 1][0][mt][ln];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + mt * 16 + 4 * (ln >> 4) + i;
-        if (t < T) part[(static_cast<size_t>(z) * T + t) * E + e] = sum[i];
+      for (int w = 1; w < kRtWaves; ++w) sum += red[tt & 1][w][mt][ln];
+      const int e = e0 + (ln & 15);
+      if (e < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + mt * 16 + 4 * (ln >> 4) + i;
+          if (t < T) part[(static_cast<size_t>(z) * T + t) * E + e] = sum[i];
+        }
       }
     }
   }
@@ -247,23 +264,27 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
 }
 
 constexpr int kSelWaves = 4;       // tokens per select workgroup (one wave each)
+constexpr int kSelSplitMinT = 512; // from this many tokens: top-k kernel, then group_kernel
 constexpr int kSelOneWaves = 16;   // waves of the single-workgroup select (small blocks)
 constexpr int kSelOneMaxT = 16;    // largest block the single-workgroup select takes
 
 // Group the T*k picks by expert for the expert kernels (every thread of the
 // workgroup calls this; picks in LDS or global memory, -1 = no expert):
-//   slots[i] = {expert, offset, count, 0} for the i-th touched group -- the
-//              shared expert (group E, all T tokens) first, then routed
-//              experts with at least 16 tokens, then the others, each run in
-//              increasing id -- and {-1, 0, 0, 0} for i = n .. E;
+//   slots[i] = {expert, offset, count, 0}: one work item of at most
+//              kSlotChunk tokens of a group -- the shared expert's chunks
+//              (group E, all T tokens) first, then the chunks of routed
+//              experts with at least 16 tokens, then the others, experts in
+//              increasing id and an expert's chunks consecutive -- and
+//              {-1, 0, 0, 0} for i = n .. moe_max_slots - 1;
 //   pair_rows[offset .. offset+count) = the (token, slot) rows t*(k+1)+j of
-//              the group's tokens (shared: t*(k+1)+k); the ranges follow
-//              expert id order after the shared expert's [0, T).
+//              the chunk's tokens (shared: t*(k+1)+k); the groups' ranges
+//              follow expert id order after the shared expert's [0, T).
 // Wave 0 ranks the experts: lane L holds experts L*epl .. L*epl+epl-1, so
-// (lane, j) order is id order and ballot popcounts give every touched
-// expert's slot position.  The order inside a group is whatever the LDS
-// atomics produce; every row's result is computed on its own, so outputs do
-// not depend on it.
+// (lane, j) order is id order, and ballot popcounts (light experts: one
+// slot each) and bit-sliced ballot prefixes (heavy experts' chunk counts,
+// pair offsets) give every expert's first slot and pair offset.  The order
+// inside a group is whatever the LDS atomics produce; every row's result is
+// computed on its own, so outputs do not depend on it.
 template <int PER>
 __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_shared, int* cnt,
                             int* eoff, int* fill, int4* __restrict__ slots,
@@ -277,62 +298,97 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
     fill[e] = 0;
   }
   __syncthreads();
-  for (int p = tid; p < T * k; p += blockDim.x) {
-    const int e = picks[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  // picks in batches of 8 per thread, every load of a batch issued first
+  const int np = T * k;
+  for (int p0 = 0; p0 < np; p0 += 8 * static_cast<int>(blockDim.x)) {
+    int eb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * static_cast<int>(blockDim.x) + tid;
+      eb[u] = p < np ? picks[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (eb[u] >= 0 && eb[u] < E) atomicAdd(&cnt[eb[u]], 1);
   }
   __syncthreads();
-  const int base = has_shared ? 1 : 0;
+  const int nsh = has_shared ? (T + kSlotChunk - 1) / kSlotChunk : 0;   // shared chunks
   if (wave == 0) {
     constexpr int EPL = PER;                          // experts per lane, at most
     const int epl = (E + kWave - 1) / kWave;          // E <= 64 * PER
     const unsigned long long bel = (1ull << lane) - 1ull;
     int c[EPL];
-    int nh = 0, nl = 0, hb = 0, lb = 0;      // totals; touched experts below this lane
+    int nl = 0, lb = 0;              // light experts: total, in lanes below
+    int hch = 0, tot = 0;            // this lane's heavy chunks and pairs
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane * epl + j;
       c[j] = (j < epl && e < E) ? cnt[e] : 0;
-      const unsigned long long mh = __ballot(c[j] >= 16);
       const unsigned long long ml = __ballot(c[j] > 0 && c[j] < 16);
-      nh += __popcll(mh);
       nl += __popcll(ml);
-      hb += __popcll(mh & bel);
       lb += __popcll(ml & bel);
+      if (c[j] >= 16) hch += (c[j] + kSlotChunk - 1) / kSlotChunk;
+      tot += c[j];
     }
-    // pair offsets in expert-id order: this lane's exclusive prefix of the
-    // per-lane pair totals, one ballot per bit of the total (< 2^15)
-    int tot = 0;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) tot += c[j];
+    // exclusive prefixes over the lanes, one ballot per bit (a lane's pairs
+    // are < 2^16: at most T <= 2^11 per expert, PER <= 16 experts; its
+    // chunks fewer still)
+    int hb = 0, nh = 0;
     int pref = has_shared ? T : 0;
 #pragma unroll
-    for (int bit = 0; bit < 15; ++bit) pref += __popcll(__ballot((tot >> bit) & 1) & bel) << bit;
-    int ho = 0, lo = 0;                       // this lane's touched experts so far
+    for (int bit = 0; bit < 16; ++bit) {
+      const unsigned long long bh = __ballot((hch >> bit) & 1);
+      hb += __popcll(bh & bel) << bit;
+      nh += __popcll(bh) << bit;
+      pref += __popcll(__ballot((tot >> bit) & 1) & bel) << bit;
+    }
+    int ho = 0, lo = 0;                       // this lane's slots so far
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       if (c[j] > 0) {
         const int e = lane * epl + j;
-        const bool heavy = c[j] >= 16;
-        const int pos = base + (heavy ? hb + ho : nh + lb + lo);
-        slots[pos] = int4{e, pref, c[j], 0};
+        if (c[j] >= 16) {
+          const int pos = nsh + hb + ho;
+          int q = 0;
+          for (int o = 0; o < c[j]; o += kSlotChunk, ++q) {
+            const int m = c[j] - o < kSlotChunk ? c[j] - o : kSlotChunk;
+            slots[pos + q] = int4{e, pref + o, m, 0};
+          }
+          ho += q;
+        } else {
+          slots[nsh + nh + lb + lo] = int4{e, pref, c[j], 0};
+          ++lo;
+        }
         eoff[e] = pref;
-        if (heavy) ++ho; else ++lo;
       }
       pref += c[j];
     }
-    const int n = base + nh + nl;
-    if (has_shared && lane == 0) slots[0] = int4{E, 0, T, 0};
-    for (int i = n + lane; i <= E; i += kWave) slots[i] = int4{-1, 0, 0, 0};
+    const int n = nsh + nh + nl;
+    for (int i = lane; i < nsh; i += kWave) {
+      const int o = i * kSlotChunk;
+      slots[i] = int4{E, o, T - o < kSlotChunk ? T - o : kSlotChunk, 0};
+    }
+    const int nmax = moe_max_slots(T, E, k, has_shared);
+    for (int i = n + lane; i < nmax; i += kWave) slots[i] = int4{-1, 0, 0, 0};
     if (lane == 0) info[0] = n;
   }
   // scatter the pairs
   __syncthreads();
-  for (int p = tid; p < T * k; p += blockDim.x) {
-    const int e = picks[p];
-    if (e < 0 || e >= E) continue;
-    const int tt = p / k;
-    pair_rows[eoff[e] + atomicAdd(&fill[e], 1)] = tt * K1 + (p - tt * k);
+  for (int p0 = 0; p0 < np; p0 += 8 * static_cast<int>(blockDim.x)) {
+    int eb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * static_cast<int>(blockDim.x) + tid;
+      eb[u] = p < np ? picks[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = eb[u];
+      if (e < 0 || e >= E) continue;
+      const int p = p0 + u * static_cast<int>(blockDim.x) + tid;
+      const int tt = p / k;
+      pair_rows[eoff[e] + atomicAdd(&fill[e], 1)] = tt * K1 + (p - tt * k);
+    }
   }
   if (has_shared)
     for (int tt = tid; tt < T; tt += blockDim.x) pair_rows[tt] = tt * K1 + k;
@@ -345,16 +401,17 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
 // (completion ticket) groups the picks read back from global memory.
 // FIRST (first pass of the block coreset selector): the picks, their
 // weights and their probabilities over all E (topk_p) only; no grouping.
-template <int PER, int NW, bool SINGLE, bool FIRST>
+template <int PER, int NW, bool SINGLE, bool FIRST, bool GROUP = true>
 __global__ __launch_bounds__(NW * 64) void select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ topk_p, int32_t* ticket, int4* __restrict__ slots,
     int32_t* __restrict__ pair_rows, int32_t* __restrict__ info, int32_t* __restrict__ user_idx,
     float* __restrict__ user_w) {
-  __shared__ int cnt[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
-  __shared__ int eoff[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
-  __shared__ int fill[FIRST ? 1 : BDM_MAX_EXPERTS + 1];
+  constexpr bool kGroups = !FIRST && GROUP;
+  __shared__ int cnt[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
+  __shared__ int eoff[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
+  __shared__ int fill[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
   __shared__ int spick[SINGLE ? kSelOneMaxT * BDM_MAX_TOPK : 1];
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -378,7 +435,7 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
       if (SINGLE) spick[t * k + lane] = sel_e;
     }
   }
-  if constexpr (!FIRST) {
+  if constexpr (kGroups) {
     if (!SINGLE) {
       // publish this workgroup's picks, then take a ticket
       __threadfence();
@@ -391,6 +448,22 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
     group_picks<PER>(SINGLE ? spick : topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots,
                      pair_rows, info);
   }
+}
+
+// The grouping on its own (many-block calls): one workgroup after the
+// top-k kernel.  With hundreds of select workgroups, the device-wide
+// release each would need before a completion ticket (its L2 written back)
+// costs more than a second launch.
+template <int PER>
+__global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ topk_idx, int T,
+                                                     int E, int k, int has_shared,
+                                                     int4* __restrict__ slots,
+                                                     int32_t* __restrict__ pair_rows,
+                                                     int32_t* __restrict__ info) {
+  __shared__ int cnt[BDM_MAX_EXPERTS + 1];
+  __shared__ int eoff[BDM_MAX_EXPERTS + 1];
+  __shared__ int fill[BDM_MAX_EXPERTS + 1];
+  group_picks<PER>(topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
 }
 
 constexpr int kCsWaves = 16;       // waves of a coreset workgroup (one block of tokens)
@@ -701,8 +774,15 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
                    int k, int renorm, int has_shared, float top_p, int block,
                    const MoeMeta& meta, int32_t* user_idx, float* user_w, int32_t* n_kept,
                    hipStream_t s) {
-  const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
-  router_kernel<<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, meta.ticket);
+  if (T >= kRtWideMinT) {
+    const dim3 grid((E + 15) / 16, (T + 32 * kRtWideTiles - 1) / (32 * kRtWideTiles),
+                    kRouterParts);
+    router_kernel<kRtWideTiles><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits,
+                                                               meta.ticket);
+  } else {
+    const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
+    router_kernel<1><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, meta.ticket);
+  }
   const int nsel = (T + kSelWaves - 1) / kSelWaves;
   const bool core = top_p > 0.0f;
   const int ncs = core ? (T + block - 1) / block : 0;
@@ -719,6 +799,12 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
     select_kernel<P, kSelOneWaves, true, false><<<1, kSelOneWaves * 64, 0, s>>>(               \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
         meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+  } else if (T >= kSelSplitMinT) {                                                             \
+    select_kernel<P, kSelWaves, false, false, false><<<nsel, kSelWaves * 64, 0, s>>>(          \
+        meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
+        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+    group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,         \
+                                       meta.pair_rows, meta.info);                             \
   } else {                                                                                     \
     select_kernel<P, kSelWaves, false, false><<<nsel, kSelWaves * 64, 0, s>>>(                 \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \

@@ -73,7 +73,7 @@ extern "C" {
 #define BDM_LAYOUT_MFMA_TILES  1
 
 /* Limits of this implementation (checked; BDM_ERR_UNSUPPORTED_SHAPE beyond). */
-#define BDM_MAX_TOKENS   1024   /* T: positions per call (several blocks may be stacked) */
+#define BDM_MAX_TOKENS   2048   /* T: positions per call (up to 64 blocks of 32 stacked) */
 #define BDM_MAX_HIDDEN   2048   /* H, multiple of 64 */
 #define BDM_MAX_INTER    1024   /* I, multiple of 32 */
 #define BDM_MAX_EXPERTS  1024   /* E */
@@ -142,7 +142,7 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
  *   topk_w       [T][k] fp32 or NULL    receives w_t
  *   workspace, workspace_bytes: see bdm_moe_workspace_bytes
- * Limits: T <= 1024, H multiple of 64 and <= 2048, E <= 1024.
+ * Limits: T <= 2048, H multiple of 64 and <= 2048, E <= 1024.
  *   Pointers 16-byte aligned (workspace 256-byte aligned).  NaN inputs give
  *   undefined values, never an out-of-bounds access.
  * No other aliasing is allowed.
@@ -299,7 +299,7 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  *   argmax       [T] int32 or NULL  receives argmax_t for every row
  *   conf         [T] fp32 or NULL   receives conf_t for every row
  *   n_committed  DEVICE int32* or NULL: number of rows committed by this call
- * Limits: T <= 1024, H multiple of 64 and <= 2048 (V unrestricted above 2).
+ * Limits: T <= 2048, H multiple of 64 and <= 2048 (V unrestricted above 2).
  */
 BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
                        int weight_layout, int32_t mask_id, float threshold, int fallback,
@@ -379,7 +379,7 @@ BDM_API int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum,
  *   p_cand       [T1-1] fp32 or NULL   p_t(cand[t]) (0 for an id outside [0, V))
  *   entropy      [T1] fp32 or NULL     H_t
  * Workspace: bdm_head_verify_workspace_bytes(T1, H, V).  Limits: 1 <= T1 <=
- * 1024, H in {256, 512, 1024, 2048}, V >= 2.  All outputs are written on the
+ * 2048, H in {256, 512, 1024, 2048}, V >= 2.  All outputs are written on the
  * stream; nothing is read back to the host.
  */
 #define BDM_VERIFY_EXACT      0

@@ -173,7 +173,7 @@ def test_two_phase_head_validation(lib):
     assert lib.bdm_unmask_from_stats(S, S, S, 32, 0, 8, 5, 0.95, 1, A, None, None, None, None) == -1
     assert lib.bdm_unmask_from_stats(S, S, S, 32, 16, 8, 5, 0.95, 1, A, None, None, None, None) == -1
     assert lib.bdm_unmask_from_stats(S, S, S, 32, 8, 8, 5, 0.95, 1, None, None, None, None, None) == -1
-    assert lib.bdm_unmask_from_stats(S, S, S, 2000, 8, 8, 5, 0.95, 1, A, None, None, None, None) == -2
+    assert lib.bdm_unmask_from_stats(S, S, S, 4000, 8, 8, 5, 0.95, 1, A, None, None, None, None) == -2
 
 
 def test_calibration_library_exports():
@@ -207,7 +207,7 @@ def test_coreset_validation(lib):
     assert call(top_p=float("nan")) == -1
     assert call(block=0) == -1
     assert call(block=33) == -1
-    assert call(T=2000) == -2
+    assert call(T=4000) == -2
 
 
 def test_denoise_validation(lib):
@@ -234,7 +234,7 @@ def test_denoise_validation(lib):
     assert call(steps=-1) == -1
     assert call(layout=2) == -1
     assert call(thr=float("inf")) == -1
-    assert call(T=2000) == -2
+    assert call(T=4000) == -2
     assert call(H=2000) == -2
     lay[1].ws_gate = None                       # shared trio broken in one layer
     assert call() == -1
@@ -268,7 +268,7 @@ def test_verify_validation(lib):
     assert call(lay=3) == -1
     assert call(T1=0) == -1
     assert call(V=1) == -1
-    assert call(T1=1025) == -2
+    assert call(T1=2049) == -2
     assert call(H=2112) == -2          # multiple of 64, not of 256
     assert call(H=768) == -2           # multiple of 256 outside {256, 512, 1024, 2048}
     assert call(wsb=16) == -3
