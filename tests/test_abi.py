@@ -65,7 +65,8 @@ def test_moe_workspace_bytes(lib):
     assert lib.bdm_moe_workspace_bytes(32, 2047, 512, 256, 8, 1, ctypes.byref(size)) == -2
     assert lib.bdm_moe_workspace_bytes(32, 4096, 512, 256, 8, 1, ctypes.byref(size)) == -2
     assert lib.bdm_moe_workspace_bytes(32, 2048, 500, 256, 8, 1, ctypes.byref(size)) == -2
-    assert lib.bdm_moe_workspace_bytes(2048, 2048, 512, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(4096, 2048, 512, 256, 8, 1, ctypes.byref(size)) == -2
+    assert lib.bdm_moe_workspace_bytes(2048, 2048, 512, 256, 8, 1, ctypes.byref(size)) == 0
     assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 17, 1, ctypes.byref(size)) == -2
     assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 2, ctypes.byref(size)) == -1
     assert lib.bdm_moe_workspace_bytes(32, 2048, 512, 256, 8, 1, None) == -1
