@@ -37,6 +37,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(HERE, "profiles", "head_coop_kernel_clover_head.traffic.md")
 EXPERT_BYTES = 3 * 2048 * 512 * 2        # gate + up + down, bf16
 HEAD_BYTES = 248320 * 2048 * 2
@@ -252,6 +253,48 @@ def main():
     verify_us = start.elapsed_time(stop) * 1e3 / args.steps
     verify_gbs = HEAD_BYTES / (verify_us * 1e-6) / 1e9
 
+    # multi-block batching: 16, 32 and 64 blocks of 32 tokens in one MoE
+    # call (one pass over the touched experts), timed back to back the same way
+    multi = {}
+    for nb in (16, 32, 64):
+        TB = nb * T
+        shp = synth.MoEShape(T=TB, H=H, E=L.E, I=L.I, k=L.k)
+        xb = [synth.moe_tokens(shp, 500 + 10 * nb + r, dev)[0] for r in range(args.sets)]
+        wsb = bdm.workspace(bdm.bdm_moe_workspace_bytes(TB, H, L.I, L.E, L.k, True), dev)
+        yb = torch.empty((TB, H), dtype=torch.bfloat16, device=dev)
+        ib = torch.empty((TB, L.k), dtype=torch.int32, device=dev)
+        ub = []
+        for r in range(args.sets):
+            kw = kw_sets[r]
+            bdm.bdm_moe_block_forward(xb[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                      kw["w_down"], L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                      ws_down=kw["ws_down"], y=yb, topk_idx=ib, ws=wsb)
+            torch.cuda.synchronize()
+            ub.append(int(torch.unique(ib).numel()))
+        nrep = max(8, args.steps // 4)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(nrep):
+            r = i % args.sets
+            kw = kw_sets[r]
+            bdm.bdm_moe_block_forward(xb[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                      kw["w_down"], L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                      ws_down=kw["ws_down"], y=yb, ws=wsb)
+        stop.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / nrep
+        ubm = float(np.mean([ub[i % args.sets] for i in range(nrep)]))
+        nbytes = (ubm + 1) * EXPERT_BYTES
+        flops = TB * (L.k + 1) * 6.0 * H * L.I
+        multi[f"{nb}_blocks"] = {
+            "tokens": TB, "us": round(us, 2), "block_tokens_per_s": round(TB / (us * 1e-6), 1),
+            "unique_experts": round(ubm, 2), "bytes": int(nbytes),
+            "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_TFLOP_s": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac_of_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del xb, wsb, yb, ib
+
     u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
     moe_bytes = (u_mean + 1) * EXPERT_BYTES
     moe_gbs = moe_bytes / (moe_loop_us * 1e-6) / 1e9
@@ -306,6 +349,7 @@ def main():
         "head_unmask": {"us": round(head_us, 2), "gemm_us": round(gemm_us, 2),
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
+        "moe_layer_multiblock": multi,
         "head_verify_33_rows": {"us": round(verify_us, 2), "bytes": HEAD_BYTES,
                                 "GB_s": round(verify_gbs, 1),
                                 "frac_of_peak": round(verify_gbs / PEAK_HBM_GBS, 4)},

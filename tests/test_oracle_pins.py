@@ -132,6 +132,23 @@ def test_union_of_routed_experts_matches_page_simulation():
     assert 160.0 < np.mean(us) < 166.5, us
 
 
+@pytest.mark.parametrize("nblocks", [2, 4])
+def test_union_of_multiblock_batch_matches_closed_form(nblocks):
+    """Several 32-token blocks in one call: the union of routed experts grows
+    as the page's closed form for independent routing, generalised to T
+    tokens, 256 (1 - (248/256)^T): 222.4 at 64 tokens, 251.7 at 128."""
+    from oracle import counts
+    shape = synth.MoEShape(T=32 * nblocks, H=2048, E=256, I=512, k=8)
+    wr = synth.moe_router(shape, 0).numpy()
+    us = []
+    for b in range(1, 7):
+        x, _, _ = synth.moe_tokens(shape, 700 + b)
+        idx, _, _, _ = moe.route(synth.bf16_bits(x), wr, shape.k)
+        us.append(len(np.unique(idx)))
+    ref = counts.expected_union(256, 8, shape.T)
+    assert abs(np.mean(us) - ref) < 0.015 * ref, (us, ref)
+
+
 # --------------------------------------------------------------------------
 # Router / top-k
 # --------------------------------------------------------------------------
