@@ -40,7 +40,6 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
   char* topk_idx = take(sizeof(int32_t) * T * k);
   char* topk_w = take(sizeof(float) * T * k);
   char* topk_p = take(sizeof(float) * T * k);
-  char* ticket = take(sizeof(int32_t) * 4);
   char* info = take(sizeof(int32_t) * 4);
   char* slots = take(sizeof(int) * 4 * bdm::moe_max_slots(T, E, k, has_shared));
   char* pair_rows = take(sizeof(int32_t) * P);
@@ -51,7 +50,6 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
     m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
     m->topk_w = reinterpret_cast<float*>(topk_w);
     m->topk_p = reinterpret_cast<float*>(topk_p);
-    m->ticket = reinterpret_cast<int32_t*>(ticket);
     m->info = reinterpret_cast<int32_t*>(info);
     m->slots = reinterpret_cast<int4*>(slots);
     m->pair_rows = reinterpret_cast<int32_t*>(pair_rows);

@@ -37,7 +37,6 @@ struct MoeMeta {
   int32_t* topk_idx;    // [T][k]        picks, decreasing weight
   float* topk_w;        // [T][k]        their weights
   float* topk_p;        // [T][k]        first-pass probabilities (block coreset selector)
-  int32_t* ticket;      // [1]           completion ticket of the select step
   int32_t* info;        // [4]           [0] number of touched expert groups
   int4* slots;          // [E+1]         {expert, offset, count, 0} per touched group, then -1
   int32_t* pair_rows;   // [T*(k+1)]     (token, slot) rows grouped by expert

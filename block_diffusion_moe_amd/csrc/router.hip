@@ -39,17 +39,15 @@ constexpr int kRtMaxKs = 4;     // k-steps per wave: H <= kRouterParts * 4 * 4 *
 
 // Partial logits over one K-part: part[z][t][e] = sum_{h in part z} x[t][h] w[e][h].
 // The fp32 partials are summed (in part order) with the bias by the select
-// step.  Block (0,0,0) also clears the select step's completion ticket.
+// step.
 // NTT token tiles of 32 per workgroup share one load and split of the
 // router weights (NTT > 1 for many-block calls).
 template <int NTT>
 __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* __restrict__ x,
                                                               int T, int H,
                                                               const float* __restrict__ wr, int E,
-                                                              float* __restrict__ part,
-                                                              int32_t* __restrict__ ticket) {
+                                                              float* __restrict__ part) {
   __shared__ f32x4 red[2][kRtWaves][2][kWave];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *ticket = 0;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
@@ -264,7 +262,6 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
 }
 
 constexpr int kSelWaves = 4;       // tokens per select workgroup (one wave each)
-constexpr int kSelSplitMinT = 512; // from this many tokens: top-k kernel, then group_kernel
 constexpr int kSelOneWaves = 16;   // waves of the single-workgroup select (small blocks)
 constexpr int kSelOneMaxT = 16;    // largest block the single-workgroup select takes
 
@@ -394,26 +391,25 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
     for (int tt = tid; tt < T; tt += blockDim.x) pair_rows[tt] = tt * K1 + k;
 }
 
-// Top-k of every token, then the grouping of the picks by expert.
-// SINGLE: one workgroup of NW waves takes every token (wave w: token w),
-// keeps the picks in LDS and groups them itself.  Otherwise one wave per
-// token, NW tokens per workgroup, and the last workgroup to finish
-// (completion ticket) groups the picks read back from global memory.
-// FIRST (first pass of the block coreset selector): the picks, their
-// weights and their probabilities over all E (topk_p) only; no grouping.
-template <int PER, int NW, bool SINGLE, bool FIRST, bool GROUP = true>
+// Top-k of every token.  SINGLE (T <= 16): one workgroup of NW waves takes
+// every token (wave w: token w), keeps the picks in LDS and groups them
+// itself.  Otherwise one wave per token, NW tokens per workgroup, and
+// group_kernel follows (a completion ticket instead would need a
+// device-wide release in every workgroup, its L2 written back, which costs
+// more than the second launch).  FIRST (first pass of the block coreset
+// selector): the picks, their weights and their probabilities over all E
+// (topk_p) only.
+template <int PER, int NW, bool SINGLE, bool FIRST>
 __global__ __launch_bounds__(NW * 64) void select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ topk_p, int32_t* ticket, int4* __restrict__ slots,
-    int32_t* __restrict__ pair_rows, int32_t* __restrict__ info, int32_t* __restrict__ user_idx,
-    float* __restrict__ user_w) {
-  constexpr bool kGroups = !FIRST && GROUP;
+    float* __restrict__ topk_p, int4* __restrict__ slots, int32_t* __restrict__ pair_rows,
+    int32_t* __restrict__ info, int32_t* __restrict__ user_idx, float* __restrict__ user_w) {
+  constexpr bool kGroups = SINGLE && !FIRST;
   __shared__ int cnt[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
   __shared__ int eoff[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
   __shared__ int fill[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
   __shared__ int spick[SINGLE ? kSelOneMaxT * BDM_MAX_TOPK : 1];
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -436,24 +432,13 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
     }
   }
   if constexpr (kGroups) {
-    if (!SINGLE) {
-      // publish this workgroup's picks, then take a ticket
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
-      __syncthreads();
-      if (!s_last) return;
-      __threadfence();
-    }
-    group_picks<PER>(SINGLE ? spick : topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots,
-                     pair_rows, info);
+    __syncthreads();
+    group_picks<PER>(spick, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
   }
 }
 
-// The grouping on its own (many-block calls): one workgroup after the
-// top-k kernel.  With hundreds of select workgroups, the device-wide
-// release each would need before a completion ticket (its L2 written back)
-// costs more than a second launch.
+// The grouping after a multi-workgroup top-k (or coreset) kernel: one
+// workgroup of 1024 threads.
 template <int PER>
 __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ topk_idx, int T,
                                                      int E, int k, int has_shared,
@@ -580,15 +565,15 @@ __device__ __forceinline__ void reroute_pick(const float (&v)[PER], int fe, cons
 //   re-route: each token's top-min(k, |kept|) over the kept experts (the
 //             others at -inf), weights as in the plain routing; the rest of
 //             its k slots hold -1 and weight 0.
-// Then the grouping, by the block's own workgroup when there is one block,
-// else by the last workgroup to finish (completion ticket).
-template <int PER>
+// Then the grouping: by the block's own workgroup when there is one block
+// (GROUP), else by group_kernel launched after this kernel.
+template <int PER, bool GROUP>
 __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, float top_p, int B, int has_shared, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, const float* __restrict__ topk_p, int32_t* ticket,
-    int4* __restrict__ slots, int32_t* __restrict__ pair_rows, int32_t* __restrict__ info,
-    int32_t* __restrict__ user_idx, float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
+    float* __restrict__ topk_w, const float* __restrict__ topk_p, int4* __restrict__ slots,
+    int32_t* __restrict__ pair_rows, int32_t* __restrict__ info, int32_t* __restrict__ user_idx,
+    float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
   constexpr int kParts = 4;                     // partial sums per expert mass
   __shared__ int cnt[BDM_MAX_EXPERTS + 1];
   __shared__ int eoff[BDM_MAX_EXPERTS + 1];
@@ -600,7 +585,7 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
   __shared__ __align__(16) int sidx[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
   __shared__ __align__(16) float sp[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
   __shared__ float sw[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
-  __shared__ int s_ntouch, s_nkeep, s_last;
+  __shared__ int s_ntouch, s_nkeep;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -756,18 +741,10 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
       }
     }
   }
-  if (gridDim.x == 1) {
+  if constexpr (GROUP) {                 // one block: its workgroup groups the picks
     __syncthreads();
     group_picks<PER>(sidx, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
-    return;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ticket, 1) == static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  group_picks<PER>(topk_idx, T, E, k, has_shared, cnt, eoff, fill, slots, pair_rows, info);
 }
 
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
@@ -777,11 +754,10 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
   if (T >= kRtWideMinT) {
     const dim3 grid((E + 15) / 16, (T + 32 * kRtWideTiles - 1) / (32 * kRtWideTiles),
                     kRouterParts);
-    router_kernel<kRtWideTiles><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits,
-                                                               meta.ticket);
+    router_kernel<kRtWideTiles><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits);
   } else {
     const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
-    router_kernel<1><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, meta.ticket);
+    router_kernel<1><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits);
   }
   const int nsel = (T + kSelWaves - 1) / kSelWaves;
   const bool core = top_p > 0.0f;
@@ -790,25 +766,30 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
   if (core) {                                                                                  \
     select_kernel<P, kSelWaves, false, true><<<nsel, kSelWaves * 64, 0, s>>>(                  \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
-    coreset_kernel<P><<<ncs, kCsWaves * 64, 0, s>>>(                                           \
-        meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,           \
-        meta.topk_w, meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info,          \
-        user_idx, user_w, n_kept);                                                             \
+        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+    if (ncs > 1) {                                                                             \
+      coreset_kernel<P, false><<<ncs, kCsWaves * 64, 0, s>>>(                                  \
+          meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,         \
+          meta.topk_w, meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w,   \
+          n_kept);                                                                             \
+      group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,       \
+                                         meta.pair_rows, meta.info);                           \
+    } else {                                                                                   \
+      coreset_kernel<P, true><<<1, kCsWaves * 64, 0, s>>>(                                     \
+          meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,         \
+          meta.topk_w, meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w,   \
+          n_kept);                                                                             \
+    }                                                                                          \
   } else if (T <= kSelOneMaxT) {                                                               \
     select_kernel<P, kSelOneWaves, true, false><<<1, kSelOneWaves * 64, 0, s>>>(               \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
-  } else if (T >= kSelSplitMinT) {                                                             \
-    select_kernel<P, kSelWaves, false, false, false><<<nsel, kSelWaves * 64, 0, s>>>(          \
-        meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
-    group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,         \
-                                       meta.pair_rows, meta.info);                             \
+        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
   } else {                                                                                     \
     select_kernel<P, kSelWaves, false, false><<<nsel, kSelWaves * 64, 0, s>>>(                 \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.ticket, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);    \
+        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+    group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,         \
+                                       meta.pair_rows, meta.info);                             \
   }
   if (E <= 256) {
     BDM_SELECT(4)

@@ -124,6 +124,20 @@ def test_coreset_eight_blocks_sampled(bdm):
     compare(out, inp, h, r, tokens=tokens)
 
 
+@pytest.mark.parametrize("T", [1024, 2048])
+def test_coreset_many_blocks_sampled(bdm, T):
+    """32 and 64 blocks in one call (the per-block selection, then the
+    grouping as its own kernel): every block's kept set, the routing of every
+    token, the outputs of a seeded sample of 24 tokens."""
+    say(f"case coreset {T // 32} blocks")
+    s = synth.MoEShape(T=T, H=2048, E=256, I=512, k=8)
+    inp = synth.moe_inputs(s, seed=1, block_seed=T, device=DEV, with_residual=True)
+    out = run_gpu(bdm, inp, 0.9, 32)
+    h, r = oracle_routing(inp, 0.9, 32)
+    tokens = np.sort(np.random.default_rng(T).choice(T, 24, replace=False))
+    compare(out, inp, h, r, tokens=tokens)
+
+
 def test_coreset_ragged_last_block(bdm):
     say("case coreset ragged last block (T=40, block 16)")
     s = synth.MoEShape(T=40, H=512, E=64, I=128, k=4)
