@@ -289,9 +289,15 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
 #pragma unroll
     for (int s = 0; s < KSW; ++s) b[s] = ld16_stream(f.p + (s0 + s) * f.step);
   };
-  u32x4 ba[KSW], bb[KSW];
-  load(G0, ba);
-  load(G0 + 1, bb);
+  // NB groups of weights in flight (ping-pong, or three buffers when the
+  // 32-row tile leaves the registers for it)
+#ifndef BDM_HEAD_BUFS
+#define BDM_HEAD_BUFS 2
+#endif
+  constexpr int NB = MT == 2 ? BDM_HEAD_BUFS : 2;
+  u32x4 bufs[NB][KSW];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) load(G0 + u, bufs[u]);
   // this wave's slice of the hidden rows (rows >= ntok are zero)
   u32x4 a[MT][KSW];
 #pragma unroll
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     for (int s = 0; s < KSW; ++s)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
-    load(G0 + j + 2, b);
+    load(G0 + j + NB, b);
     float* pp = &part[j & 1][wave][0][0][0];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -369,11 +375,13 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     }
   };
   int j = 0;
-  for (; j + 1 < n; j += 2) {
-    step(j, ba);
-    step(j + 1, bb);
+  for (; j + NB - 1 < n; j += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) step(j + u, bufs[u]);
   }
-  if (j < n) step(j, ba);
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (j + u < n) step(j + u, bufs[u]);
 
   // the 16 columns of a token sit in one DPP row; each token in one wave
 #pragma unroll
