@@ -340,13 +340,15 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
     partial(bg, wg, q + 1, &part[0][buf][wave][0][0][0]);
     partial(bu, wu, q + 1, &part[1][buf][wave][0][0][0]);
     __syncthreads();
-    // fold: 64 tokens x 16 columns, two per thread
+    // fold: 64 tokens x 16 columns, two per thread; thread o reads element
+    // (mt, i, lane ln) of every wave's partials, consecutive threads
+    // consecutive lanes (no bank conflicts): token 16 mt + 4 (ln / 16) + i,
+    // column ln % 16
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int o = tid + f * kGuWaves * kWave;
-      const int r = o >> 4, cc = o & 15;
-      const int mt = r >> 4, rr = r & 15;
-      const int ln = 16 * (rr >> 2) + cc, i = rr & 3;
+      const int ln = o & 63, i = (o >> 6) & 3, mt = o >> 8;
+      const int r = 16 * mt + 4 * (ln >> 4) + i, cc = ln & 15;
       float gs = part[0][buf][0][mt][i][ln], us = part[1][buf][0][mt][i][ln];
 #pragma unroll
       for (int w = 1; w < kGuWaves; ++w) {
@@ -420,8 +422,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
   }
   if (tid < 16 * MT) srow[tid] = prow;
   __syncthreads();
-  // stage the activation rows: chunk (r, s, gg) of 8 values -> tile
-  // (r / 16, s), lane (r % 16) + 16 gg; all loads first
+  // stage the activation rows: chunk ch -> tile (mt, s) = ch / 64, lane
+  // l = ch % 64 holding row 16 mt + l % 16, values 8 (l / 16) .. +7 of
+  // k-step s (consecutive threads write consecutive 16 bytes: no bank
+  // conflicts); all loads of a batch first
   constexpr int NCH = 16 * MT * KSMAX * 4 / (NW * kWave);
   static_assert(NCH * NW * kWave == 16 * MT * KSMAX * 4, "whole chunks per thread");
   constexpr int NB = NCH >= 4 ? 4 : NCH;           // chunks per batch
@@ -432,14 +436,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int ch = tid + (u0 + u) * NW * kWave;
-      const int gg = ch & 3, s = (ch >> 2) % KSMAX, r = (ch >> 2) / KSMAX;
-      v[u] = ld16(act + static_cast<size_t>(srow[r]) * I + (s < KS ? s : 0) * 32 + gg * 8);
+      const int l = ch & 63, s = (ch >> 6) % KSMAX, r = 16 * ((ch >> 6) / KSMAX) + (l & 15);
+      v[u] = ld16(act + static_cast<size_t>(srow[r]) * I + (s < KS ? s : 0) * 32 + (l >> 4) * 8);
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int ch = tid + (u0 + u) * NW * kWave;
-      const int gg = ch & 3, s = (ch >> 2) % KSMAX, r = (ch >> 2) / KSMAX;
-      at[r >> 4][s][(r & 15) + 16 * gg] = (r < m && s < KS) ? v[u] : u32x4{0u, 0u, 0u, 0u};
+      const int l = ch & 63, s = (ch >> 6) % KSMAX, r = 16 * ((ch >> 6) / KSMAX) + (l & 15);
+      at[r >> 4][s][l] = (r < m && s < KS) ? v[u] : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();

@@ -245,8 +245,9 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 // of 16 rows: 32 or 64 rows per pass over the weights) held in its
 // registers for the whole run.  The 8 partial products of a group meet in
 // LDS and are summed in wave order, and each (token, column) of the group is
-// folded into the online-softmax state of one lane (tokens 32f + 4w +
-// lane/16 for f < MT/2, column lane%16).  The workgroup takes one contiguous
+// folded into the online-softmax state of one lane (for f < MT/2: token
+// 16 (2f + w/4) + 4 (lane/16) + w%4, column lane%16, so the 64 lanes of a
+// wave read 64 consecutive partials).  The workgroup takes one contiguous
 // run of groups; its waves move in step (one barrier per group), and the
 // loads of the next two groups are in flight while a group is reduced.
 // Loads past the run read the hidden rows instead (valid, L2-resident,
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   int mycand[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int ot = 32 * f + 4 * wave + g;
+    const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
     st[f] = softstat_empty();
     vs[f] = vstat_empty();
     mycand[f] = -1;
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     const bool live = v < V && v + voff != mask_id;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int ot = 32 * f + 4 * wave + g;
+      const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
       const int omt = ot >> 4, oq = (ot >> 2) & 3, oi = ot & 3;
       float l = 0.0f;
 #pragma unroll
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   // the 16 columns of a token sit in one DPP row; each token in one wave
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int ot = 32 * f + 4 * wave + g;
+    const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
     const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
     if constexpr (VERIFY) {
       const VStat r = row_merge_vstat(vs[f]);

@@ -100,14 +100,15 @@ def test_multiblock_rows_equal_single_block_calls(bdm, T, zipf):
 @LAYOUTS
 @pytest.mark.parametrize("shape", [(65, 256, 16, 64, 2), (200, 256, 4, 64, 2),
                                    (130, 512, 2, 32, 1), (300, 128, 8, 96, 3),
-                                   (300, 512, 8, 96, 3), (260, 256, 16, 32, 2),
-                                   (400, 1024, 6, 128, 2)],
+                                   (450, 512, 8, 96, 3), (400, 256, 16, 32, 2),
+                                   (400, 1024, 6, 128, 2), (390, 2048, 4, 64, 1)],
                          ids=lambda s: "T%d_H%d_E%d_I%d_k%d" % s)
 def test_multiblock_small_full(bdm, shape, layout):
     """Small shapes whose groups exceed one work item (shared 65 = 64 + 1;
     routed groups of ~100-130 tokens), on both the few-token kernels and
-    (T >= 256, H a multiple of 256) the many-token ones, with partial column
-    runs (I = 96) and guarded k-steps: every output against the oracle."""
+    (T >= 384, H of 256, 512, 1024 or 2048) the many-token ones, with partial
+    column runs (I = 96) and guarded k-steps: every output against the
+    oracle."""
     T, H, E, I, k = shape
     say(f"case multiblock small T={T} H={H} E={E} I={I} k={k} layout={layout}")
     s = synth.MoEShape(T=T, H=H, E=E, I=I, k=k)
