@@ -146,6 +146,12 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   Pointers 16-byte aligned (workspace 256-byte aligned).  NaN inputs give
  *   undefined values, never an out-of-bounds access.
  * No other aliasing is allowed.
+ *
+ * Several blocks in one call (multi-block batching): stack the blocks' rows
+ * in x (T = 32 x blocks, up to 64 blocks).  Tokens never interact, so each
+ * row of y, topk_idx and topk_w is bit for bit what a call with that row's
+ * block alone gives; the call reads each touched expert's weights once per
+ * 64 of its tokens instead of once per block.
  */
 BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           const float* w_router, const float* router_bias, int E, int k,
