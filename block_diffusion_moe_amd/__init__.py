@@ -7,7 +7,8 @@ Build the library with ``python -m block_diffusion_moe_amd.build``.
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
 from .binding import (BDM_LAYOUT_MFMA_TILES, BDM_LAYOUT_ROW_MAJOR, BDM_MASK_ID_CLOVER,
-                      BDM_THRESHOLD_DEFAULT, BDM_VERIFY_EXACT, BDM_VERIFY_THRESHOLD, EXPORTS, LIB_PATH, BdmError, MoeLayerC, Packed,
+                      BDM_THRESHOLD_DEFAULT, BDM_VERIFY_EXACT, BDM_VERIFY_THRESHOLD, EXPORTS,
+                      LIB_PATH, BdmError, MoeLayerC, MoeStack, Packed,
                       bdm_denoise_block, bdm_denoise_workspace_bytes,
                       bdm_head_stat_parts, bdm_head_verify_workspace_bytes,
                       bdm_head_workspace_bytes, bdm_lm_head_stats, bdm_lm_head_unmask,
@@ -17,7 +18,8 @@ from .binding import (BDM_LAYOUT_MFMA_TILES, BDM_LAYOUT_ROW_MAJOR, BDM_MASK_ID_C
 
 __all__ = [
     "BDM_LAYOUT_MFMA_TILES", "BDM_LAYOUT_ROW_MAJOR", "BDM_MASK_ID_CLOVER",
-    "BDM_THRESHOLD_DEFAULT", "BDM_VERIFY_EXACT", "BDM_VERIFY_THRESHOLD", "EXPORTS", "LIB_PATH", "BdmError", "MoeLayerC", "Packed",
+    "BDM_THRESHOLD_DEFAULT", "BDM_VERIFY_EXACT", "BDM_VERIFY_THRESHOLD", "EXPORTS",
+    "LIB_PATH", "BdmError", "MoeLayerC", "MoeStack", "Packed",
     "bdm_denoise_block", "bdm_denoise_workspace_bytes",
     "bdm_head_stat_parts", "bdm_head_verify_workspace_bytes", "bdm_head_workspace_bytes",
     "bdm_lm_head_stats", "bdm_lm_head_verify",

@@ -268,53 +268,74 @@ def bdm_denoise_workspace_bytes(T, H, I, E, k, has_shared=True) -> int:
     return n.value
 
 
+class MoeStack:
+    """The layers of a pre-norm expert stack checked and marshalled once into
+    the host array of bdm_moe_layer structs bdm_denoise_block takes (the
+    tensors stay referenced here).  `layers`: list of dicts with w_router,
+    router_bias (optional), w_gate, w_up, w_down, ws_gate, ws_up, ws_down
+    (tensors, or all expert matrices `Packed`)."""
+
+    def __init__(self, layers):
+        if not layers:
+            raise ValueError("at least one layer")
+        self.layers = list(layers)
+        E, I, H = self.layers[0]["w_gate"].shape
+        dev = self.layers[0]["w_router"].device
+        self.E, self.I, self.H = E, I, H
+        self.has_shared = self.layers[0].get("ws_gate") is not None
+        self.arr = (MoeLayerC * len(self.layers))()
+        mats = []
+        for i, lw in enumerate(self.layers):
+            _check(lw["w_router"], "w_router", torch.float32, (E, H), dev)
+            _check(lw.get("router_bias"), "router_bias", torch.float32, (E,), dev)
+            _check(lw["w_gate"], "w_gate", torch.bfloat16, (E, I, H), dev)
+            _check(lw["w_up"], "w_up", torch.bfloat16, (E, I, H), dev)
+            _check(lw["w_down"], "w_down", torch.bfloat16, (E, H, I), dev)
+            for nm, shp in (("ws_gate", (I, H)), ("ws_up", (I, H)), ("ws_down", (H, I))):
+                _check(lw.get(nm), nm, torch.bfloat16, shp, dev)
+            for f, _ in MoeLayerC._fields_:
+                ptr = _ptr(lw.get(f))
+                setattr(self.arr[i], f, None if ptr is None else ptr.value)
+            mats += [lw[n] for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+                     if lw.get(n) is not None]
+        packed = [isinstance(t, Packed) for t in mats]
+        if any(packed) and not all(packed):
+            raise ValueError("expert weights must be all row-major or all packed")
+        self.packed = all(packed)
+        self.device = dev
+
+    def __len__(self):
+        return len(self.layers)
+
+
 def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
                       threshold: float = 0.95, max_steps=None, renorm: bool = True, ws=None,
                       stream=None):
     """The denoise loop over the block `tokens` (int32 device [T], updated in
-    place).  `layers`: list of dicts with w_router, router_bias (optional),
-    w_gate, w_up, w_down, ws_gate, ws_up, ws_down (tensors, or all expert
-    matrices and w_head `Packed`).  Returns (steps, commits per step)."""
+    place).  `layers`: a MoeStack, or the list of layer dicts it takes
+    (marshalled on every call then).  Returns (steps, commits per step)."""
     T = tokens.shape[0]
     V, H = w_embed.shape
     dev = tokens.device
+    stack = layers if isinstance(layers, MoeStack) else MoeStack(layers)
     _check(tokens, "tokens", torch.int32, (T,))
     _check(w_embed, "w_embed", torch.bfloat16, (V, H), dev)
     _check(w_head, "w_head", torch.bfloat16, (V, H), dev)
-    if not layers:
-        raise ValueError("at least one layer")
-    E, I, _ = layers[0]["w_gate"].shape
-    has_shared = layers[0].get("ws_gate") is not None
-    arr = (MoeLayerC * len(layers))()
-    mats = []
-    for i, lw in enumerate(layers):
-        _check(lw["w_router"], "w_router", torch.float32, (E, H), dev)
-        _check(lw.get("router_bias"), "router_bias", torch.float32, (E,), dev)
-        _check(lw["w_gate"], "w_gate", torch.bfloat16, (E, I, H), dev)
-        _check(lw["w_up"], "w_up", torch.bfloat16, (E, I, H), dev)
-        _check(lw["w_down"], "w_down", torch.bfloat16, (E, H, I), dev)
-        for nm, shp in (("ws_gate", (I, H)), ("ws_up", (I, H)), ("ws_down", (H, I))):
-            _check(lw.get(nm), nm, torch.bfloat16, shp, dev)
-        for f, _ in MoeLayerC._fields_:
-            ptr = _ptr(lw.get(f))
-            setattr(arr[i], f, None if ptr is None else ptr.value)
-        mats += [lw[n] for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
-                 if lw.get(n) is not None]
-    mats.append(w_head)
-    packed = [isinstance(t, Packed) for t in mats]
-    if any(packed) and not all(packed):
+    if stack.H != H or stack.device != dev:
+        raise ValueError("the stack's hidden size or device differs from w_embed's")
+    if isinstance(w_head, Packed) != stack.packed:
         raise ValueError("expert and head weights must be all row-major or all packed")
-    layout = BDM_LAYOUT_MFMA_TILES if all(packed) else BDM_LAYOUT_ROW_MAJOR
-    need = bdm_denoise_workspace_bytes(T, H, I, E, k, has_shared)
+    layout = BDM_LAYOUT_MFMA_TILES if stack.packed else BDM_LAYOUT_ROW_MAJOR
+    need = bdm_denoise_workspace_bytes(T, H, stack.I, stack.E, k, stack.has_shared)
     if ws is None:
         ws = workspace(need, dev)
     limit = T if max_steps is None else int(max_steps)
     steps = _c_int(0)
     commits = (ctypes.c_int32 * max(1, limit))()
     _raise("bdm_denoise_block", load().bdm_denoise_block(
-        _ptr(tokens), T, _ptr(w_embed), V, H, arr, len(layers), E, int(k), I, int(renorm),
-        _ptr(w_head), layout, int(mask_id), float(threshold), limit, ctypes.byref(steps),
-        commits, _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(tokens), T, _ptr(w_embed), V, H, stack.arr, len(stack), stack.E, int(k), stack.I,
+        int(renorm), _ptr(w_head), layout, int(mask_id), float(threshold), limit,
+        ctypes.byref(steps), commits, _ptr(ws), ws.numel(), _stream(stream)))
     return steps.value, [int(commits[i]) for i in range(steps.value)]
 
 

@@ -133,9 +133,10 @@ def test_denoise_clover_stack_invariants_and_first_step(bdm):
     torch.cuda.synchronize()
     assert steps == 1 and commits == [int(nc.item())]
     assert torch.equal(one, ref)
-    # the whole loop
+    # the whole loop (layers marshalled once: the same results as the list)
     tok = tok0.clone()
-    steps, commits = bdm.bdm_denoise_block(tok, emb, players, w_head, s.k, HS.mask_id, 0.95)
+    steps, commits = bdm.bdm_denoise_block(tok, emb, bdm.MoeStack(players), w_head, s.k,
+                                           HS.mask_id, 0.95)
     torch.cuda.synchronize()
     say(f"  {steps} steps, commits {commits}")
     masked0 = int((tok0 == HS.mask_id).sum())
