@@ -101,7 +101,8 @@ def test_multiblock_rows_equal_single_block_calls(bdm, T, zipf):
 @pytest.mark.parametrize("shape", [(65, 256, 16, 64, 2), (200, 256, 4, 64, 2),
                                    (130, 512, 2, 32, 1), (300, 128, 8, 96, 3),
                                    (450, 512, 8, 96, 3), (400, 256, 16, 32, 2),
-                                   (400, 1024, 6, 128, 2), (390, 2048, 4, 64, 1)],
+                                   (400, 1024, 6, 128, 2), (390, 2048, 4, 64, 1),
+                                   (400, 256, 512, 1024, 4), (512, 512, 1024, 64, 8)],
                          ids=lambda s: "T%d_H%d_E%d_I%d_k%d" % s)
 def test_multiblock_small_full(bdm, shape, layout):
     """Small shapes whose groups exceed one work item (shared 65 = 64 + 1;
