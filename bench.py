@@ -165,6 +165,7 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
     norm_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     moe_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     gemm_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -179,6 +180,23 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     ms_step_plain = start.elapsed_time(stop) / args.steps
+
+    # the same steps replayed from HIP graphs (one captured step per weight
+    # set; no call in the step allocates, synchronises or records a memset)
+    graphs = []
+    for r in range(args.sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        graphs[i % args.sets].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_graph = start.elapsed_time(stop) / args.steps
+    del graphs
 
     # the head GEMM kernel alone: the same launches back to back over the
     # rotated sets, two events on the stream they run on around all of them
@@ -302,11 +320,14 @@ def main():
     value = T / (ms_step_plain * 1e-3)
 
     gemm_gbs = HEAD_BYTES / (gemm_loop_us * 1e-6) / 1e9
+    stream_gbs = stream_read_gbs(torch, dev, max(8, args.steps // 10))
     roof = {"bound": "hbm", "kernel": "head_coop_kernel (bdm_lm_head_stats)",
             "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": head_traffic(),
             "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_loop_us, 2),
-            "launches_timed": args.steps, "us_per_launch_in_step": round(gemm_us, 2)}
+            "launches_timed": args.steps, "us_per_launch_in_step": round(gemm_us, 2),
+            "measured_stream_read_GB_s": round(stream_gbs, 1),
+            "frac_of_measured_stream_read": round(gemm_gbs / stream_gbs, 4)}
 
     stack = None
     if args.stack_layers > 0:
@@ -340,7 +361,8 @@ def main():
         "moe_layer": {"us": round(moe_loop_us, 2), "us_in_step": round(moe_us, 2),
                       "block_tokens_per_s": round(T / (moe_loop_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
-                      "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4)},
+                      "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4),
+                      "frac_of_measured_stream_read": round(moe_gbs / stream_gbs, 4)},
         "moe_layer_coreset_top_p_0.9": {
             "us": round(cs_us, 2), "block_tokens_per_s": round(T / (cs_us * 1e-6), 1),
             "kept_experts": round(kept_mean, 2), "bytes": int(cs_bytes),
@@ -356,6 +378,9 @@ def main():
         "denoise_step_stack": stack,
         "rmsnorm_us": round(norm_us, 2),
         "ms_per_step_with_events": round(ms_step, 4),
+        "ms_per_step_event_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4)
+                                          for q in (10, 50, 90)],
+        "ms_per_step_graph_replay": round(ms_step_graph, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -438,6 +463,39 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
     del stack, layers, emb, w_head
     torch.cuda.empty_cache()
     return out
+
+
+def stream_read_gbs(torch, dev, reps):
+    """Read bandwidth of a plain 1 GiB stream with the weight kernels' access
+    (16-byte non-temporal loads, libbdmcal.so): the box's achievable ceiling
+    for this path, measured beside it."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                   "block_diffusion_moe_amd", "libbdmcal.so"))
+    lib.bdmcal_stream_read.restype = ctypes.c_int
+    lib.bdmcal_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+    nbytes, blocks = 1 << 30, 1024
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch(b):
+        if lib.bdmcal_stream_read(b.data_ptr(), nbytes, out.data_ptr(), blocks, st) != 0:
+            raise RuntimeError("bdmcal_stream_read failed")
+    for b in bufs:
+        launch(b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        launch(bufs[i % 2])
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+    del bufs, out
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def head_traffic():

@@ -1,4 +1,6 @@
-// Calibration copy for HBM traffic counters (not part of the bdmoe ABI).
+// Calibration kernels (not part of the bdmoe ABI): a copy for the HBM
+// traffic counters and a read-only stream that measures the box's
+// achievable read bandwidth for the weight-streaming access pattern.
 //
 // bdmcal_stream_copy copies `bytes` bytes (a multiple of 16 KiB) with the
 // access pattern of the weight-streaming kernels: every lane reads 16 bytes
@@ -27,7 +29,72 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(const u32x4* __re
   for (int i = 0; i < kPerThread; ++i) dst[base + i * kThreads] = v[i];
 }
 
+// bdmcal_stream_read reads `bytes` bytes (a multiple of 16) once: a
+// grid-stride loop over 32 KiB chunks (a workgroup reads one contiguous
+// chunk per step, a wave 1 KiB per load instruction), every lane keeping
+// two batches of 8 non-temporal 16-byte loads in flight (ping-pong) and
+// folding them into an XOR (written per thread to `out`, so the loads cannot
+// be dropped).
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                                   long n16,
+                                                                   uint32_t* __restrict__ out) {
+  constexpr long kBatch = static_cast<long>(kReadThreads) * kReadUnroll;   // 16-byte units
+  const long stride = static_cast<long>(gridDim.x) * kBatch;
+  long i = static_cast<long>(blockIdx.x) * kBatch + threadIdx.x;
+  uint32_t acc = 0u;
+  u32x4 a[kReadUnroll], b[kReadUnroll];
+  auto full = [&](long base) { return base + (kReadUnroll - 1) * kReadThreads < n16; };
+  auto load = [&](long base, u32x4(&v)[kReadUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(src + base + u * kReadThreads);
+  };
+  auto fold = [&](const u32x4(&v)[kReadUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  };
+  if (full(i)) {
+    load(i, a);
+    for (;;) {
+      const bool nb = full(i + stride);
+      if (nb) load(i + stride, b);
+      fold(a);
+      i += stride;
+      if (!nb) break;
+      const bool na = full(i + stride);
+      if (na) load(i + stride, a);
+      fold(b);
+      i += stride;
+      if (!na) break;
+    }
+  }
+  // the rest of a partial chunk (only past the last full one)
+  for (; i < n16; i += kReadThreads) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[static_cast<long>(blockIdx.x) * kReadThreads + threadIdx.x] = acc;
+}
+
 }  // namespace bdmcal
+
+extern "C" __attribute__((visibility("default"))) int bdmcal_stream_read(const void* src,
+                                                                        long bytes,
+                                                                        uint32_t* out,
+                                                                        int blocks,
+                                                                        void* stream) {
+  using namespace bdmcal;
+  // out: blocks * 256 entries
+  if (!src || !out || bytes <= 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65535) return -1;
+  if (reinterpret_cast<uintptr_t>(src) & 15) return -1;
+  (void)hipGetLastError();
+  stream_read_kernel<<<blocks, kReadThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(src), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" __attribute__((visibility("default"))) int bdmcal_stream_copy(const void* src,
                                                                         void* dst, long bytes,

@@ -178,8 +178,9 @@ def test_two_phase_head_validation(lib):
 
 
 def test_calibration_library_exports():
-    """The counter-calibration copy kernel lives in its own library and
-    rejects sizes it cannot copy exactly (checks only, no launch)."""
+    """The calibration kernels (counter-calibration copy, read-bandwidth
+    probe) live in their own library and reject arguments they cannot serve
+    (checks only, no launch)."""
     import ctypes
     import os
     path = os.path.join(ROOT, "block_diffusion_moe_amd", "libbdmcal.so")
@@ -192,6 +193,13 @@ def test_calibration_library_exports():
     assert f(None, _fake(1 << 20), 16384, None) == -1
     assert f(_fake(1 << 20), _fake(1 << 21), 16000, None) == -1
     assert f(_fake(1 << 20), _fake(1 << 20), 16384, None) == -1
+    r = cal.bdmcal_stream_read
+    r.restype = ctypes.c_int
+    r.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert r(None, 1 << 20, _fake(1 << 21), 4, None) == -1
+    assert r(_fake(1 << 20), 1000, _fake(1 << 21), 4, None) == -1
+    assert r(_fake(1 << 20), 1 << 20, None, 4, None) == -1
+    assert r(_fake(1 << 20), 1 << 20, _fake(1 << 21), 0, None) == -1
 
 
 def test_coreset_validation(lib):
