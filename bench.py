@@ -546,12 +546,31 @@ def cpu_baseline(blocks, min_s=10.0, max_blocks=12):
         dt += time.perf_counter() - t0
         ntok += xb.shape[0]
         nblk += 1
+    # the same step on one host thread (one block), phases timed apart
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        h, xb, wh, tok = host[0]
+        with threadpool_limits(limits=1, user_api="blas"):
+            t0 = time.perf_counter()
+            xn = onorm.rmsnorm(xb, 1e-6)
+            y = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                               h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)["y"]
+            t1 = time.perf_counter()
+            ohead.head_unmask(y, wh, tok, synth.HEAD.mask_id, 0.95)
+            t2 = time.perf_counter()
+        single = {"value": round(xb.shape[0] / (t2 - t0), 4), "unit": "block-tokens/s",
+                  "cores": 1, "moe_layer_s": round(t1 - t0, 3), "head_s": round(t2 - t1, 3),
+                  "sample": "one 32-slot block, BLAS limited to one thread"}
+    except ImportError:
+        pass
     return {"value": round(ntok / dt, 4), "unit": "block-tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{nblk} whole 32-slot blocks ({ntok} tokens, cycling over "
                       f"{min(nblk, len(blocks))} weight sets) through RMSNorm + MoE layer + "
                       f"head/unmask (numpy float64 oracle), {dt:.1f} s; weights copied to host "
-                      f"before the timed region"}
+                      f"before the timed region",
+            "single_thread": single}
 
 
 def _blas_threads():
