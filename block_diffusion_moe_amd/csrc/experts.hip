@@ -36,7 +36,11 @@ namespace bdm {
 constexpr int kGuCols = 16;     // I columns per gate/up work item
 constexpr int kGuWaves = 8;     // waves splitting K in gate/up
 constexpr int kGuMt = 2;        // 16-token tiles multiplied per pass
-constexpr int kDnRows = 64;     // H rows per down work item (4 waves x 16)
+#ifndef BDM_DN_WAVES
+#define BDM_DN_WAVES 4
+#endif
+constexpr int kDnWaves = BDM_DN_WAVES;  // waves per down work item, 16 rows of H each
+constexpr int kDnRows = 16 * kDnWaves;  // H rows per down work item
 
 // A slot names a real group: expert id in [0, E] (E only with a shared
 // expert), 1 <= count, and its pair rows inside [0, P).
@@ -170,12 +174,12 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
 // work item = (touched group, 64 rows of H); each wave owns 16 output rows
 // and the whole K = I (KS k-steps, KS <= KSMAX)
 template <int KSMAX, bool GUARD>
-__global__ __launch_bounds__(256, 2) void down_kernel(
+__global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
     const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
     const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
     const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
     float* __restrict__ ypair) {
-  const int tiles = H / kDnRows;
+  const int tiles = (H + kDnRows - 1) / kDnRows;
   const int4 slot = slots[blockIdx.x / tiles];
   const int e = slot.x;
   const int off = slot.y;
@@ -186,6 +190,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(
   const int c = lane & 15;
   const int g = lane >> 4;
   const int n0 = (blockIdx.x % tiles) * kDnRows + wave * 16;
+  if (n0 >= H) return;                          // past H in the last tile (no barriers here)
   const int KS = I / 32;
 
   // rows of the first token tile (A operand row c; output rows 4g..4g+3)
@@ -568,7 +573,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
   // upper bound on the slots; workgroups past the actual list exit at once
   const int groups = moe_max_slots(T, E, k, has_shared);
   const int P = T * (k + 1);
-  const dim3 gu(groups * (I / kGuCols)), dn(groups * (H / kDnRows));
+  const dim3 gu(groups * (I / kGuCols)), dn(groups * ((H + kDnRows - 1) / kDnRows));
   const int KS = H / 32;
   const int KI = I / 32;
 #ifndef BDM_WIDE_MIN_T
@@ -606,13 +611,13 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                                                        meta.act);
   }
   if (KI == 16) {
-    down_kernel<16, false><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<16, false><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                               meta.pair_rows, meta.ypair);
   } else if (KI < 16) {
-    down_kernel<16, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<16, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   } else {
-    down_kernel<32, true><<<dn, 256, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<32, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   }
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
