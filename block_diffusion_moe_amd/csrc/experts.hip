@@ -256,9 +256,10 @@ constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per
 // gate/up: work item = (slot, kWideGuGroups column groups).  The 8 waves
 // split K = H (KSW k-steps each) and hold their K-slice of the slot's token
 // rows in registers; the weights stream one 16-row group at a time,
-// alternating gate and up, each load issued two steps ahead (the gate and
-// up buffers ping-pong).  The 8 partial products of a group meet in LDS and
-// are summed in wave order; silu(g) * u is stored as bf16.
+// alternating gate and up, and each k-step of a matrix's next group is
+// requested as soon as the current one has been multiplied.  The 8 partial
+// products of a group meet in LDS (double-buffered, one barrier per group)
+// and are summed in wave order; silu(g) * u is stored as bf16.
 template <int KSW>
 __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
     const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
@@ -371,12 +372,13 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
 // down: work item = (slot, 8 waves x kWideDnGroups groups of 16 rows of H).
 // The slot's activation rows are staged once in LDS in MFMA operand order
 // (tile (mt, s) = 64 lanes x 16 B, conflict-free reads); every wave then
-// owns its own 16-row groups over the whole K = I, their weights loaded
-// two groups ahead, and stores fp32 results per (token, slot) row.
-template <int KSMAX>
+// owns its own 16-row groups over the whole K = I, each k-step of its next
+// group requested as soon as the current one has been multiplied, and
+// stores fp32 results per (token, slot) row.
 #ifndef BDM_DN_WIDE_WAVES_PER_EU
 #define BDM_DN_WIDE_WAVES_PER_EU 4     // two workgroups per CU (<= 128 registers)
 #endif
+template <int KSMAX>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
     BDM_DN_WIDE_WAVES_PER_EU, BDM_DN_WIDE_WAVES_PER_EU))) void down_wide_kernel(
     const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
