@@ -451,11 +451,40 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
         gtimes.append(e0.elapsed_time(e1))
     ms = 1e3 * float(np.median(times))
     nbytes = (touched + nl) * EXPERT_BYTES + HEAD_BYTES
+    # the same step with the block coreset selector in every layer (shipped
+    # on at top_p 0.9); bytes from this step's kept experts per layer
+    x = emb[tok0.long()].contiguous()
+    nk = torch.zeros((1,), dtype=torch.int32, device=dev)
+    kept = 0
+    for lw in layers:
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        bdm.bdm_moe_block_forward(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"],
+                                  L.k, ws_gate=lw["ws_gate"], ws_up=lw["ws_up"],
+                                  ws_down=lw["ws_down"], residual=x, y=x, ws=ws,
+                                  coreset_top_p=0.9, coreset_block=L.T, n_kept=nk)
+        torch.cuda.synchronize()
+        kept += int(nk.item())
+    ctimes = []
+    for _ in range(reps):
+        tok.copy_(tok0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        bdm.bdm_denoise_block(tok, emb, stack, w_head, L.k, HS.mask_id, 0.95, max_steps=1,
+                              ws=dws, coreset_top_p=0.9)
+        ctimes.append(time.perf_counter() - t0)
+    cms = 1e3 * float(np.median(ctimes))
+    cbytes = (kept + nl) * EXPERT_BYTES + HEAD_BYTES
     out = {"layers": nl, "ms": round(ms, 3), "block_tokens_per_s": round(L.T / (ms * 1e-3), 1),
            "touched_experts_all_layers": touched, "bytes": int(nbytes),
            "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "gpu_ms": round(float(np.median(gtimes)), 3),
+           "coreset_top_p_0.9": {"ms": round(cms, 3),
+                                 "block_tokens_per_s": round(L.T / (cms * 1e-3), 1),
+                                 "kept_experts_all_layers": kept, "bytes": int(cbytes),
+                                 "GB_s": round(cbytes / (cms * 1e-3) / 1e9, 1),
+                                 "frac_of_peak": round(cbytes / (cms * 1e-3) / 1e9
+                                                       / PEAK_HBM_GBS, 4)},
            "block": "31 committed tokens (distinct seeded ids) + 1 masked slot",
            "timing": f"host wall clock of bdm_denoise_block(max_steps=1) (its per-step host "
                      f"read included), median of {reps}; gpu_ms: events on the stream around "

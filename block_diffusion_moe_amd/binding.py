@@ -40,8 +40,8 @@ _SIGS = {
                                              ctypes.POINTER(_c_size)]),
     "bdm_denoise_block": (_c_int, [_vp, _c_int, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _vp, _c_int, ctypes.c_int32,
-                                   _c_float, _c_int, ctypes.POINTER(_c_int), _vp, _vp, _c_size,
-                                   _vp]),
+                                   _c_float, _c_float, _c_int, ctypes.POINTER(_c_int), _vp, _vp,
+                                   _c_size, _vp]),
     "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
                                     _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "bdm_head_verify_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int,
@@ -310,10 +310,12 @@ class MoeStack:
 
 def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
                       threshold: float = 0.95, max_steps=None, renorm: bool = True, ws=None,
-                      stream=None):
+                      stream=None, coreset_top_p=None):
     """The denoise loop over the block `tokens` (int32 device [T], updated in
     place).  `layers`: a MoeStack, or the list of layer dicts it takes
-    (marshalled on every call then).  Returns (steps, commits per step)."""
+    (marshalled on every call then).  `coreset_top_p`: route every layer
+    through the block coreset selector at that top_p (None: plain top-k).
+    Returns (steps, commits per step)."""
     T = tokens.shape[0]
     V, H = w_embed.shape
     dev = tokens.device
@@ -334,8 +336,9 @@ def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
     commits = (ctypes.c_int32 * max(1, limit))()
     _raise("bdm_denoise_block", load().bdm_denoise_block(
         _ptr(tokens), T, _ptr(w_embed), V, H, stack.arr, len(stack), stack.E, int(k), stack.I,
-        int(renorm), _ptr(w_head), layout, int(mask_id), float(threshold), limit,
-        ctypes.byref(steps), commits, _ptr(ws), ws.numel(), _stream(stream)))
+        int(renorm), _ptr(w_head), layout, int(mask_id), float(threshold),
+        float(coreset_top_p or 0.0), limit, ctypes.byref(steps), commits, _ptr(ws), ws.numel(),
+        _stream(stream)))
     return steps.value, [int(commits[i]) for i in range(steps.value)]
 
 

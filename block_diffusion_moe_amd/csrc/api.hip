@@ -424,8 +424,8 @@ int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int has_share
 int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
                       const bdm_moe_layer* layers, int L, int E, int k, int I, int renorm,
                       const uint16_t* w_head, int weight_layout, int32_t mask_id, float threshold,
-                      int max_steps, int* steps_taken, int32_t* commits, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      float coreset_top_p, int max_steps, int* steps_taken, int32_t* commits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!tokens || !w_embed || !w_head || !steps_taken || !workspace || (L > 0 && !layers))
     return BDM_ERR_INVALID_ARG;
   if (L < 0 || max_steps < 0 || (renorm != 0 && renorm != 1)) return BDM_ERR_INVALID_ARG;
@@ -433,6 +433,7 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
     return BDM_ERR_INVALID_ARG;
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
+  if (!(coreset_top_p >= 0.0f && coreset_top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
   int has_shared = 1;
   for (int l = 0; l < L; ++l) {
     const bdm_moe_layer& w = layers[l];
@@ -479,7 +480,8 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
     // layer's input, after the last layer the final norm
     for (int l = 0; l < L; ++l) {
       const bdm_moe_layer& w = layers[l];
-      bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared, 0.0f, 0,
+      bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared,
+                         coreset_top_p, T < BDM_CORESET_MAX_BLOCK ? T : BDM_CORESET_MAX_BLOCK,
                          meta, nullptr, nullptr, nullptr, s);
       bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
                           w.ws_up, w.ws_down, x, x, xn, meta, weight_layout, s);

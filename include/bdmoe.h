@@ -244,7 +244,9 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
  *   x = w_embed[tokens];  for each layer: x = bf16(x + MoE(RMSNorm(x)));
  *   h = RMSNorm(x);  tokens = unmask(head(h))        (RMSNorm eps 1e-6, gamma 1)
  * with MoE = bdm_moe_block_forward, the head and rule = bdm_lm_head_unmask
- * with the fallback on.
+ * with the fallback on.  With coreset_top_p > 0 every layer's MoE is
+ * bdm_moe_block_forward_coreset over blocks of min(T, 32) tokens ([files]
+ * "What Clover is": the selector ships on at top_p 0.9).
  *
  * Arguments
  *   tokens      [T] int32 device, in/out: the block (mask_id = masked slot)
@@ -254,6 +256,8 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
  *   w_head      [V][H] bf16 device: the untied head
  *   weight_layout     layout of every expert matrix and of w_head
  *   mask_id, threshold   as in bdm_lm_head_unmask
+ *   coreset_top_p  0: plain top-k routing; in (0, 1]: the block coreset
+ *               expert selector at that top_p in every layer
  *   max_steps   steps at most (the loop also stops when no slot is masked)
  *   steps_taken HOST int: steps run
  *   commits     HOST [max_steps] int32 or NULL: slots committed per step
@@ -265,9 +269,9 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
 BDM_API int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
                               const bdm_moe_layer* layers, int L, int E, int k, int I,
                               int renorm, const uint16_t* w_head, int weight_layout,
-                              int32_t mask_id, float threshold, int max_steps,
-                              int* steps_taken, int32_t* commits, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              int32_t mask_id, float threshold, float coreset_top_p,
+                              int max_steps, int* steps_taken, int32_t* commits,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * bdm_head_workspace_bytes -- workspace size for bdm_lm_head_unmask.

@@ -37,13 +37,17 @@ from . import head, norm, stack
 
 
 def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
-                 threshold: float = 0.95, eps: float = 1e-6):
+                 threshold: float = 0.95, eps: float = 1e-6, coreset_top_p=None):
     """Steps 1-4 once.  Returns the oracle.head dict (new tokens, argmax, conf,
     n_committed, exclusion masks) plus 'near_route' ([T] any layer's top-k
-    near tie) and 'h' (the final normalised hidden state, bf16 bits)."""
+    near tie, or coreset rounding call) and 'h' (the final normalised hidden
+    state, bf16 bits).  ``coreset_top_p``: every layer routes through the
+    block coreset selector (the files page, "What Clover is": shipped on at
+    0.9) over blocks of min(32, T) slots."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x = np.asarray(embed_bits)[tokens]
-    y, near = stack.stack_forward(x, layers, k, eps)
+    y, near = stack.stack_forward(x, layers, k, eps, coreset_top_p=coreset_top_p,
+                                  block=min(32, max(1, len(tokens))))
     h = norm.rmsnorm(y, eps)
     out = head.head_unmask(h, head_bits, tokens, mask_id, threshold)
     out["near_route"] = near.any(axis=0) if len(layers) else np.zeros(len(tokens), bool)
@@ -52,13 +56,15 @@ def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
 
 
 def denoise_block(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
-                  threshold: float = 0.95, max_steps: int | None = None, eps: float = 1e-6):
+                  threshold: float = 0.95, max_steps: int | None = None, eps: float = 1e-6,
+                  coreset_top_p=None):
     """The loop.  Returns (final tokens, commits per step)."""
     tokens = np.asarray(tokens, dtype=np.int64).copy()
     limit = len(tokens) if max_steps is None else max_steps
     commits = []
     while (tokens == mask_id).any() and len(commits) < limit:
-        out = denoise_step(tokens, embed_bits, layers, head_bits, k, mask_id, threshold, eps)
+        out = denoise_step(tokens, embed_bits, layers, head_bits, k, mask_id, threshold, eps,
+                           coreset_top_p)
         tokens = out["tokens"]
         commits.append(out["n_committed"])
     return tokens, commits

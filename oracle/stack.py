@@ -13,22 +13,32 @@ block's rows to follow (the others are not computed).
 """
 import numpy as np
 
-from . import moe, norm
+from . import coreset, moe, norm
 
 
-def stack_forward(x_bits, layers, k, eps=1e-6, tokens=None):
+def stack_forward(x_bits, layers, k, eps=1e-6, tokens=None, coreset_top_p=None, block=32):
     """layers: list of dicts with w_router, w_gate, w_up, w_down, ws_gate,
-    ws_up, ws_down (and optional router_bias).  Returns (y bits, per-layer
-    near-tie flags [L][T'])."""
+    ws_up, ws_down (and optional router_bias).  With ``coreset_top_p`` every
+    layer routes through the block coreset selector (oracle.coreset, blocks of
+    ``block`` rows; the files page, "The expert selection") instead of the
+    plain top-k.  Returns (y bits, per-layer near flags [L][T']: a routing
+    near tie, or a coreset rounding call)."""
     x = np.asarray(x_bits)
     if tokens is not None:
+        if coreset_top_p:
+            raise ValueError("the coreset selector needs every row of its block")
         x = x[np.asarray(tokens)]
     near = []
     for L in layers:
         xn = norm.rmsnorm(x, eps)
+        routing = None
+        if coreset_top_p:
+            l32 = moe.router_logits(xn, L["w_router"], L.get("router_bias"))
+            c = coreset.coreset_route(l32, k, coreset_top_p, block=block)
+            routing = (c["idx"], c["w"], c["near_tie"])
         r = moe.moe_block(xn, L["w_router"], L["w_gate"], L["w_up"], L["w_down"], k,
                           L.get("ws_gate"), L.get("ws_up"), L.get("ws_down"),
-                          residual=x, bias=L.get("router_bias"))
+                          residual=x, bias=L.get("router_bias"), routing=routing)
         x = r["y"]
         near.append(r["near_tie"])
     return x, np.array(near)

@@ -232,17 +232,20 @@ def test_denoise_validation(lib):
 
     def call(**kw):
         a = dict(tokens=A, T=32, emb=A, V=248320, H=2048, layers=lay, L=2, E=256, k=8, I=512,
-                 renorm=1, head=A, layout=0, mask=151669, thr=0.95, steps=32)
+                 renorm=1, head=A, layout=0, mask=151669, thr=0.95, top_p=0.0, steps=32)
         a.update(kw)
         return lib.bdm_denoise_block(a["tokens"], a["T"], a["emb"], a["V"], a["H"], a["layers"],
                                      a["L"], a["E"], a["k"], a["I"], a["renorm"], a["head"],
-                                     a["layout"], a["mask"], a["thr"], a["steps"],
+                                     a["layout"], a["mask"], a["thr"], a["top_p"], a["steps"],
                                      ctypes.byref(steps), None, A, size, None)
     assert call(tokens=None) == -1
     assert call(mask=248320) == -1
     assert call(steps=-1) == -1
     assert call(layout=2) == -1
     assert call(thr=float("inf")) == -1
+    assert call(top_p=-0.1) == -1
+    assert call(top_p=1.5) == -1
+    assert call(top_p=float("nan")) == -1
     assert call(T=4000) == -2
     assert call(H=2000) == -2
     lay[1].ws_gate = None                       # shared trio broken in one layer

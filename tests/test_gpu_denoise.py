@@ -53,9 +53,11 @@ def _embed(V, H, seed, device):
     return torch.randn((V, H), generator=g, device=device).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("threshold", [0.95, 0.0, 0.02])
-def test_denoise_tiny_teacher_forced(bdm, threshold):
-    say(f"case denoise tiny threshold={threshold}")
+@pytest.mark.parametrize("threshold,top_p", [(0.95, None), (0.0, None), (0.02, None),
+                                             (0.95, 0.9), (0.02, 0.5)])
+def test_denoise_tiny_teacher_forced(bdm, threshold, top_p):
+    """With top_p, every layer routes through the block coreset selector."""
+    say(f"case denoise tiny threshold={threshold} coreset_top_p={top_p}")
     s = synth.MoEShape(T=8, H=64, E=16, I=32, k=2)
     V, mask = 512, 0
     layers = _layers(s, (11, 12, 13), DEV)
@@ -70,10 +72,10 @@ def test_denoise_tiny_teacher_forced(bdm, threshold):
     while (cur == mask).any():
         before = cur.cpu().numpy().astype(np.int64)
         steps, commits = bdm.bdm_denoise_block(cur, emb, layers, w_head, s.k, mask, threshold,
-                                               max_steps=1)
+                                               max_steps=1, coreset_top_p=top_p)
         torch.cuda.synchronize()
         after = cur.cpu().numpy().astype(np.int64)
-        o = oden.denoise_step(before, eb, hl, hb, s.k, mask, threshold)
+        o = oden.denoise_step(before, eb, hl, hb, s.k, mask, threshold, coreset_top_p=top_p)
         assert steps == 1 and commits[0] >= 1
         excl = o["near_route"] | o["near_tie"] | o["near_threshold"]
         keep = ~excl
@@ -88,7 +90,8 @@ def test_denoise_tiny_teacher_forced(bdm, threshold):
     say(f"  commits per step {history}")
     # the whole loop at once gives the same block, bit for bit
     full = tok0.clone()
-    steps, commits = bdm.bdm_denoise_block(full, emb, layers, w_head, s.k, mask, threshold)
+    steps, commits = bdm.bdm_denoise_block(full, emb, layers, w_head, s.k, mask, threshold,
+                                           coreset_top_p=top_p)
     torch.cuda.synchronize()
     assert commits == history and steps == len(history)
     assert torch.equal(full, cur)
@@ -96,11 +99,13 @@ def test_denoise_tiny_teacher_forced(bdm, threshold):
         assert history == [s.T - 1]
 
 
-def test_denoise_clover_stack_invariants_and_first_step(bdm):
-    """40 Clover-shaped layers, the 248,320-row head, packed weights."""
+@pytest.mark.parametrize("top_p", [None, 0.9])
+def test_denoise_clover_stack_invariants_and_first_step(bdm, top_p):
+    """40 Clover-shaped layers, the 248,320-row head, packed weights; plain
+    routing, and the coreset selector at the shipped top_p 0.9."""
     s = synth.LAYER
     HS = synth.HEAD
-    say("case denoise 40-layer stack + head")
+    say(f"case denoise 40-layer stack + head coreset_top_p={top_p}")
     layers = _layers(s, range(100, 100 + synth.STACK_LAYERS), DEV)
     pk = bdm.bdm_pack_weights
     players = [{**{n: lw[n] for n in ("w_router",)},
@@ -120,23 +125,24 @@ def test_denoise_clover_stack_invariants_and_first_step(bdm):
     ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(s.T, s.H, s.I, s.E, s.k, True), DEV)
     for lw in players:
         bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        kw = {} if top_p is None else {"coreset_top_p": top_p, "coreset_block": s.T}
         bdm.bdm_moe_block_forward(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"],
                                   s.k, ws_gate=lw["ws_gate"], ws_up=lw["ws_up"],
-                                  ws_down=lw["ws_down"], residual=x, y=x, ws=ws)
+                                  ws_down=lw["ws_down"], residual=x, y=x, ws=ws, **kw)
     bdm.bdm_rmsnorm(x, xn, eps=1e-6)
     ref = tok0.clone()
     nc = torch.zeros(1, dtype=torch.int32, device=DEV)
     bdm.bdm_lm_head_unmask(xn, w_head, HS.mask_id, 0.95, True, ref, n_committed=nc)
     one = tok0.clone()
     steps, commits = bdm.bdm_denoise_block(one, emb, players, w_head, s.k, HS.mask_id, 0.95,
-                                           max_steps=1)
+                                           max_steps=1, coreset_top_p=top_p)
     torch.cuda.synchronize()
     assert steps == 1 and commits == [int(nc.item())]
     assert torch.equal(one, ref)
     # the whole loop (layers marshalled once: the same results as the list)
     tok = tok0.clone()
     steps, commits = bdm.bdm_denoise_block(tok, emb, bdm.MoeStack(players), w_head, s.k,
-                                           HS.mask_id, 0.95)
+                                           HS.mask_id, 0.95, coreset_top_p=top_p)
     torch.cuda.synchronize()
     say(f"  {steps} steps, commits {commits}")
     masked0 = int((tok0 == HS.mask_id).sum())

@@ -14,6 +14,7 @@ import oracle.verify as VF
 import oracle.head as H
 import oracle.moe as M
 import oracle.norm as N
+import oracle.stack as S
 from oracle import bf16
 import tests.test_oracle_pins as P
 
@@ -136,6 +137,11 @@ def _step_no_final_norm(tokens, embed_bits, layers, head_bits, k, mask_id, thres
     return out
 
 
+def _stack_ignores_coreset(orig):
+    return lambda x, layers, k, eps=1e-6, tokens=None, coreset_top_p=None, block=32: orig(
+        x, layers, k, eps, tokens)
+
+
 def _loop_one_step(orig):
     return lambda *a, **kw: orig(*a, **dict(kw, max_steps=1))
 
@@ -177,6 +183,7 @@ MUTANTS = {
     "verify_bonus_from_last_row": (VF, "verify", _verify_bonus_last_row),
     "denoise_no_final_norm": (D, "denoise_step", lambda o: _step_no_final_norm),
     "denoise_stops_after_one_step": (D, "denoise_block", _loop_one_step),
+    "stack_ignores_coreset": (S, "stack_forward", _stack_ignores_coreset),
     "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
     "coreset_cut_one_more": (C, "cut", _cut_one_more),
     "coreset_mass_ties_high_id": (C, "mass_order", lambda o: _order_ties_high),
@@ -218,6 +225,7 @@ PINS = [
     P.test_denoise_loop_terminates_commits_and_never_revisits,
     P.test_denoise_step_is_its_parts_composed,
     P.test_denoise_confident_block_finishes_in_one_step,
+    P.test_denoise_with_coreset_selector,
     P.test_verify_bound_matches_page_points,
     P.test_verify_entropy_and_probabilities_closed_form,
     P.test_verify_threshold_decision_and_prefix,

@@ -589,6 +589,38 @@ def test_denoise_step_is_its_parts_composed():
     np.testing.assert_allclose(out["conf"], ref["conf"], rtol=0, atol=0)
 
 
+def test_denoise_with_coreset_selector():
+    """The loop with the block coreset selector on (the files page, "What
+    Clover is": shipped at top_p 0.9).  top_p = 1 keeps every touched expert:
+    the step is the plain one bit for bit.  A top_p so small that one expert
+    is kept per layer: every token of a layer goes to that expert alone with
+    weight 1, so the layer is x + FFN_e(xn) + FFN_shared(xn), computed here
+    densely with the single-expert FFN."""
+    from oracle import coreset as cs, denoise, stack
+    layers, emb, wh = _tiny_model(seed=4)
+    tokens = np.array([5, 5, 9, 5, 5, 40, 5, 5])
+    plain = denoise.denoise_step(tokens, emb, layers, wh, 2, 5, 0.95)
+    full = denoise.denoise_step(tokens, emb, layers, wh, 2, 5, 0.95, coreset_top_p=1.0)
+    assert np.array_equal(plain["h"], full["h"]) and np.array_equal(plain["tokens"],
+                                                                    full["tokens"])
+    x = emb[tokens]
+    y, _ = stack.stack_forward(x, layers, 2, coreset_top_p=1e-9, block=8)
+    ref = x
+    for lw in layers:
+        xn = norm.rmsnorm(ref, 1e-6)
+        l32 = moe.router_logits(xn, lw["w_router"])
+        kept = cs.block_coreset(l32, 2, 1e-9)["kept"]
+        assert len(kept) == 1
+        e = int(kept[0])
+        xf, rf = bf16.to_f64(xn), bf16.to_f64(ref)
+        out = np.stack([rf[t] + moe.expert_ffn(xf[t], lw["w_gate"][e], lw["w_up"][e],
+                                               lw["w_down"][e])
+                        + moe.expert_ffn(xf[t], lw["ws_gate"], lw["ws_up"], lw["ws_down"])
+                        for t in range(len(tokens))])
+        ref = bf16.from_f64(out)
+    assert np.array_equal(y, ref)
+
+
 def test_denoise_confident_block_finishes_in_one_step():
     """A threshold no probability can miss (0 < conf always) commits every
     masked slot in the first step; a threshold above 1 commits one per step."""
