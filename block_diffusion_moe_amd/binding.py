@@ -40,10 +40,11 @@ _SIGS = {
                                              ctypes.POINTER(_c_size)]),
     "bdm_denoise_block": (_c_int, [_vp, _c_int, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
                                    _c_int, _c_int, _c_int, _vp, _c_int, ctypes.c_int32,
-                                   _c_float, _c_float, _c_int, ctypes.POINTER(_c_int), _vp, _vp,
-                                   _c_size, _vp]),
+                                   _c_float, _c_float, _c_int, _c_int, ctypes.POINTER(_c_int),
+                                   _vp, _vp, _c_size, _vp]),
     "bdm_lm_head_unmask": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, ctypes.c_int32,
-                                    _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+                                    _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                    _vp]),
     "bdm_head_verify_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int,
                                                  ctypes.POINTER(_c_size)]),
     "bdm_lm_head_verify": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _c_int,
@@ -53,7 +54,7 @@ _SIGS = {
     "bdm_lm_head_stats": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                                    ctypes.c_int32, _vp, _vp, _vp, _c_int, _vp]),
     "bdm_unmask_from_stats": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, ctypes.c_int32,
-                                       _c_float, _c_int, _vp, _vp, _vp, _vp, _vp]),
+                                       _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "bdm_packed_weight_elems": (_c_int, [ctypes.c_long, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_pack_weights": (_c_int, [_vp, ctypes.c_long, _c_int, _vp, _vp]),
     "bdm_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
@@ -310,12 +311,14 @@ class MoeStack:
 
 def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
                       threshold: float = 0.95, max_steps=None, renorm: bool = True, ws=None,
-                      stream=None, coreset_top_p=None):
+                      stream=None, coreset_top_p=None, block_tokens: int = 0):
     """The denoise loop over the block `tokens` (int32 device [T], updated in
     place).  `layers`: a MoeStack, or the list of layer dicts it takes
     (marshalled on every call then).  `coreset_top_p`: route every layer
     through the block coreset selector at that top_p (None: plain top-k).
-    Returns (steps, commits per step)."""
+    `block_tokens` > 0: the rows are several blocks of that many slots, each
+    with its own commit rule.  Returns (steps, commits per step, summed over
+    the blocks)."""
     T = tokens.shape[0]
     V, H = w_embed.shape
     dev = tokens.device
@@ -331,19 +334,23 @@ def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
     need = bdm_denoise_workspace_bytes(T, H, stack.I, stack.E, k, stack.has_shared)
     if ws is None:
         ws = workspace(need, dev)
-    limit = T if max_steps is None else int(max_steps)
+    limit = (T if block_tokens <= 0 else min(T, int(block_tokens))) if max_steps is None \
+        else int(max_steps)
     steps = _c_int(0)
     commits = (ctypes.c_int32 * max(1, limit))()
     _raise("bdm_denoise_block", load().bdm_denoise_block(
         _ptr(tokens), T, _ptr(w_embed), V, H, stack.arr, len(stack), stack.E, int(k), stack.I,
         int(renorm), _ptr(w_head), layout, int(mask_id), float(threshold),
-        float(coreset_top_p or 0.0), limit, ctypes.byref(steps), commits, _ptr(ws), ws.numel(),
-        _stream(stream)))
+        float(coreset_top_p or 0.0), int(block_tokens), limit, ctypes.byref(steps), commits,
+        _ptr(ws), ws.numel(), _stream(stream)))
     return steps.value, [int(commits[i]) for i in range(steps.value)]
 
 
 def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool, tokens,
-                       argmax=None, conf=None, n_committed=None, ws=None, stream=None):
+                       argmax=None, conf=None, n_committed=None, ws=None, stream=None,
+                       block_tokens: int = 0):
+    """Head + commit rule; ``block_tokens`` > 0 applies the rule to every
+    block of that many rows on its own (0: the rows are one block)."""
     T, H = h.shape
     V = w_head.shape[0]
     dev = h.device
@@ -358,9 +365,9 @@ def bdm_lm_head_unmask(h, w_head, mask_id: int, threshold: float, fallback: bool
         ws = workspace(need, dev)
     layout = BDM_LAYOUT_MFMA_TILES if isinstance(w_head, Packed) else BDM_LAYOUT_ROW_MAJOR
     st = load().bdm_lm_head_unmask(_ptr(h), T, H, _ptr(w_head), V, layout, int(mask_id),
-                                   float(threshold), int(fallback), _ptr(tokens), _ptr(argmax),
-                                   _ptr(conf), _ptr(n_committed), _ptr(ws), ws.numel(),
-                                   _stream(stream))
+                                   float(threshold), int(fallback), int(block_tokens),
+                                   _ptr(tokens), _ptr(argmax), _ptr(conf), _ptr(n_committed),
+                                   _ptr(ws), ws.numel(), _stream(stream))
     _raise("bdm_lm_head_unmask", st)
     return tokens
 
@@ -444,7 +451,7 @@ def bdm_lm_head_stats(h, w_head, mask_id: int, stat_max, stat_sum, stat_arg, voc
 
 def bdm_unmask_from_stats(stat_max, stat_sum, stat_arg, mask_id: int, threshold: float,
                           fallback: bool, tokens, argmax=None, conf=None, n_committed=None,
-                          stream=None):
+                          stream=None, block_tokens: int = 0):
     """Phase 2: merge the [T][parts] triples (all columns of the given views) and
     apply the commit rule to tokens."""
     T, parts = stat_max.shape
@@ -456,8 +463,8 @@ def bdm_unmask_from_stats(stat_max, stat_sum, stat_arg, mask_id: int, threshold:
     stride = stat_max.stride(0)
     _raise("bdm_unmask_from_stats", load().bdm_unmask_from_stats(
         _ptr(stat_max), _ptr(stat_sum), _ptr(stat_arg), T, parts, stride, int(mask_id),
-        float(threshold), int(fallback), _ptr(tokens), _ptr(argmax), _ptr(conf),
-        _ptr(n_committed), _stream(stream)))
+        float(threshold), int(fallback), int(block_tokens), _ptr(tokens), _ptr(argmax),
+        _ptr(conf), _ptr(n_committed), _stream(stream)))
     return tokens
 
 

@@ -264,9 +264,9 @@ int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {
 
 int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
                        int weight_layout, int32_t mask_id, float threshold, int fallback,
-                       int32_t* tokens,
-                       int32_t* argmax, float* conf, int32_t* n_committed, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int block_tokens, int32_t* tokens, int32_t* argmax, float* conf,
+                       int32_t* n_committed, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (!h || !w_head || !tokens || !workspace) return BDM_ERR_INVALID_ARG;
   int st = check_head_shape(T, H, V);
   if (st != BDM_OK) return st;
@@ -274,6 +274,7 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
   if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
+  if (block_tokens < 0) return BDM_ERR_INVALID_ARG;
   if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
     return BDM_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(w_head) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
@@ -291,7 +292,7 @@ int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, 
   bdm::launch_head_stats(h, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s, parts.a,
                          parts.grid, parts.grid, s);
   bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
-                     fallback, tokens, argmax, conf, n_committed, nullptr, s);
+                     fallback, block_tokens, tokens, argmax, conf, n_committed, nullptr, s);
   return last_hip_status();
 }
 
@@ -368,17 +369,18 @@ int bdm_lm_head_stats(const uint16_t* h, int T, int H, const uint16_t* w_head, i
 
 int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum, const int32_t* stat_arg,
                           int T, int parts, int stat_stride, int32_t mask_id, float threshold,
-                          int fallback, int32_t* tokens, int32_t* argmax, float* conf,
-                          int32_t* n_committed, void* stream) {
+                          int fallback, int block_tokens, int32_t* tokens, int32_t* argmax,
+                          float* conf, int32_t* n_committed, void* stream) {
   if (!stat_max || !stat_sum || !stat_arg || !tokens) return BDM_ERR_INVALID_ARG;
   if (T < 1 || parts < 1 || stat_stride < parts) return BDM_ERR_INVALID_ARG;
   if (T > BDM_MAX_TOKENS) return BDM_ERR_UNSUPPORTED_SHAPE;
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
   if (fallback != 0 && fallback != 1) return BDM_ERR_INVALID_ARG;
+  if (block_tokens < 0) return BDM_ERR_INVALID_ARG;
   (void)hipGetLastError();
   bdm::launch_unmask(stat_max, stat_sum, stat_arg, T, parts, stat_stride, mask_id, threshold,
-                     fallback, tokens, argmax, conf, n_committed, nullptr,
+                     fallback, block_tokens, tokens, argmax, conf, n_committed, nullptr,
                      static_cast<hipStream_t>(stream));
   return last_hip_status();
 }
@@ -424,8 +426,8 @@ int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int has_share
 int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
                       const bdm_moe_layer* layers, int L, int E, int k, int I, int renorm,
                       const uint16_t* w_head, int weight_layout, int32_t mask_id, float threshold,
-                      float coreset_top_p, int max_steps, int* steps_taken, int32_t* commits,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      float coreset_top_p, int block_tokens, int max_steps, int* steps_taken,
+                      int32_t* commits, void* workspace, size_t workspace_bytes, void* stream) {
   if (!tokens || !w_embed || !w_head || !steps_taken || !workspace || (L > 0 && !layers))
     return BDM_ERR_INVALID_ARG;
   if (L < 0 || max_steps < 0 || (renorm != 0 && renorm != 1)) return BDM_ERR_INVALID_ARG;
@@ -434,6 +436,10 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
   if (!(coreset_top_p >= 0.0f && coreset_top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
+  if (block_tokens < 0) return BDM_ERR_INVALID_ARG;
+  // the rule's blocks (0: the whole call) and the coreset selector's
+  const int B = (block_tokens == 0 || block_tokens > T) ? T : block_tokens;
+  const int cs_block = B < BDM_CORESET_MAX_BLOCK ? B : BDM_CORESET_MAX_BLOCK;
   int has_shared = 1;
   for (int l = 0; l < L; ++l) {
     const bdm_moe_layer& w = layers[l];
@@ -481,15 +487,14 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
     for (int l = 0; l < L; ++l) {
       const bdm_moe_layer& w = layers[l];
       bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared,
-                         coreset_top_p, T < BDM_CORESET_MAX_BLOCK ? T : BDM_CORESET_MAX_BLOCK,
-                         meta, nullptr, nullptr, nullptr, s);
+                         coreset_top_p, cs_block, meta, nullptr, nullptr, nullptr, s);
       bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
                           w.ws_up, w.ws_down, x, x, xn, meta, weight_layout, s);
     }
     bdm::launch_head_stats(xn, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s,
                            parts.a, parts.grid, parts.grid, s);
     bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
-                       1, tokens, nullptr, nullptr, cnt, cnt + 1, s);
+                       1, B, tokens, nullptr, nullptr, cnt, cnt + 1, s);
     int32_t host[2] = {0, 0};
     if (hipMemcpyAsync(host, cnt, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)

@@ -411,10 +411,11 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
 
 // One workgroup.  16 threads (one DPP row) per token merge that token's
 // partials (all loads issued first), the row reduction finishes the merge,
-// and one wave applies the commit rule over the block.
+// and the commit rule is applied to every block of B rows on its own (B >= T:
+// the whole call is one block), a wave per block.
 __global__ __launch_bounds__(1024) void head_merge_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const int32_t* __restrict__ pa,
-    int T, int nparts, int pstride, int32_t mask_id, float threshold, int fallback,
+    int T, int nparts, int pstride, int32_t mask_id, float threshold, int fallback, int B,
     int32_t* tokens,
     int32_t* __restrict__ argmax_out, float* __restrict__ conf_out,
     int32_t* __restrict__ n_committed, int32_t* __restrict__ n_left) {
@@ -452,36 +453,60 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
     }
   }
   __syncthreads();
-  if (tid >= kWave) return;
 
-  // Commit rule, one wave.  Best masked row for the fallback: largest conf,
-  // equal -> lowest position.
-  const int lane = tid;
-  int ncommit = 0, nmasked = 0;
-  float best_c = -INFINITY;
-  int best_t = INT32_MAX;
-  for (int t0 = 0; t0 < T; t0 += kWave) {
-    const int t = t0 + lane;
-    int commit = 0;
-    nmasked += wave_sum_i((t < T && stok[t] == mask_id) ? 1 : 0);
-    if (t < T && stok[t] == mask_id) {
-      const float cf = sconf[t];
-      if (cf >= threshold) commit = 1;
-      if (cf > best_c || (cf == best_c && t < best_t)) {
-        best_c = cf;
-        best_t = t;
+  // Commit rule per block of B rows, wave w taking blocks w, w + 16, ...
+  // Best masked row of a block for the fallback: largest conf, equal ->
+  // lowest position.
+  __shared__ int wsum[2][1024 / kWave];
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int nw = static_cast<int>(blockDim.x) / kWave;
+  const int nblk = (T + B - 1) / B;
+  int wcommit = 0, wleft = 0;
+  for (int b = wave; b < nblk; b += nw) {
+    const int r0 = b * B;
+    const int r1 = (T - r0) < B ? T : r0 + B;
+    int ncommit = 0, nmasked = 0;
+    float best_c = -INFINITY;
+    int best_t = INT32_MAX;
+    for (int t0 = r0; t0 < r1; t0 += kWave) {
+      const int t = t0 + lane;
+      const bool m = t < r1 && stok[t] == mask_id;
+      int commit = 0;
+      nmasked += wave_sum_i(m ? 1 : 0);
+      if (m) {
+        const float cf = sconf[t];
+        if (cf >= threshold) commit = 1;
+        if (cf > best_c || (cf == best_c && t < best_t)) {
+          best_c = cf;
+          best_t = t;
+        }
       }
+      if (commit) tokens[t] = sarg[t];
+      ncommit += wave_sum_i(commit);
     }
-    if (commit) tokens[t] = sarg[t];
-    ncommit += wave_sum_i(commit);
+    wave_argmax(best_c, best_t);
+    if (fallback && ncommit == 0 && best_t != INT32_MAX) {
+      if (lane == 0) tokens[best_t] = sarg[best_t];
+      ncommit = 1;
+    }
+    wcommit += ncommit;
+    wleft += nmasked - ncommit;
   }
-  wave_argmax(best_c, best_t);
-  if (fallback && ncommit == 0 && best_t != INT32_MAX) {
-    if (lane == 0) tokens[best_t] = sarg[best_t];
-    ncommit = 1;
+  if (lane == 0) {
+    wsum[0][wave] = wcommit;
+    wsum[1][wave] = wleft;
   }
-  if (lane == 0 && n_committed) *n_committed = ncommit;
-  if (lane == 0 && n_left) *n_left = nmasked - ncommit;
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0, l = 0;
+    for (int w = 0; w < nw; ++w) {
+      c += wsum[0][w];
+      l += wsum[1][w];
+    }
+    if (n_committed) *n_committed = c;
+    if (n_left) *n_left = l;
+  }
 }
 
 // Verify epilogue ([files] "Two ways to run it"), one workgroup: merge the
@@ -635,11 +660,12 @@ void launch_head_verify_stats(const uint16_t* h, int T, int H, const uint16_t* w
 }
 
 void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
-                   int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
-                   int32_t* argmax, float* conf, int32_t* n_committed, int32_t* n_left,
-                   hipStream_t s) {
+                   int pstride, int32_t mask_id, float threshold, int fallback, int block,
+                   int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
+                   int32_t* n_left, hipStream_t s) {
+  const int B = (block <= 0 || block > T) ? T : block;
   head_merge_kernel<<<1, 1024, static_cast<size_t>(T) * 12, s>>>(
-      pm, ps, pa, T, parts, pstride, mask_id, threshold, fallback, tokens, argmax, conf,
+      pm, ps, pa, T, parts, pstride, mask_id, threshold, fallback, B, tokens, argmax, conf,
       n_committed, n_left);
 }
 

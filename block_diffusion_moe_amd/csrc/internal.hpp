@@ -79,10 +79,12 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
                        int pstride, int grid, hipStream_t s);
 
 // n_left (nullable): masked rows that remain after the rule
+// the commit rule is applied to every block of `block` rows on its own
+// (block <= 0 or >= T: the whole call is one block)
 void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, int parts,
-                   int pstride, int32_t mask_id, float threshold, int fallback, int32_t* tokens,
-                   int32_t* argmax, float* conf, int32_t* n_committed, int32_t* n_left,
-                   hipStream_t s);
+                   int pstride, int32_t mask_id, float threshold, int fallback, int block,
+                   int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
+                   int32_t* n_left, hipStream_t s);
 
 // x[t] = w_embed[tokens[t]] (ids clamped to [0, V)), bf16 rows of H
 void launch_embed(const int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,

@@ -245,8 +245,8 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
  *   h = RMSNorm(x);  tokens = unmask(head(h))        (RMSNorm eps 1e-6, gamma 1)
  * with MoE = bdm_moe_block_forward, the head and rule = bdm_lm_head_unmask
  * with the fallback on.  With coreset_top_p > 0 every layer's MoE is
- * bdm_moe_block_forward_coreset over blocks of min(T, 32) tokens ([files]
- * "What Clover is": the selector ships on at top_p 0.9).
+ * bdm_moe_block_forward_coreset ([files] "What Clover is": the selector
+ * ships on at top_p 0.9).
  *
  * Arguments
  *   tokens      [T] int32 device, in/out: the block (mask_id = masked slot)
@@ -257,7 +257,12 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
  *   weight_layout     layout of every expert matrix and of w_head
  *   mask_id, threshold   as in bdm_lm_head_unmask
  *   coreset_top_p  0: plain top-k routing; in (0, 1]: the block coreset
- *               expert selector at that top_p in every layer
+ *               expert selector at that top_p in every layer (over blocks
+ *               of min(block, 32) tokens)
+ *   block_tokens  several blocks in one call: the T rows are blocks of this
+ *               many slots, each with its own commit rule (every step
+ *               commits at least one slot of every block still masked); the
+ *               loop runs until no block has a masked slot.  0: one block
  *   max_steps   steps at most (the loop also stops when no slot is masked)
  *   steps_taken HOST int: steps run
  *   commits     HOST [max_steps] int32 or NULL: slots committed per step
@@ -270,8 +275,9 @@ BDM_API int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, i
                               const bdm_moe_layer* layers, int L, int E, int k, int I,
                               int renorm, const uint16_t* w_head, int weight_layout,
                               int32_t mask_id, float threshold, float coreset_top_p,
-                              int max_steps, int* steps_taken, int32_t* commits,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              int block_tokens, int max_steps, int* steps_taken,
+                              int32_t* commits, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * bdm_head_workspace_bytes -- workspace size for bdm_lm_head_unmask.
@@ -305,6 +311,10 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  *   mask_id      0 <= mask_id < V   (V >= 2)
  *   threshold    commit threshold (finite, compared with >=)
  *   fallback     1: the progress rule above; 0: threshold only
+ *   block_tokens the rule (threshold and fallback) applies to every block of
+ *                this many rows on its own (several blocks in one call:
+ *                each commits at least one masked row); 0: the T rows are
+ *                one block
  *   tokens       [T] int32          in/out: current block contents
  *   argmax       [T] int32 or NULL  receives argmax_t for every row
  *   conf         [T] fp32 or NULL   receives conf_t for every row
@@ -313,8 +323,9 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  */
 BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* w_head, int V,
                        int weight_layout, int32_t mask_id, float threshold, int fallback,
-                       int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       int block_tokens, int32_t* tokens, int32_t* argmax, float* conf,
+                       int32_t* n_committed, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * The head in two phases, for callers that merge statistics themselves (for
@@ -341,7 +352,8 @@ BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* 
  * bdm_unmask_from_stats -- phase 2: per token, merge stat_*[t*stat_stride +
  *   0 .. parts-1] (max of maxima; sums rescaled to the common max and added;
  *   equal maxima keep the lowest id), conf = 1/sum, argmax = that id, then the
- *   commit rule of bdm_lm_head_unmask on tokens (same arguments and outputs).
+ *   commit rule of bdm_lm_head_unmask on tokens (same arguments, block_tokens
+ *   included, and outputs).
  */
 BDM_API int bdm_head_stat_parts(int* parts);
 
@@ -353,8 +365,8 @@ BDM_API int bdm_lm_head_stats(const uint16_t* h, int T, int H, const uint16_t* w
 BDM_API int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum,
                                   const int32_t* stat_arg, int T, int parts, int stat_stride,
                                   int32_t mask_id, float threshold, int fallback,
-                                  int32_t* tokens, int32_t* argmax, float* conf,
-                                  int32_t* n_committed, void* stream);
+                                  int block_tokens, int32_t* tokens, int32_t* argmax,
+                                  float* conf, int32_t* n_committed, void* stream);
 
 /*
  * bdm_lm_head_verify -- the verify epilogue of self-speculative decoding

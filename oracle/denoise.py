@@ -37,19 +37,22 @@ from . import head, norm, stack
 
 
 def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
-                 threshold: float = 0.95, eps: float = 1e-6, coreset_top_p=None):
+                 threshold: float = 0.95, eps: float = 1e-6, coreset_top_p=None, block=None):
     """Steps 1-4 once.  Returns the oracle.head dict (new tokens, argmax, conf,
     n_committed, exclusion masks) plus 'near_route' ([T] any layer's top-k
     near tie, or coreset rounding call) and 'h' (the final normalised hidden
     state, bf16 bits).  ``coreset_top_p``: every layer routes through the
     block coreset selector (the files page, "What Clover is": shipped on at
-    0.9) over blocks of min(32, T) slots."""
+    0.9) over blocks of min(32, B) slots.  ``block`` = B: the rows are
+    several blocks of B slots, each with its own commit rule (one block of
+    T slots when None)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x = np.asarray(embed_bits)[tokens]
+    B = block if block else len(tokens)
     y, near = stack.stack_forward(x, layers, k, eps, coreset_top_p=coreset_top_p,
-                                  block=min(32, max(1, len(tokens))))
+                                  block=min(32, max(1, B)))
     h = norm.rmsnorm(y, eps)
-    out = head.head_unmask(h, head_bits, tokens, mask_id, threshold)
+    out = head.head_unmask(h, head_bits, tokens, mask_id, threshold, block=block)
     out["near_route"] = near.any(axis=0) if len(layers) else np.zeros(len(tokens), bool)
     out["h"] = h
     return out
@@ -57,14 +60,14 @@ def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
 
 def denoise_block(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
                   threshold: float = 0.95, max_steps: int | None = None, eps: float = 1e-6,
-                  coreset_top_p=None):
+                  coreset_top_p=None, block=None):
     """The loop.  Returns (final tokens, commits per step)."""
     tokens = np.asarray(tokens, dtype=np.int64).copy()
     limit = len(tokens) if max_steps is None else max_steps
     commits = []
     while (tokens == mask_id).any() and len(commits) < limit:
         out = denoise_step(tokens, embed_bits, layers, head_bits, k, mask_id, threshold, eps,
-                           coreset_top_p)
+                           coreset_top_p, block)
         tokens = out["tokens"]
         commits.append(out["n_committed"])
     return tokens, commits

@@ -62,9 +62,20 @@ def confidence(l32, mask_id: int):
     return a.astype(np.int64), conf, gap
 
 
-def unmask(tokens, argmax, conf, mask_id: int, threshold: float, fallback: bool = True):
-    """Step 4.  Returns (new tokens [T] int64, committed [T] bool)."""
+def unmask(tokens, argmax, conf, mask_id: int, threshold: float, fallback: bool = True,
+           block=None):
+    """Step 4.  Returns (new tokens [T] int64, committed [T] bool).  With
+    ``block``, the rows are several blocks of that many slots and the rule
+    (threshold and fallback) applies to each block on its own."""
     tokens = np.asarray(tokens, dtype=np.int64)
+    if block and block < len(tokens):
+        outs, commits = [], []
+        for b0 in range(0, len(tokens), block):
+            o, c = unmask(tokens[b0:b0 + block], np.asarray(argmax)[b0:b0 + block],
+                          np.asarray(conf)[b0:b0 + block], mask_id, threshold, fallback)
+            outs.append(o)
+            commits.append(c)
+        return np.concatenate(outs), np.concatenate(commits)
     c32 = np.asarray(conf, dtype=np.float32)
     masked = tokens == mask_id
     commit = masked & (c32 >= np.float32(threshold))
@@ -76,21 +87,25 @@ def unmask(tokens, argmax, conf, mask_id: int, threshold: float, fallback: bool 
 
 
 def head_unmask(h_bits, w_head_bits, tokens, mask_id: int, threshold: float = 0.95,
-                fallback: bool = True):
-    """Steps 1-4 for one block.  Returns dict with tokens, argmax, conf,
-    committed, n_committed and the exclusion masks used by parity tests."""
+                fallback: bool = True, block=None):
+    """Steps 1-4 for one block (or, with ``block``, for each block of that many
+    rows).  Returns dict with tokens, argmax, conf, committed, n_committed and
+    the exclusion masks used by parity tests."""
     l32 = head_logits(h_bits, w_head_bits)
     a, conf, gap = confidence(l32, mask_id)
-    new, commit = unmask(tokens, a, conf, mask_id, threshold, fallback)
+    new, commit = unmask(tokens, a, conf, mask_id, threshold, fallback, block)
     masked = np.asarray(tokens) == mask_id
     c32 = conf.astype(np.float32).astype(np.float64)
     near_thr = np.abs(c32 - threshold) < GAP_EXCLUDE
     # the fallback pick is a coin toss when the two best masked confidences
-    # are within a relative 1e-4 of each other
+    # of a block are within a relative 1e-4 of each other
     fb_tie = False
-    if fallback and masked.sum() >= 2 and not (masked & (c32 >= threshold)).any():
-        mc = np.sort(c32[masked])[::-1]
-        fb_tie = bool(mc[0] - mc[1] < REL_GAP_FALLBACK * mc[0])
+    B = block if block else len(masked)
+    for b0 in range(0, len(masked), B):
+        mb, cb = masked[b0:b0 + B], c32[b0:b0 + B]
+        if fallback and mb.sum() >= 2 and not (mb & (cb >= threshold)).any():
+            mc = np.sort(cb[mb])[::-1]
+            fb_tie |= bool(mc[0] - mc[1] < REL_GAP_FALLBACK * mc[0])
     return {
         "tokens": new,
         "argmax": a,

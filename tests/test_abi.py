@@ -128,12 +128,12 @@ def test_head_and_rmsnorm_validation(lib):
     W = _fake(1 << 24)
 
     def head(**kw):
-        a = dict(h=A, T=32, H=2048, w=A, V=248320, lay=0, mask=151669, thr=0.95, fb=1, tok=T,
-                 am=None, cf=None, nc=None, ws=W, wsb=1 << 30, st=None)
+        a = dict(h=A, T=32, H=2048, w=A, V=248320, lay=0, mask=151669, thr=0.95, fb=1, blk=0,
+                 tok=T, am=None, cf=None, nc=None, ws=W, wsb=1 << 30, st=None)
         a.update(kw)
         return lib.bdm_lm_head_unmask(a["h"], a["T"], a["H"], a["w"], a["V"], a["lay"],
-                                      a["mask"], a["thr"], a["fb"], a["tok"], a["am"], a["cf"],
-                                      a["nc"], a["ws"], a["wsb"], a["st"])
+                                      a["mask"], a["thr"], a["fb"], a["blk"], a["tok"], a["am"],
+                                      a["cf"], a["nc"], a["ws"], a["wsb"], a["st"])
 
     assert head(h=None) == -1
     assert head(tok=None) == -1
@@ -141,6 +141,7 @@ def test_head_and_rmsnorm_validation(lib):
     assert head(mask=-1) == -1
     assert head(thr=float("nan")) == -1
     assert head(fb=3) == -1
+    assert head(blk=-1) == -1
     assert head(lay=5) == -1
     assert head(T=0) == -1
     assert head(T=4096) == -2
@@ -171,10 +172,14 @@ def test_two_phase_head_validation(lib):
     assert lib.bdm_lm_head_stats(A, 32, 2048, A, 1000, -1, 0, 5, S, S, S, 1024, None) == -1
     assert lib.bdm_lm_head_stats(A, 32, 2048, A, 1000, 0, 3, 5, S, S, S, 1024, None) == -1
     assert lib.bdm_lm_head_stats(A, 32, 2000, A, 1000, 0, 0, 5, S, S, S, 1024, None) == -2
-    assert lib.bdm_unmask_from_stats(S, S, S, 32, 0, 8, 5, 0.95, 1, A, None, None, None, None) == -1
-    assert lib.bdm_unmask_from_stats(S, S, S, 32, 16, 8, 5, 0.95, 1, A, None, None, None, None) == -1
-    assert lib.bdm_unmask_from_stats(S, S, S, 32, 8, 8, 5, 0.95, 1, None, None, None, None, None) == -1
-    assert lib.bdm_unmask_from_stats(S, S, S, 4000, 8, 8, 5, 0.95, 1, A, None, None, None, None) == -2
+    u = lib.bdm_unmask_from_stats
+    assert u(S, S, S, 32, 0, 8, 5, 0.95, 1, 0, A, None, None, None, None) == -1
+    assert u(S, S, S, 32, 16, 8, 5, 0.95, 1, 0, A, None, None, None, None) == -1
+    assert u(S, S, S, 32, 8, 8, 5, 0.95, 1, 0, None, None, None, None, None) == -1
+    assert lib.bdm_unmask_from_stats(S, S, S, 4000, 8, 8, 5, 0.95, 1, 0, A, None, None, None,
+                                     None) == -2
+    assert lib.bdm_unmask_from_stats(S, S, S, 32, 8, 8, 5, 0.95, 1, -2, A, None, None, None,
+                                     None) == -1
 
 
 def test_calibration_library_exports():
@@ -232,11 +237,12 @@ def test_denoise_validation(lib):
 
     def call(**kw):
         a = dict(tokens=A, T=32, emb=A, V=248320, H=2048, layers=lay, L=2, E=256, k=8, I=512,
-                 renorm=1, head=A, layout=0, mask=151669, thr=0.95, top_p=0.0, steps=32)
+                 renorm=1, head=A, layout=0, mask=151669, thr=0.95, top_p=0.0, blk=0, steps=32)
         a.update(kw)
         return lib.bdm_denoise_block(a["tokens"], a["T"], a["emb"], a["V"], a["H"], a["layers"],
                                      a["L"], a["E"], a["k"], a["I"], a["renorm"], a["head"],
-                                     a["layout"], a["mask"], a["thr"], a["top_p"], a["steps"],
+                                     a["layout"], a["mask"], a["thr"], a["top_p"], a["blk"],
+                                     a["steps"],
                                      ctypes.byref(steps), None, A, size, None)
     assert call(tokens=None) == -1
     assert call(mask=248320) == -1
@@ -246,6 +252,7 @@ def test_denoise_validation(lib):
     assert call(top_p=-0.1) == -1
     assert call(top_p=1.5) == -1
     assert call(top_p=float("nan")) == -1
+    assert call(blk=-1) == -1
     assert call(T=4000) == -2
     assert call(H=2000) == -2
     lay[1].ws_gate = None                       # shared trio broken in one layer

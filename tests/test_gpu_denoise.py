@@ -100,6 +100,49 @@ def test_denoise_tiny_teacher_forced(bdm, threshold, top_p):
 
 
 @pytest.mark.parametrize("top_p", [None, 0.9])
+def test_denoise_multiblock_tiny(bdm, top_p):
+    """Three blocks of 8 slots in one loop (each its own commit rule): every
+    step against the oracle's (teacher-forced, near calls excluded), and the
+    final tokens equal each block denoised alone, bit for bit."""
+    say(f"case denoise multi-block tiny coreset_top_p={top_p}")
+    s = synth.MoEShape(T=24, H=64, E=16, I=32, k=2)
+    V, mask, B = 512, 0, 8
+    layers = _layers(s, (21, 22), DEV)
+    emb = _embed(V, s.H, 3, DEV)
+    w_head = synth.head_weights(synth.HeadShape(T=24, H=64, V=V, mask_id=mask), 6, device=DEV)
+    w_head = (w_head.float() * 30.0).to(torch.bfloat16)
+    hl, eb, hb = _host_layers(layers), synth.bf16_bits(emb), synth.bf16_bits(w_head)
+    tok0 = torch.full((s.T,), mask, dtype=torch.int32, device=DEV)
+    tok0[[2, 11, 20]] = torch.tensor([7, 8, 9], dtype=torch.int32, device=DEV)
+    cur = tok0.clone()
+    while (cur == mask).any():
+        before = cur.cpu().numpy().astype(np.int64)
+        steps, commits = bdm.bdm_denoise_block(cur, emb, layers, w_head, s.k, mask, 0.95,
+                                               max_steps=1, coreset_top_p=top_p, block_tokens=B)
+        torch.cuda.synchronize()
+        after = cur.cpu().numpy().astype(np.int64)
+        o = oden.denoise_step(before, eb, hl, hb, s.k, mask, 0.95, coreset_top_p=top_p,
+                              block=B)
+        excl = o["near_route"] | o["near_tie"] | o["near_threshold"]
+        if not excl.any() and not o["fallback_tie"]:
+            assert np.array_equal(after, o["tokens"]), (after, o["tokens"])
+            assert commits[0] == o["n_committed"]
+        else:
+            assert np.array_equal(after[~excl], o["tokens"][~excl])
+        for b in range(0, s.T, B):              # every block still masked commits
+            if (before[b:b + B] == mask).any():
+                assert (after[b:b + B] != before[b:b + B]).any()
+    full = tok0.clone()
+    bdm.bdm_denoise_block(full, emb, layers, w_head, s.k, mask, 0.95, coreset_top_p=top_p,
+                          block_tokens=B)
+    for b in range(0, s.T, B):
+        one = tok0[b:b + B].clone()
+        bdm.bdm_denoise_block(one, emb, layers, w_head, s.k, mask, 0.95, coreset_top_p=top_p)
+        torch.cuda.synchronize()
+        assert torch.equal(one, full[b:b + B]), b
+
+
+@pytest.mark.parametrize("top_p", [None, 0.9])
 def test_denoise_clover_stack_invariants_and_first_step(bdm, top_p):
     """40 Clover-shaped layers, the 248,320-row head, packed weights; plain
     routing, and the coreset selector at the shipped top_p 0.9."""

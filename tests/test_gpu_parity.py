@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from oracle import norm as onorm
+from oracle import head as ohead, norm as onorm
 from tests.conftest import gpu_available
 from tests.gpu_common import (assert_bf16_close, compare_head, compare_moe, oracle_head,
                               oracle_moe, run_head, run_moe, say)
@@ -326,6 +326,39 @@ def test_head_wide_pass_equals_32_row_calls(bdm, T):
         torch.cuda.synchronize()
         for x, z in zip(wide, narrow):
             assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_head_rule_per_block(bdm, layout):
+    """Two blocks of 32 in one call, the rule per block: block 0 has rows
+    above the threshold, block 1 none (its most confident masked row is
+    committed by the fallback, as it would be alone)."""
+    say(f"case head rule per block layout={layout}")
+    s = synth.HeadShape(T=32, H=2048, V=70001, mask_id=321)
+    W = synth.head_weights(s, 8, device=DEV)
+    b0 = synth.head_block(s, W, block_seed=11, n_boost=10)
+    b1 = synth.head_block(s, W, block_seed=12, boost=12.0, boost_all=True)
+    h = torch.cat([b0.h, b1.h]).contiguous()
+    tok = torch.cat([b0.tokens, b1.tokens]).contiguous()
+    Wl = bdm.bdm_pack_weights(W) if layout else W
+    am = torch.empty(64, dtype=torch.int32, device=DEV)
+    cf = torch.empty(64, dtype=torch.float32, device=DEV)
+    nc = torch.empty(1, dtype=torch.int32, device=DEV)
+    out = tok.clone()
+    bdm.bdm_lm_head_unmask(h, Wl, s.mask_id, 0.95, True, out, argmax=am, conf=cf,
+                           n_committed=nc, block_tokens=32)
+    torch.cuda.synchronize()
+    o = ohead.head_unmask(synth.bf16_bits(h), synth.bf16_bits(W), tok.cpu().numpy(), s.mask_id,
+                          0.95, True, block=32)
+    assert o["committed"][32:].sum() == 1 and o["committed"][:32].sum() >= 1
+    o["mask_id"] = s.mask_id
+    compare_head((out, am, cf, nc), o, tok.cpu().numpy())
+    # each block alone gives the same rows
+    for b, blk in enumerate((b0, b1)):
+        one = blk.tokens.clone()
+        bdm.bdm_lm_head_unmask(blk.h, Wl, s.mask_id, 0.95, True, one)
+        torch.cuda.synchronize()
+        assert torch.equal(one, out[32 * b:32 * (b + 1)])
 
 
 def test_head_repeatable_bitwise(bdm):

@@ -142,6 +142,11 @@ def _stack_ignores_coreset(orig):
         x, layers, k, eps, tokens)
 
 
+def _unmask_whole_call(orig):
+    return lambda tokens, argmax, conf, mask_id, threshold, fallback=True, block=None: orig(
+        tokens, argmax, conf, mask_id, threshold, fallback)
+
+
 def _loop_one_step(orig):
     return lambda *a, **kw: orig(*a, **dict(kw, max_steps=1))
 
@@ -184,6 +189,7 @@ MUTANTS = {
     "denoise_no_final_norm": (D, "denoise_step", lambda o: _step_no_final_norm),
     "denoise_stops_after_one_step": (D, "denoise_block", _loop_one_step),
     "stack_ignores_coreset": (S, "stack_forward", _stack_ignores_coreset),
+    "unmask_ignores_blocks": (H, "unmask", _unmask_whole_call),
     "coreset_mass_counts": (C, "expert_mass", lambda o: _mass_counts),
     "coreset_cut_one_more": (C, "cut", _cut_one_more),
     "coreset_mass_ties_high_id": (C, "mass_order", lambda o: _order_ties_high),
@@ -226,6 +232,8 @@ PINS = [
     P.test_denoise_step_is_its_parts_composed,
     P.test_denoise_confident_block_finishes_in_one_step,
     P.test_denoise_with_coreset_selector,
+    P.test_unmask_rule_per_block,
+    P.test_denoise_multiblock_equals_blocks_alone,
     P.test_verify_bound_matches_page_points,
     P.test_verify_entropy_and_probabilities_closed_form,
     P.test_verify_threshold_decision_and_prefix,

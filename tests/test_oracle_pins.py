@@ -621,6 +621,41 @@ def test_denoise_with_coreset_selector():
     assert np.array_equal(y, ref)
 
 
+def test_unmask_rule_per_block():
+    """Several blocks in one call: the rule applies to each block on its own.
+    Block 0 has a row above the threshold, block 1 none: per block, block 1
+    still commits its most confident masked row (the fallback), while the
+    rule over the whole call would commit block 0's row only."""
+    from oracle import head as oh
+    M = 7
+    tokens = np.array([M, M, 3, M, M, M, M, M])
+    argmax = np.arange(10, 18)
+    conf = np.array([0.97, 0.5, 0.99, 0.2, 0.1, 0.6, 0.3, 0.6], dtype=np.float32)
+    whole, wc = oh.unmask(tokens, argmax, conf, M, 0.95)
+    assert list(np.flatnonzero(wc)) == [0]
+    per, pc = oh.unmask(tokens, argmax, conf, M, 0.95, block=4)
+    assert list(np.flatnonzero(pc)) == [0, 5]         # equal confidences: lower position
+    assert per[5] == 15 and per[7] == M and per[2] == 3
+
+
+def test_denoise_multiblock_equals_blocks_alone():
+    """Three blocks of six slots denoised together: tokens never interact and
+    each block has its own rule, so the result is each block's own loop, and
+    every step commits at least one slot of every block still masked."""
+    from oracle import denoise
+    layers, emb, wh = _tiny_model(seed=5)
+    rng = np.random.default_rng(8)
+    tokens = np.full(18, 5)
+    tokens[[1, 8, 15]] = rng.integers(10, 90, 3)
+    final, commits = denoise.denoise_block(tokens, emb, layers, wh, 2, 5, 0.95, block=6)
+    alone = [denoise.denoise_block(tokens[b:b + 6], emb, layers, wh, 2, 5, 0.95)
+             for b in range(0, 18, 6)]
+    assert np.array_equal(final, np.concatenate([f for f, _ in alone]))
+    assert len(commits) == max(len(c) for _, c in alone)
+    for i, c in enumerate(commits):
+        assert c == sum(cs[i] for _, cs in alone if i < len(cs))
+
+
 def test_denoise_confident_block_finishes_in_one_step():
     """A threshold no probability can miss (0 < conf always) commits every
     masked slot in the first step; a threshold above 1 commits one per step."""
