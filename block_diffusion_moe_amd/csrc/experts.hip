@@ -10,8 +10,8 @@
 // 64-byte k-slice of 16 rows), while the few token rows come from L2.
 //
 // Work is indexed by the slot table of touched expert groups the select step
-// builds ({expert, offset, count}; the shared expert, group E, first, then
-// the heavy ones); workgroups past its end exit at once.  A workgroup loads
+// builds ({expert, offset, count, slots of the group}; the shared expert,
+// group E, first, then the heavy ones); workgroups past its end exit at once.  A workgroup loads
 // its slot, the first token rows of its group, then its weight burst; no
 // weight load sits behind a branch (k-steps past K read k-step 0 and are
 // zeroed by a select), so the compiler keeps every load in flight.
@@ -249,6 +249,19 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 #ifndef BDM_WIDE_DN_GROUPS
 #define BDM_WIDE_DN_GROUPS 1
 #endif
+#ifndef BDM_WIDE_XCD
+#define BDM_WIDE_XCD 1
+#endif
+#ifndef BDM_WIDE_REUSE
+#define BDM_WIDE_REUSE 1
+#endif
+// weight loads of the many-token kernels: through the caches when another
+// slot reads the same weights (TEMP), else streamed
+template <bool TEMP>
+__device__ __forceinline__ u32x4 ld16_w(const void* p) {
+  if constexpr (TEMP && BDM_WIDE_REUSE) return ld16(p);
+  else return ld16_stream(p);
+}
 constexpr int kWideMt = 4;                             // 16-token row tiles per work item
 constexpr int kWideGuGroups = BDM_WIDE_GU_GROUPS;      // 16-column groups of I per gate/up item
 constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per wave in down
@@ -260,26 +273,19 @@ constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per
 // requested as soon as the current one has been multiplied.  The 8 partial
 // products of a group meet in LDS (double-buffered, one barrier per group)
 // and are summed in wave order; silu(g) * u is stored as bf16.
-template <int KSW>
-__global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
+template <int KSW, bool TEMP>
+__device__ __forceinline__ void gateup_wide_item(
+    float (*part)[2][kGuWaves][kWideMt][4][kWave], int* srow, const int4 slot, int run,
     const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
     const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
-    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
-    uint16_t* __restrict__ act) {
-  static_assert(kGuWaves == 8, "8 waves split K");
+    const int32_t* __restrict__ pair_rows, uint16_t* __restrict__ act) {
   constexpr int MT = kWideMt;
-  __shared__ float part[2][2][kGuWaves][MT][4][kWave];   // [gate/up][buffer]: 128 KB
-  __shared__ int srow[16 * MT];
-
   const int ngi = I / 16;                                 // column groups of I
-  const int runs = (ngi + kWideGuGroups - 1) / kWideGuGroups;
-  const int4 slot = slots[blockIdx.x / runs];
   const int e = slot.x;
   const int off = slot.y;
   const int m = slot.z < 16 * MT ? slot.z : 16 * MT;
-  if (!slot_ok(e, off, slot.z, E, P, ws_gate != nullptr)) return;
-  const int q0 = (blockIdx.x % runs) * kWideGuGroups;    // first column group
+  const int q0 = run * kWideGuGroups;                     // first column group
   const int nq = (ngi - q0) < kWideGuGroups ? (ngi - q0) : kWideGuGroups;
   const int K1 = k + 1;
   const int tid = threadIdx.x;
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
     const FragPtr f = q < nq ? frag_ptr(W, wrow + 16L * (q0 + q), H, lane, layout)
                              : FragPtr{x + c * 8, 0};
 #pragma unroll
-    for (int s = 0; s < KSW; ++s) b[s] = ld16_stream(f.p + (s0 + s) * f.step);
+    for (int s = 0; s < KSW; ++s) b[s] = ld16_w<TEMP>(f.p + (s0 + s) * f.step);
   };
   // pair rows first, then the weight burst (in-order completion: the rows
   // can be waited for without waiting for the weights)
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
     for (int s = 0; s < KSW; ++s) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
-      b[s] = ld16_stream(fn.p + (s0 + s) * fn.step);
+      b[s] = ld16_w<TEMP>(fn.p + (s0 + s) * fn.step);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -369,6 +375,50 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
   }
 }
 
+template <int KSW>
+__global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
+    const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
+    const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
+    const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    const int32_t* __restrict__ info, int nslots, uint16_t* __restrict__ act) {
+  static_assert(kGuWaves == 8, "8 waves split K");
+  __shared__ float part[2][2][kGuWaves][kWideMt][4][kWave];   // [gate/up][buffer]: 128 KB
+  __shared__ int srow[16 * kWideMt];
+
+  const int runs = (I / 16 + kWideGuGroups - 1) / kWideGuGroups;
+  int si, run;
+  if (BDM_WIDE_XCD) {
+    // workgroup b runs on XCD b % 8: XCD x takes items [x Q, x Q + Q) of
+    // the n slots x runs items in run-major order, so the chunks of one
+    // expert's column run are adjacent, on one XCD, at the same time
+    int n = info[0];
+    n = n < 0 ? 0 : (n > nslots ? nslots : n);
+    const int N = n * runs;
+    const int Q = (N + 7) / 8;
+    const int ii = static_cast<int>(blockIdx.x) / 8;
+    const int w = static_cast<int>(blockIdx.x % 8) * Q + ii;
+    if (ii >= Q || w >= N) return;
+    si = w % n;
+    run = w / n;
+  } else {
+    si = blockIdx.x / runs;
+    run = blockIdx.x % runs;
+  }
+  const int4 slot = slots[si];
+  // past the touched groups (-1), or a slot that is not a valid group
+  if (!slot_ok(slot.x, slot.y, slot.z, E, P, ws_gate != nullptr)) return;
+  // a group split over several slots is read once per slot: those reads
+  // go through the caches (the sibling slots run next to it), the others
+  // stream
+  if (slot.w > 1)
+    gateup_wide_item<KSW, true>(part, srow, slot, run, x, H, I, E, k, P, layout, w_gate, w_up,
+                                ws_gate, ws_up, pair_rows, act);
+  else
+    gateup_wide_item<KSW, false>(part, srow, slot, run, x, H, I, E, k, P, layout, w_gate, w_up,
+                                 ws_gate, ws_up, pair_rows, act);
+}
+
 // down: work item = (slot, 8 waves x kWideDnGroups groups of 16 rows of H).
 // The slot's activation rows are staged once in LDS in MFMA operand order
 // (tile (mt, s) = 64 lanes x 16 B, conflict-free reads); every wave then
@@ -378,33 +428,26 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
 #ifndef BDM_DN_WIDE_WAVES_PER_EU
 #define BDM_DN_WIDE_WAVES_PER_EU 4     // two workgroups per CU (<= 128 registers)
 #endif
-template <int KSMAX>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
-    BDM_DN_WIDE_WAVES_PER_EU, BDM_DN_WIDE_WAVES_PER_EU))) void down_wide_kernel(
+template <int KSMAX, bool TEMP>
+__device__ __forceinline__ void down_wide_item(
+    u32x4 (*at)[KSMAX][kWave], int* srow, const int4 slot, int run,
     const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
     const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
-    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
-    float* __restrict__ ypair) {
+    const int32_t* __restrict__ pair_rows, float* __restrict__ ypair) {
   constexpr int MT = kWideMt;
   constexpr int NW = 8;
-  __shared__ u32x4 at[MT][KSMAX][kWave];               // 64 KB at KSMAX = 16
-  __shared__ int srow[16 * MT];
-
   const int ngh = H / 16;
   const int per = NW * kWideDnGroups;                  // groups per work item
-  const int runs = (ngh + per - 1) / per;
-  const int4 slot = slots[blockIdx.x / runs];
   const int e = slot.x;
   const int off = slot.y;
   const int m = slot.z < 16 * MT ? slot.z : 16 * MT;
-  if (!slot_ok(e, off, slot.z, E, P, ws_down != nullptr)) return;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
   const int KS = I / 32;
-  const int gbase = (blockIdx.x % runs) * per + wave * kWideDnGroups;
+  const int gbase = run * per + wave * kWideDnGroups;
 
   const uint16_t* W = e == E ? ws_down : w_down;
   const long wrow = (e == E) ? 0 : static_cast<long>(e) * H;
@@ -417,7 +460,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
   };
   auto ldk = [&](FragPtr f, int s) -> u32x4 {
     const bool on = s < KS;
-    const u32x4 v = ld16_stream(f.p + (on ? s : 0) * f.step);
+    const u32x4 v = ld16_w<TEMP>(f.p + (on ? s : 0) * f.step);
     return on ? v : u32x4{0u, 0u, 0u, 0u};
   };
   const int prow = tid < 16 * MT ? clamp_row(pair_rows[off + (tid < m ? tid : 0)], P) : 0;
@@ -483,6 +526,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
         }
     }
   }
+}
+
+template <int KSMAX>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    BDM_DN_WIDE_WAVES_PER_EU, BDM_DN_WIDE_WAVES_PER_EU))) void down_wide_kernel(
+    const uint16_t* __restrict__ act, int H, int I, int E, int P, int layout,
+    const uint16_t* __restrict__ w_down, const uint16_t* __restrict__ ws_down,
+    const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
+    float* __restrict__ ypair) {
+  __shared__ u32x4 at[kWideMt][KSMAX][kWave];          // 64 KB at KSMAX = 16
+  __shared__ int srow[16 * kWideMt];
+  // item b = (slot b / runs, run b % runs): with 16 runs (H = 2048) run r of
+  // every slot lands on XCD r % 8, so sibling slots of one group meet there
+  const int runs = (H / 16 + 8 * kWideDnGroups - 1) / (8 * kWideDnGroups);
+  const int4 slot = slots[blockIdx.x / runs];
+  if (!slot_ok(slot.x, slot.y, slot.z, E, P, ws_down != nullptr)) return;
+  const int run = blockIdx.x % runs;
+  if (slot.w > 1)
+    down_wide_item<KSMAX, true>(at, srow, slot, run, act, H, I, E, P, layout, w_down, ws_down,
+                                pair_rows, ypair);
+  else
+    down_wide_item<KSMAX, false>(at, srow, slot, run, act, H, I, E, P, layout, w_down, ws_down,
+                                 pair_rows, ypair);
 }
 
 // One workgroup per token; a thread owns 8 consecutive columns and issues all
@@ -588,14 +654,16 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
     const int dn_runs = (H / 16 + 8 * kWideDnGroups - 1) / (8 * kWideDnGroups);
     using GuWide = void (*)(const uint16_t*, int, int, int, int, int, int, const uint16_t*,
                             const uint16_t*, const uint16_t*, const uint16_t*, const int4*,
-                            const int32_t*, uint16_t*);
+                            const int32_t*, const int32_t*, int, uint16_t*);
     const GuWide guw = ksw == 1   ? &gateup_wide_kernel<1>
                        : ksw == 2 ? &gateup_wide_kernel<2>
                        : ksw == 4 ? &gateup_wide_kernel<4>
                                   : &gateup_wide_kernel<8>;
-    guw<<<groups * gu_runs, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up,
-                                                  ws_gate, ws_up, meta.slots, meta.pair_rows,
-                                                  meta.act);
+    // (the XCD mapping needs every (XCD, index) pair up to ceil(items / 8))
+    const int gu_grid = BDM_WIDE_XCD ? (groups * gu_runs + 7) / 8 * 8 : groups * gu_runs;
+    guw<<<gu_grid, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
+                                          ws_up, meta.slots, meta.pair_rows, meta.info, groups,
+                                          meta.act);
     down_wide_kernel<16><<<groups * dn_runs, 512, 0, s>>>(meta.act, H, I, E, P, layout, w_down,
                                                           ws_down, meta.slots, meta.pair_rows,
                                                           meta.ypair);

@@ -38,7 +38,7 @@ struct MoeMeta {
   float* topk_w;        // [T][k]        their weights
   float* topk_p;        // [T][k]        first-pass probabilities (block coreset selector)
   int32_t* info;        // [4]           [0] number of touched expert groups
-  int4* slots;          // [E+1]         {expert, offset, count, 0} per touched group, then -1
+  int4* slots;          // [E+1]         {expert, offset, count, slots of the group} per slot, then -1
   int32_t* pair_rows;   // [T*(k+1)]     (token, slot) rows grouped by expert
   uint16_t* act;        // [T*(k+1)][I]  bf16 SwiGLU activations
   float* ypair;         // [T*(k+1)][H]  fp32 expert outputs

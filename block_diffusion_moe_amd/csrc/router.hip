@@ -346,14 +346,15 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
         const int e = lane * epl + j;
         if (c[j] >= 16) {
           const int pos = nsh + hb + ho;
+          const int nch = (c[j] + kSlotChunk - 1) / kSlotChunk;
           int q = 0;
           for (int o = 0; o < c[j]; o += kSlotChunk, ++q) {
             const int m = c[j] - o < kSlotChunk ? c[j] - o : kSlotChunk;
-            slots[pos + q] = int4{e, pref + o, m, 0};
+            slots[pos + q] = int4{e, pref + o, m, nch};
           }
           ho += q;
         } else {
-          slots[nsh + nh + lb + lo] = int4{e, pref, c[j], 0};
+          slots[nsh + nh + lb + lo] = int4{e, pref, c[j], 1};
           ++lo;
         }
         eoff[e] = pref;
@@ -363,7 +364,7 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
     const int n = nsh + nh + nl;
     for (int i = lane; i < nsh; i += kWave) {
       const int o = i * kSlotChunk;
-      slots[i] = int4{E, o, T - o < kSlotChunk ? T - o : kSlotChunk, 0};
+      slots[i] = int4{E, o, T - o < kSlotChunk ? T - o : kSlotChunk, nsh};
     }
     const int nmax = moe_max_slots(T, E, k, has_shared);
     for (int i = n + lane; i < nmax; i += kWave) slots[i] = int4{-1, 0, 0, 0};
