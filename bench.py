@@ -196,6 +196,14 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     ms_step_graph = start.elapsed_time(stop) / args.steps
+    # and once more with an event pair around every replay (percentiles)
+    evg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        evg[i][0].record()
+        graphs[i % args.sets].replay()
+        evg[i][1].record()
+    torch.cuda.synchronize()
+    graph_ms = np.array([e[0].elapsed_time(e[1]) for e in evg])
     del graphs
 
     # the head GEMM kernel alone: the same launches back to back over the
@@ -313,6 +321,36 @@ def main():
             "mfma_frac_of_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del xb, wsb, yb, ib
 
+    # the head statistics over the same 16 / 32 / 64 blocks (all their rows
+    # in one call: every 64-row pass in one launch), rotated head sets
+    head_multi = {}
+    P = bdm.bdm_head_stat_parts()
+    g_h = torch.Generator(device=dev)
+    g_h.manual_seed(4242)
+    for nb in (16, 32, 64):
+        TB = nb * T
+        hb = torch.randn((TB, H), generator=g_h, device=dev).to(torch.bfloat16)
+        st = [torch.empty((TB, P), dtype=dt, device=dev)
+              for dt in (torch.float32, torch.float32, torch.int32)]
+        for r in range(args.sets):
+            bdm.bdm_lm_head_stats(hb, heads[r], HS.mask_id, *st)
+        nrep = max(8, args.steps // 4)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(nrep):
+            bdm.bdm_lm_head_stats(hb, heads[i % args.sets], HS.mask_id, *st)
+        stop.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(stop) * 1e3 / nrep
+        flops = 2.0 * TB * H * HS.V
+        head_multi[f"{nb}_blocks"] = {
+            "rows": TB, "us": round(us, 2), "rows_per_s": round(TB / (us * 1e-6), 1),
+            "head_GB_s": round(HEAD_BYTES / (us * 1e-6) / 1e9, 1),
+            "mfma_TFLOP_s": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac_of_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "us_if_one_launch_per_64_rows": round(gemm_loop_us * (TB // 64), 1)}
+        del hb, st
+
     u_mean = float(np.mean([touched[i % args.sets] for i in range(args.steps)]))
     moe_bytes = (u_mean + 1) * EXPERT_BYTES
     moe_gbs = moe_bytes / (moe_loop_us * 1e-6) / 1e9
@@ -372,6 +410,7 @@ def main():
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
         "moe_layer_multiblock": multi,
+        "head_stats_multiblock": head_multi,
         "head_verify_33_rows": {"us": round(verify_us, 2), "bytes": HEAD_BYTES,
                                 "GB_s": round(verify_gbs, 1),
                                 "frac_of_peak": round(verify_gbs / PEAK_HBM_GBS, 4)},
@@ -381,6 +420,8 @@ def main():
         "ms_per_step_event_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4)
                                           for q in (10, 50, 90)],
         "ms_per_step_graph_replay": round(ms_step_graph, 4),
+        "ms_per_step_graph_replay_p10_p50_p90": [round(float(np.percentile(graph_ms, q)), 4)
+                                                 for q in (10, 50, 90)],
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -255,11 +255,20 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
 //
 // VERIFY (the verify epilogue): no row is masked and the state is a VStat
 // (adds q = sum e^(l-m)(l-m) and the logit of the row's candidate cand[t]).
-template <int KSW, int MT, bool VERIFY>
+//
+// Several passes in one launch (npass > 1, rows [tok0, tok0 + ntok) cut into
+// npass passes of rpp rows): the vocabulary keeps its gridDim.x ranges, and
+// the npass workgroups that run the passes of a group of npass consecutive
+// ranges sit on one XCD (workgroup b runs on XCD b % 8) and start together,
+// so the weights they stream are read from HBM about once and from L2 by the
+// others (REUSE: loads that allocate in the caches).  Each workgroup streams
+// its ranges back to back and writes one partial per (row, range), the same
+// numbers as one launch per pass.
+template <int KSW, int MT, bool VERIFY, bool REUSE>
 __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     const uint16_t* __restrict__ h, int H, const uint16_t* __restrict__ w, int V, int voff,
-    int layout, int32_t mask_id, int tok0, int ntok, float* __restrict__ pm,
-    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride,
+    int layout, int32_t mask_id, int tok0, int ntok, int npass, int rpp,
+    float* __restrict__ pm, float* __restrict__ ps, int32_t* __restrict__ pa, int pstride,
     const int32_t* __restrict__ cand, int ncand, float* __restrict__ pq,
     float* __restrict__ plc) {
   static_assert(kHeadWaves == 8 && (MT == 2 || MT == 4), "4 token rows of a tile per wave");
@@ -271,9 +280,23 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   const int lane = tid % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
+  // this workgroup's pass and first range (one pass per launch unless REUSE)
+  const int np = REUSE ? npass : 1;
+  int pass = 0, qa = blockIdx.x;
+  if (np > 1) {
+    const int i = static_cast<int>(blockIdx.x) / 8;
+    const int per_xcd = static_cast<int>(gridDim.x) / 8 / np;   // range groups per XCD
+    pass = i % np;
+    qa = (static_cast<int>(blockIdx.x % 8) * per_xcd + i / np) * np;
+  }
+  const int pt0 = tok0 + pass * rpp;                            // this pass's rows
+  const int rem = tok0 + ntok - pt0;
+  const int pn = np == 1 ? ntok : (rem < rpp ? rem : rpp);
+  if (pn <= 0) return;
   const long ngroups = (V + 15) / 16;
-  const long G0 = static_cast<long>(blockIdx.x) * ngroups / gridDim.x;
-  const long G1 = static_cast<long>(blockIdx.x + 1) * ngroups / gridDim.x;
+  auto bound = [&](int q) -> long { return static_cast<long>(q) * ngroups / gridDim.x; };
+  const long G0 = bound(qa);
+  const long G1 = bound(qa + np);
   const int n = static_cast<int>(G1 - G0);
   const int s0 = wave * KSW;
 
@@ -288,7 +311,10 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   auto load = [&](long gi, u32x4(&b)[KSW]) {
     const FragPtr f = wfrag(gi);
 #pragma unroll
-    for (int s = 0; s < KSW; ++s) b[s] = ld16_stream(f.p + (s0 + s) * f.step);
+    for (int s = 0; s < KSW; ++s) {
+      if constexpr (REUSE) b[s] = ld16(f.p + (s0 + s) * f.step);
+      else b[s] = ld16_stream(f.p + (s0 + s) * f.step);
+    }
   };
   // NB groups of weights in flight (ping-pong, or three buffers when the
   // 32-row tile leaves the registers for it)
@@ -303,8 +329,8 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   u32x4 a[MT][KSW];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const bool ok = 16 * mt + c < ntok;
-    const uint16_t* r = h + static_cast<size_t>(tok0 + (ok ? 16 * mt + c : 0)) * H + g * 8;
+    const bool ok = 16 * mt + c < pn;
+    const uint16_t* r = h + static_cast<size_t>(pt0 + (ok ? 16 * mt + c : 0)) * H + g * 8;
 #pragma unroll
     for (int s = 0; s < KSW; ++s) {
       const u32x4 x = ld16(r + (s0 + s) * 32);
@@ -321,7 +347,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     st[f] = softstat_empty();
     vs[f] = vstat_empty();
     mycand[f] = -1;
-    if (VERIFY) mycand[f] = (tok0 + ot < ncand && ot < ntok) ? cand[tok0 + ot] : -1;
+    if (VERIFY) mycand[f] = (pt0 + ot < ncand && ot < pn) ? cand[pt0 + ot] : -1;
   }
 
   auto step = [&](int j, u32x4(&b)[KSW]) {
@@ -375,37 +401,76 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
       }
     }
   };
-  int j = 0;
-  for (; j + NB - 1 < n; j += NB) {
+  // the partials of range q for this lane's tokens (the 16 columns of a
+  // token sit in one DPP row, each token in one wave)
+  auto write_partials = [&](int q) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) step(j + u, bufs[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (j + u < n) step(j + u, bufs[u]);
-
-  // the 16 columns of a token sit in one DPP row; each token in one wave
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
-    const size_t o = static_cast<size_t>(tok0 + ot) * pstride + blockIdx.x;
-    if constexpr (VERIFY) {
-      const VStat r = row_merge_vstat(vs[f]);
-      if (c == 0 && ot < ntok) {
-        pm[o] = r.m;
-        ps[o] = r.s;
-        pa[o] = r.a;
-        pq[o] = r.q;
-        plc[o] = r.lc;
-      }
-    } else {
-      const SoftStat r = row_merge_stat(st[f]);
-      if (c == 0 && ot < ntok) {
-        pm[o] = r.m;
-        ps[o] = r.s;
-        pa[o] = r.a;
+    for (int f = 0; f < NF; ++f) {
+      const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
+      const size_t o = static_cast<size_t>(pt0 + ot) * pstride + q;
+      if constexpr (VERIFY) {
+        const VStat r = row_merge_vstat(vs[f]);
+        if (c == 0 && ot < pn) {
+          pm[o] = r.m;
+          ps[o] = r.s;
+          pa[o] = r.a;
+          pq[o] = r.q;
+          plc[o] = r.lc;
+        }
+      } else {
+        const SoftStat r = row_merge_stat(st[f]);
+        if (c == 0 && ot < pn) {
+          pm[o] = r.m;
+          ps[o] = r.s;
+          pa[o] = r.a;
+        }
       }
     }
+  };
+  if constexpr (!REUSE) {
+    int j = 0;
+    for (; j + NB - 1 < n; j += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) step(j + u, bufs[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (j + u < n) step(j + u, bufs[u]);
+    write_partials(blockIdx.x);
+  } else {
+    // range qa + qi ends before group nb (relative to G0); flush writes its
+    // partials and starts the next range
+    int qi = 0;
+    long nb = bound(qa + 1) - G0;
+    auto flush = [&]() {
+      write_partials(qa + qi);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        st[f] = softstat_empty();
+        vs[f] = vstat_empty();
+      }
+      ++qi;
+      nb = bound(qa + qi + 1) - G0;
+    };
+    // ranges that end at or before group jj (workgroup-uniform)
+    auto advance = [&](int jj) {
+      while (qi < np - 1 && jj >= nb) flush();
+    };
+    int j = 0;
+    for (; j + NB - 1 < n; j += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        advance(j + u);
+        step(j + u, bufs[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (j + u < n) {
+        advance(j + u);
+        step(j + u, bufs[u]);
+      }
+    while (qi < np) flush();
   }
 }
 
@@ -607,16 +672,16 @@ static HeadKernel head_kernel_for(int H) {
 }
 
 using CoopKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int, int32_t, int,
-                            int, float*, float*, int32_t*, int, const int32_t*, int, float*,
-                            float*);
+                            int, int, int, float*, float*, int32_t*, int, const int32_t*, int,
+                            float*, float*);
 
-template <int MT, bool VERIFY>
+template <int MT, bool VERIFY, bool REUSE = false>
 static CoopKernel coop_kernel_for(int H) {
   switch (H / 256) {
-    case 1: return &head_coop_kernel<1, MT, VERIFY>;
-    case 2: return &head_coop_kernel<2, MT, VERIFY>;
-    case 4: return &head_coop_kernel<4, MT, VERIFY>;
-    case 8: return &head_coop_kernel<8, MT, VERIFY>;
+    case 1: return &head_coop_kernel<1, MT, VERIFY, REUSE>;
+    case 2: return &head_coop_kernel<2, MT, VERIFY, REUSE>;
+    case 4: return &head_coop_kernel<4, MT, VERIFY, REUSE>;
+    case 8: return &head_coop_kernel<8, MT, VERIFY, REUSE>;
     default: return nullptr;
   }
 }
@@ -629,12 +694,28 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
 #ifndef BDM_HEAD_COOP
 #define BDM_HEAD_COOP 1
 #endif
+#ifndef BDM_HEAD_PASS_PAR
+#define BDM_HEAD_PASS_PAR 1
+#endif
   if (BDM_HEAD_COOP && H % 256 == 0 && coop_kernel_for<2, false>(H)) {
+    // more rows than one pass takes: every pass in one launch (a power of
+    // two of them, at most 32, so that whole groups of them fill each XCD)
+    const int passes = (T + kCoopChunk - 1) / kCoopChunk;
+    int np = 1;
+    while (np < passes) np *= 2;
+    if (BDM_HEAD_PASS_PAR && np > 1 && np <= 32 && grid % (8 * np) == 0) {
+      const int rpp = (T + np - 1) / np;                  // <= kCoopChunk
+      CoopKernel k = rpp <= 32 ? coop_kernel_for<2, false, true>(H)
+                               : coop_kernel_for<4, false, true>(H);
+      k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, 0, T, np, rpp, pm,
+                                         ps, pa, pstride, nullptr, 0, nullptr, nullptr);
+      return;
+    }
     for (int t0 = 0; t0 < T; t0 += kCoopChunk) {
       const int n = (T - t0) < kCoopChunk ? (T - t0) : kCoopChunk;
       CoopKernel k = n <= 32 ? coop_kernel_for<2, false>(H) : coop_kernel_for<4, false>(H);
-      k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, pm, ps, pa,
-                                         pstride, nullptr, 0, nullptr, nullptr);
+      k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, voff, layout, mask_id, t0, n, 1, n, pm, ps,
+                                         pa, pstride, nullptr, 0, nullptr, nullptr);
     }
     return;
   }
@@ -654,8 +735,8 @@ void launch_head_verify_stats(const uint16_t* h, int T, int H, const uint16_t* w
   for (int t0 = 0; t0 < T; t0 += kCoopChunk) {
     const int n = (T - t0) < kCoopChunk ? (T - t0) : kCoopChunk;
     CoopKernel k = n <= 32 ? coop_kernel_for<2, true>(H) : coop_kernel_for<4, true>(H);
-    k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, 0, layout, -1, t0, n, pm, ps, pa, pstride,
-                                       cand, ncand, pq, plc);
+    k<<<grid, kHeadWaves * 64, 0, s>>>(h, H, w, V, 0, layout, -1, t0, n, 1, n, pm, ps, pa,
+                                       pstride, cand, ncand, pq, plc);
   }
 }
 

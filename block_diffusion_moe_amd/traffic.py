@@ -40,8 +40,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-# the head GEMM of the unmask step (either variant; not the verify epilogue's
-# instance head_coop_kernel<KSW, true>)
+# the head GEMM of the unmask step over one block (either kernel; not the
+# verify epilogue's instance head_coop_kernel<KSW, MT, true, false> nor the
+# many-row one head_coop_kernel<KSW, MT, false, true>)
 HEAD_KERNELS = ("head_coop_kernel", "head_tile_kernel")
 HEAD_SOURCES = ("head.hip", "device.hpp", "internal.hpp")
 
@@ -127,8 +128,8 @@ def summarize(a):
         wb = w_fac * 1024.0 * sum(wv) / len(wv)
         rows.append((n, len(fv), fb, wb))
         short = n.split("::")[-1]
-        verify_variant = short.startswith("head_coop_kernel<") and short.endswith(", true>")
-        if short.startswith(HEAD_KERNELS) and not verify_variant:
+        other_variant = short.startswith("head_coop_kernel<") and "true" in short
+        if short.startswith(HEAD_KERNELS) and not other_variant:
             head_bytes = fb + wb if head_bytes is None else max(head_bytes, fb + wb)
     out = [f"<!-- source_sha256 = {kernel_source_digest()} -->"]
     if head_bytes is not None:

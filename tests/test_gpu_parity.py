@@ -304,13 +304,17 @@ def test_head_two_phase_and_vocab_shards(bdm, layout):
     compare_head((tok, am, cf, nc), o, blk.tokens.cpu().numpy())
 
 
-@pytest.mark.parametrize("T", [33, 64, 100])
-def test_head_wide_pass_equals_32_row_calls(bdm, T):
-    """Up to 64 rows share one pass over the head weights; every row's
-    partial statistics equal those of the same row computed in a call of at
-    most 32 rows, bit for bit (the per-row arithmetic does not change)."""
-    say(f"case head wide pass T={T}")
-    s = synth.HeadShape(T=T, H=2048, V=70001, mask_id=5)
+@pytest.mark.parametrize("T,V", [(33, 70001), (64, 70001), (100, 70001), (130, 70001),
+                                 (300, 70001), (2048, 70001), (512, 248320), (97, 1000)])
+def test_head_wide_pass_equals_32_row_calls(bdm, T, V):
+    """Up to 64 rows share one pass over the head weights, and more rows run
+    as several passes in one launch (2 .. 32 of them, workgroups of one
+    vocabulary range side by side); every row's partial statistics equal
+    those of the same row computed in a call of at most 32 rows, bit for bit
+    (the per-row arithmetic and the vocabulary ranges do not change).  V =
+    1000 leaves most ranges empty."""
+    say(f"case head wide pass T={T} V={V}")
+    s = synth.HeadShape(T=T, H=2048, V=V, mask_id=5)
     W = synth.head_weights(s, 6, device=DEV)
     blk = synth.head_block(s, W, block_seed=T, n_boost=8)
     P = bdm.bdm_head_stat_parts()
@@ -326,6 +330,20 @@ def test_head_wide_pass_equals_32_row_calls(bdm, T):
         torch.cuda.synchronize()
         for x, z in zip(wide, narrow):
             assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+
+
+@LAYOUTS
+@pytest.mark.parametrize("T", [65, 130, 256])
+def test_head_many_rows(bdm, T, layout):
+    """Several 64-row passes in one launch against the oracle: every row's
+    argmax/conf and the commit decisions."""
+    say(f"case head many rows T={T} layout={layout}")
+    s = synth.HeadShape(T=T, H=2048, V=70001, mask_id=777)
+    W = synth.head_weights(s, T + 1, device=DEV)
+    blk = synth.head_block(s, W, block_seed=T + 2, n_boost=T // 3, committed_rows=5)
+    out = run_head(bdm, blk, layout=layout)
+    o = oracle_head(blk)
+    compare_head(out, o, blk.tokens.cpu().numpy())
 
 
 @pytest.mark.parametrize("layout", [0, 1])
