@@ -350,21 +350,9 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     if (VERIFY) mycand[f] = (pt0 + ot < ncand && ot < pn) ? cand[pt0 + ot] : -1;
   }
 
-  auto step = [&](int j, u32x4(&b)[KSW]) {
-    f32x4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KSW; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
-    load(G0 + j + NB, b);
-    float* pp = &part[j & 1][wave][0][0][0];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pp[(mt * 4 + i) * kWave + lane] = acc[mt][i];
-    __syncthreads();
+  // fold group j's partial products (in LDS buffer j & 1) into the lanes'
+  // online-softmax states
+  auto fold = [&](int j) {
     const int v = static_cast<int>((G0 + j) * 16) + c;
     const bool live = v < V && v + voff != mask_id;
 #pragma unroll
@@ -400,6 +388,30 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
         x.m = nm;
       }
     }
+  };
+  // the group's products (and the next loads), into LDS buffer j & 1
+  auto mma = [&](int j, u32x4(&b)[KSW], f32x4(&acc)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSW; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(a[mt][s], b[s], acc[mt]);
+    load(G0 + j + NB, b);
+  };
+  auto store = [&](int j, const f32x4(&acc)[MT]) {
+    float* pp = &part[j & 1][wave][0][0][0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[(mt * 4 + i) * kWave + lane] = acc[mt][i];
+  };
+  auto step = [&](int j, u32x4(&b)[KSW]) {
+    f32x4 acc[MT];
+    mma(j, b, acc);
+    store(j, acc);
+    __syncthreads();
+    fold(j);
   };
   // the partials of range q for this lane's tokens (the 16 columns of a
   // token sit in one DPP row, each token in one wave)
@@ -456,20 +468,26 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
     auto advance = [&](int jj) {
       while (qi < np - 1 && jj >= nb) flush();
     };
+    // software-pipelined: group j's products are computed while group j-1
+    // is folded (its partials were published by the previous barrier), so
+    // the fold's LDS reads and exponentials hide behind the MFMAs
+    auto pstep = [&](int j, u32x4(&b)[KSW]) {
+      f32x4 acc[MT];
+      mma(j, b, acc);
+      if (j > 0) fold(j - 1);
+      store(j, acc);
+      advance(j);                      // ranges that end with group j - 1
+      __syncthreads();
+    };
     int j = 0;
     for (; j + NB - 1 < n; j += NB) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        advance(j + u);
-        step(j + u, bufs[u]);
-      }
+      for (int u = 0; u < NB; ++u) pstep(j + u, bufs[u]);
     }
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
-      if (j + u < n) {
-        advance(j + u);
-        step(j + u, bufs[u]);
-      }
+      if (j + u < n) pstep(j + u, bufs[u]);
+    if (n > 0) fold(n - 1);
     while (qi < np) flush();
   }
 }
