@@ -321,6 +321,44 @@ def main():
             "mfma_frac_of_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del xb, wsb, yb, ib
 
+    # the load-skew batch: 8 blocks (256 tokens) through the same layers
+    # with a log-Zipf router bias (s = 1.1), so a few experts take most tokens
+    skew_x = [synth.moe_tokens(synth.SKEW, 700 + r, dev)[0] for r in range(args.sets)]
+    skew_b = [synth.zipf_router_bias(L.E, r, 1.1, dev) for r in range(args.sets)]
+    wsk = bdm.workspace(bdm.bdm_moe_workspace_bytes(256, H, L.I, L.E, L.k, True), dev)
+    yk = torch.empty((256, H), dtype=torch.bfloat16, device=dev)
+    ik = torch.empty((256, L.k), dtype=torch.int32, device=dev)
+    uk, hot = [], []
+
+    def skew_call(r, topk=None):
+        kw = kw_sets[r]
+        bdm.bdm_moe_block_forward(skew_x[r], sets[r][0].w_router, kw["w_gate"], kw["w_up"],
+                                  kw["w_down"], L.k, router_bias=skew_b[r], ws_gate=kw["ws_gate"],
+                                  ws_up=kw["ws_up"], ws_down=kw["ws_down"], y=yk, topk_idx=topk,
+                                  ws=wsk)
+    for r in range(args.sets):
+        skew_call(r, ik)
+        torch.cuda.synchronize()
+        cnt = torch.bincount(ik.reshape(-1).long(), minlength=L.E)
+        uk.append(int((cnt > 0).sum()))
+        hot.append(int(cnt.max()))
+    nrep = max(8, args.steps // 4)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(nrep):
+        skew_call(i % args.sets)
+    stop.record()
+    torch.cuda.synchronize()
+    sk_us = start.elapsed_time(stop) * 1e3 / nrep
+    ukm = float(np.mean([uk[i % args.sets] for i in range(nrep)]))
+    sk_bytes = (ukm + 1) * EXPERT_BYTES
+    skew = {"tokens": 256, "us": round(sk_us, 2),
+            "block_tokens_per_s": round(256 / (sk_us * 1e-6), 1),
+            "unique_experts": round(ukm, 2), "busiest_expert_tokens": hot, "bytes": int(sk_bytes),
+            "GB_s": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(sk_bytes / (sk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del skew_x, skew_b, wsk, yk, ik
+
     # the head statistics over the same 16 / 32 / 64 blocks (all their rows
     # in one call: every 64-row pass in one launch), rotated head sets
     head_multi = {}
@@ -410,6 +448,7 @@ def main():
                         "merge_us": round(merge_us, 2), "bytes": HEAD_BYTES,
                         "GB_s": round(head_gbs, 1), "frac_of_peak": round(head_gbs / PEAK_HBM_GBS, 4)},
         "moe_layer_multiblock": multi,
+        "moe_layer_skew_8_blocks": skew,
         "head_stats_multiblock": head_multi,
         "head_verify_33_rows": {"us": round(verify_us, 2), "bytes": HEAD_BYTES,
                                 "GB_s": round(verify_gbs, 1),

@@ -244,7 +244,10 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 // that of the kernels above (same K split, same summation order), so the
 // results are bit-identical to theirs.
 #ifndef BDM_WIDE_GU_GROUPS
-#define BDM_WIDE_GU_GROUPS 8
+#define BDM_WIDE_GU_GROUPS 8           // from kWideGuBigT tokens; 4 below
+#endif
+#ifndef BDM_WIDE_GU_BIG_T
+#define BDM_WIDE_GU_BIG_T 512
 #endif
 #ifndef BDM_WIDE_DN_GROUPS
 #define BDM_WIDE_DN_GROUPS 1
@@ -264,9 +267,10 @@ __device__ __forceinline__ u32x4 ld16_w(const void* p) {
 }
 constexpr int kWideMt = 4;                             // 16-token row tiles per work item
 constexpr int kWideGuGroups = BDM_WIDE_GU_GROUPS;      // 16-column groups of I per gate/up item
+constexpr int kWideGuBigT = BDM_WIDE_GU_BIG_T;         // (fewer slots below: 4 groups, more items)
 constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per wave in down
 
-// gate/up: work item = (slot, kWideGuGroups column groups).  The 8 waves
+// gate/up: work item = (slot, gpi column groups).  The 8 waves
 // split K = H (KSW k-steps each) and hold their K-slice of the slot's token
 // rows in registers; the weights stream one 16-row group at a time,
 // alternating gate and up, and each k-step of a matrix's next group is
@@ -275,7 +279,7 @@ constexpr int kWideDnGroups = BDM_WIDE_DN_GROUPS;      // 16-row groups of H per
 // and are summed in wave order; silu(g) * u is stored as bf16.
 template <int KSW, bool TEMP>
 __device__ __forceinline__ void gateup_wide_item(
-    float (*part)[2][kGuWaves][kWideMt][4][kWave], int* srow, const int4 slot, int run,
+    float (*part)[2][kGuWaves][kWideMt][4][kWave], int* srow, const int4 slot, int run, int gpi,
     const uint16_t* __restrict__ x, int H, int I, int E, int k, int P, int layout,
     const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
@@ -285,8 +289,8 @@ __device__ __forceinline__ void gateup_wide_item(
   const int e = slot.x;
   const int off = slot.y;
   const int m = slot.z < 16 * MT ? slot.z : 16 * MT;
-  const int q0 = run * kWideGuGroups;                     // first column group
-  const int nq = (ngi - q0) < kWideGuGroups ? (ngi - q0) : kWideGuGroups;
+  const int q0 = run * gpi;                               // first column group
+  const int nq = (ngi - q0) < gpi ? (ngi - q0) : gpi;
   const int K1 = k + 1;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -381,12 +385,12 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
     const uint16_t* __restrict__ w_gate, const uint16_t* __restrict__ w_up,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up,
     const int4* __restrict__ slots, const int32_t* __restrict__ pair_rows,
-    const int32_t* __restrict__ info, int nslots, uint16_t* __restrict__ act) {
+    const int32_t* __restrict__ info, int nslots, int gpi, uint16_t* __restrict__ act) {
   static_assert(kGuWaves == 8, "8 waves split K");
   __shared__ float part[2][2][kGuWaves][kWideMt][4][kWave];   // [gate/up][buffer]: 128 KB
   __shared__ int srow[16 * kWideMt];
 
-  const int runs = (I / 16 + kWideGuGroups - 1) / kWideGuGroups;
+  const int runs = (I / 16 + gpi - 1) / gpi;
   int si, run;
   if (BDM_WIDE_XCD) {
     // workgroup b runs on XCD b % 8: XCD x takes items [x Q, x Q + Q) of
@@ -412,11 +416,11 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
   // go through the caches (the sibling slots run next to it), the others
   // stream
   if (slot.w > 1)
-    gateup_wide_item<KSW, true>(part, srow, slot, run, x, H, I, E, k, P, layout, w_gate, w_up,
-                                ws_gate, ws_up, pair_rows, act);
+    gateup_wide_item<KSW, true>(part, srow, slot, run, gpi, x, H, I, E, k, P, layout, w_gate,
+                                w_up, ws_gate, ws_up, pair_rows, act);
   else
-    gateup_wide_item<KSW, false>(part, srow, slot, run, x, H, I, E, k, P, layout, w_gate, w_up,
-                                 ws_gate, ws_up, pair_rows, act);
+    gateup_wide_item<KSW, false>(part, srow, slot, run, gpi, x, H, I, E, k, P, layout, w_gate,
+                                 w_up, ws_gate, ws_up, pair_rows, act);
 }
 
 // down: work item = (slot, 8 waves x kWideDnGroups groups of 16 rows of H).
@@ -644,17 +648,22 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
   const dim3 gu(groups * (I / kGuCols)), dn(groups * ((H + kDnRows - 1) / kDnRows));
   const int KS = H / 32;
   const int KI = I / 32;
+// many-token kernels from 8 blocks: a skewed 8-block batch (its hottest
+// experts take ~250 tokens, four 64-token slots) runs 20% faster on them, an
+// even one 2% slower
 #ifndef BDM_WIDE_MIN_T
-#define BDM_WIDE_MIN_T 384
+#define BDM_WIDE_MIN_T 256
 #endif
   const int ksw = H / 256;
   if (T >= BDM_WIDE_MIN_T && H % 256 == 0 && (ksw == 1 || ksw == 2 || ksw == 4 || ksw == 8) &&
       KI <= 16) {
-    const int gu_runs = (I / 16 + kWideGuGroups - 1) / kWideGuGroups;
+    // fewer tokens, fewer slots: narrower gate/up items keep every CU busy
+    const int gpi = T >= kWideGuBigT ? kWideGuGroups : 4;
+    const int gu_runs = (I / 16 + gpi - 1) / gpi;
     const int dn_runs = (H / 16 + 8 * kWideDnGroups - 1) / (8 * kWideDnGroups);
     using GuWide = void (*)(const uint16_t*, int, int, int, int, int, int, const uint16_t*,
                             const uint16_t*, const uint16_t*, const uint16_t*, const int4*,
-                            const int32_t*, const int32_t*, int, uint16_t*);
+                            const int32_t*, const int32_t*, int, int, uint16_t*);
     const GuWide guw = ksw == 1   ? &gateup_wide_kernel<1>
                        : ksw == 2 ? &gateup_wide_kernel<2>
                        : ksw == 4 ? &gateup_wide_kernel<4>
@@ -663,7 +672,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
     const int gu_grid = BDM_WIDE_XCD ? (groups * gu_runs + 7) / 8 * 8 : groups * gu_runs;
     guw<<<gu_grid, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
                                           ws_up, meta.slots, meta.pair_rows, meta.info, groups,
-                                          meta.act);
+                                          gpi, meta.act);
     down_wide_kernel<16><<<groups * dn_runs, 512, 0, s>>>(meta.act, H, I, E, P, layout, w_down,
                                                           ws_down, meta.slots, meta.pair_rows,
                                                           meta.ypair);

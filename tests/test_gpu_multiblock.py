@@ -107,7 +107,7 @@ def test_multiblock_rows_equal_single_block_calls(bdm, T, zipf):
 def test_multiblock_small_full(bdm, shape, layout):
     """Small shapes whose groups exceed one work item (shared 65 = 64 + 1;
     routed groups of ~100-130 tokens), on both the few-token kernels and
-    (T >= 384, H of 256, 512, 1024 or 2048) the many-token ones, with partial
+    (T >= 256, H of 256, 512, 1024 or 2048) the many-token ones, with partial
     column runs (I = 96) and guarded k-steps: every output against the
     oracle."""
     T, H, E, I, k = shape
