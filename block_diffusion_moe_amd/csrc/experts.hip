@@ -429,6 +429,9 @@ __global__ __launch_bounds__(kGuWaves * 64, 1) void gateup_wide_kernel(
 // owns its own 16-row groups over the whole K = I, each k-step of its next
 // group requested as soon as the current one has been multiplied, and
 // stores fp32 results per (token, slot) row.
+#ifndef BDM_DN_STAGE_SKIP
+#define BDM_DN_STAGE_SKIP 1
+#endif
 #ifndef BDM_DN_WIDE_WAVES_PER_EU
 #define BDM_DN_WIDE_WAVES_PER_EU 4     // two workgroups per CU (<= 128 registers)
 #endif
@@ -487,11 +490,20 @@ __device__ __forceinline__ void down_wide_item(
 #pragma unroll
   for (int u0 = 0; u0 < NCH; u0 += NB) {
     u32x4 v[NB];
+    // a batch whose rows all lie past the slot's tokens stores zeros only
+    // (workgroup-uniform)
+    const bool live = !BDM_DN_STAGE_SKIP || 16 * ((u0 * NW * kWave / 64) / KSMAX) < m;
+    if (live) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int ch = tid + (u0 + u) * NW * kWave;
-      const int l = ch & 63, s = (ch >> 6) % KSMAX, r = 16 * ((ch >> 6) / KSMAX) + (l & 15);
-      v[u] = ld16(act + static_cast<size_t>(srow[r]) * I + (s < KS ? s : 0) * 32 + (l >> 4) * 8);
+      for (int u = 0; u < NB; ++u) {
+        const int ch = tid + (u0 + u) * NW * kWave;
+        const int l = ch & 63, s = (ch >> 6) % KSMAX, r = 16 * ((ch >> 6) / KSMAX) + (l & 15);
+        v[u] = ld16(act + static_cast<size_t>(srow[r]) * I + (s < KS ? s : 0) * 32 +
+                    (l >> 4) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {

@@ -34,7 +34,10 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
 
 constexpr int kRtWaves = 4;     // waves per router workgroup
 constexpr int kRtWideTiles = 4; // token tiles per router workgroup in many-block calls
-constexpr int kRtWideMinT = 512;
+#ifndef BDM_RT_WIDE_MIN_T
+#define BDM_RT_WIDE_MIN_T 512
+#endif
+constexpr int kRtWideMinT = BDM_RT_WIDE_MIN_T;
 constexpr int kRtMaxKs = 4;     // k-steps per wave: H <= kRouterParts * 4 * 4 * 32 = 2048
 
 // Partial logits over one K-part: part[z][t][e] = sum_{h in part z} x[t][h] w[e][h].
