@@ -240,9 +240,11 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 // work item (one slot: at most kSlotChunk = 64 tokens) holds all of them as
 // four 16-token MFMA row tiles.  Every weight byte is still read once per
 // slot, straight into registers, while the token rows are read once per
-// work item (not once per 16 weight rows).  Per element the arithmetic is
-// that of the kernels above (same K split, same summation order), so the
-// results are bit-identical to theirs.
+// work item (not once per 16 weight rows).  A group of more than 64 tokens
+// is split into sibling slots; their weight loads go through the caches and
+// the siblings run side by side on one XCD, so the repeated reads mostly
+// hit L2.  Per element the arithmetic is that of the kernels above (same K
+// split, same summation order), so the results are bit-identical to theirs.
 #ifndef BDM_WIDE_GU_GROUPS
 #define BDM_WIDE_GU_GROUPS 8           // from kWideGuBigT tokens; 4 below
 #endif
