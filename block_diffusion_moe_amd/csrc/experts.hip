@@ -260,6 +260,9 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 #ifndef BDM_WIDE_REUSE
 #define BDM_WIDE_REUSE 1
 #endif
+#ifndef BDM_GU_TILE_SKIP
+#define BDM_GU_TILE_SKIP 1
+#endif
 // weight loads of the many-token kernels: through the caches when another
 // slot reads the same weights (TEMP), else streamed
 template <bool TEMP>
@@ -320,17 +323,23 @@ __device__ __forceinline__ void gateup_wide_item(
   load(wu, 0, bu);
   if (tid < 16 * MT) srow[tid] = prow;
   __syncthreads();
-  // this wave's K-slice of the slot's token rows (rows >= m are zero)
+  // this wave's K-slice of the slot's token rows (rows >= m are zero; a
+  // tile wholly past m loads nothing, a workgroup-uniform test)
   u32x4 a[MT][KSW];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = 16 * mt + c;
-    const bool ok = r < m;
-    const uint16_t* xr = x + static_cast<size_t>(srow[r] / K1) * H + g * 8;
+    if (!BDM_GU_TILE_SKIP || 16 * mt < m) {
+      const int r = 16 * mt + c;
+      const bool ok = r < m;
+      const uint16_t* xr = x + static_cast<size_t>(srow[r] / K1) * H + g * 8;
 #pragma unroll
-    for (int s = 0; s < KSW; ++s) {
-      const u32x4 v = ld16(xr + (s0 + s) * 32);
-      a[mt][s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < KSW; ++s) {
+        const u32x4 v = ld16(xr + (s0 + s) * 32);
+        a[mt][s] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSW; ++s) a[mt][s] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
