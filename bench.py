@@ -396,13 +396,14 @@ def main():
     value = T / (ms_step_plain * 1e-3)
 
     gemm_gbs = HEAD_BYTES / (gemm_loop_us * 1e-6) / 1e9
-    stream_gbs = stream_read_gbs(torch, dev, max(8, args.steps // 10))
+    stream_gbs, stream_pattern = stream_read_gbs(torch, dev, max(8, args.steps // 10))
     roof = {"bound": "hbm", "kernel": "head_coop_kernel (bdm_lm_head_stats)",
             "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": head_traffic(),
             "bytes_per_launch": HEAD_BYTES, "us_per_launch": round(gemm_loop_us, 2),
             "launches_timed": args.steps, "us_per_launch_in_step": round(gemm_us, 2),
             "measured_stream_read_GB_s": round(stream_gbs, 1),
+            "measured_stream_read_pattern": stream_pattern,
             "frac_of_measured_stream_read": round(gemm_gbs / stream_gbs, 4)}
 
     stack = None
@@ -623,35 +624,45 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
 
 def stream_read_gbs(torch, dev, reps):
     """Read bandwidth of a plain 1 GiB stream with the weight kernels' access
-    (16-byte non-temporal loads, libbdmcal.so): the box's achievable ceiling
-    for this path, measured beside it."""
+    (16-byte non-temporal loads, libbdmcal.so), in two orders: a grid-stride
+    loop of 1,024 workgroups, and one contiguous region per workgroup (256
+    and 512 workgroups, the persistent kernels' order).  The best of them is
+    the box's achievable ceiling for this path, measured beside it.  Returns
+    (GB/s, pattern)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                    "block_diffusion_moe_amd", "libbdmcal.so"))
-    lib.bdmcal_stream_read.restype = ctypes.c_int
-    lib.bdmcal_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
-                                       ctypes.c_int, ctypes.c_void_p]
-    nbytes, blocks = 1 << 30, 1024
+    sig = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    for f in (lib.bdmcal_stream_read, lib.bdmcal_stream_read_region):
+        f.restype = ctypes.c_int
+        f.argtypes = sig
+    nbytes = 1 << 30
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
-    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    out = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream().cuda_stream
-
-    def launch(b):
-        if lib.bdmcal_stream_read(b.data_ptr(), nbytes, out.data_ptr(), blocks, st) != 0:
-            raise RuntimeError("bdmcal_stream_read failed")
-    for b in bufs:
-        launch(b)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(reps):
-        launch(bufs[i % 2])
-    e1.record()
-    torch.cuda.synchronize()
-    gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+    best = (0.0, "")
+    for name, fn, blocks in (("grid-stride, 1024 workgroups", lib.bdmcal_stream_read, 1024),
+                             ("one region per workgroup, 256", lib.bdmcal_stream_read_region, 256),
+                             ("one region per workgroup, 512", lib.bdmcal_stream_read_region,
+                              512)):
+        def launch(b):
+            if fn(b.data_ptr(), nbytes, out.data_ptr(), blocks, st) != 0:
+                raise RuntimeError("stream read probe failed")
+        for b in bufs:
+            launch(b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            launch(bufs[i % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+        if gbs > best[0]:
+            best = (gbs, name)
     del bufs, out
     torch.cuda.empty_cache()
-    return gbs
+    return best
 
 
 def head_traffic():

@@ -79,7 +79,64 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   out[static_cast<long>(blockIdx.x) * kReadThreads + threadIdx.x] = acc;
 }
 
+// The same read in the other common order: workgroup b reads its own
+// contiguous region (bytes / blocks, rounded down to whole 16 KiB batches;
+// the remainder is not read), 4 loads per lane per batch, two batches in
+// flight.  With one workgroup per CU this is the order of a persistent
+// kernel that gives each workgroup one run of weight rows.
+constexpr int kRegUnroll = 4;
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_region_kernel(
+    const u32x4* __restrict__ src, long per, uint32_t* __restrict__ out) {
+  constexpr long kB = static_cast<long>(kReadThreads) * kRegUnroll;     // 16-byte units
+  const long begin = static_cast<long>(blockIdx.x) * per;
+  const long end = begin + per;
+  uint32_t acc = 0u;
+  u32x4 a[kRegUnroll], b[kRegUnroll];
+  auto load = [&](long base, u32x4(&v)[kRegUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kRegUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(src + base + u * kReadThreads + threadIdx.x);
+  };
+  auto fold = [&](const u32x4(&v)[kRegUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kRegUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  };
+  long i = begin;                                  // batch base, a multiple of kB
+  if (i < end) {
+    load(i, a);
+    for (;;) {
+      const bool nb = i + kB < end;
+      if (nb) load(i + kB, b);
+      fold(a);
+      i += kB;
+      if (!nb) break;
+      const bool na = i + kB < end;
+      if (na) load(i + kB, a);
+      fold(b);
+      i += kB;
+      if (!na) break;
+    }
+  }
+  out[static_cast<long>(blockIdx.x) * kReadThreads + threadIdx.x] = acc;
+}
+
 }  // namespace bdmcal
+
+extern "C" __attribute__((visibility("default"))) int bdmcal_stream_read_region(
+    const void* src, long bytes, uint32_t* out, int blocks, void* stream) {
+  using namespace bdmcal;
+  // out: blocks * 256 entries; every workgroup gets at least one batch
+  constexpr long kB = static_cast<long>(kReadThreads) * kRegUnroll;
+  if (!src || !out || bytes <= 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65535) return -1;
+  if (reinterpret_cast<uintptr_t>(src) & 15) return -1;
+  const long per = (bytes / 16 / blocks) / kB * kB;
+  if (per < kB) return -1;
+  (void)hipGetLastError();
+  stream_read_region_kernel<<<blocks, kReadThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(src), per, out);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" __attribute__((visibility("default"))) int bdmcal_stream_read(const void* src,
                                                                         long bytes,

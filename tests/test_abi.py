@@ -205,6 +205,13 @@ def test_calibration_library_exports():
     assert r(_fake(1 << 20), 1000, _fake(1 << 21), 4, None) == -1
     assert r(_fake(1 << 20), 1 << 20, None, 4, None) == -1
     assert r(_fake(1 << 20), 1 << 20, _fake(1 << 21), 0, None) == -1
+    g = cal.bdmcal_stream_read_region
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert g(None, 1 << 20, _fake(1 << 21), 4, None) == -1
+    assert g(_fake(1 << 20), 1000, _fake(1 << 21), 4, None) == -1
+    assert g(_fake(1 << 20), 1 << 20, _fake(1 << 21), 0, None) == -1
+    assert g(_fake(1 << 20), 1 << 14, _fake(1 << 21), 2, None) == -1   # under one batch each
 
 
 def test_coreset_validation(lib):
