@@ -99,13 +99,15 @@ def test_denoise_tiny_teacher_forced(bdm, threshold, top_p):
         assert history == [s.T - 1]
 
 
+@pytest.mark.parametrize("T", [24, 20], ids=["3x8", "8+8+4"])
 @pytest.mark.parametrize("top_p", [None, 0.9])
-def test_denoise_multiblock_tiny(bdm, top_p):
-    """Three blocks of 8 slots in one loop (each its own commit rule): every
-    step against the oracle's (teacher-forced, near calls excluded), and the
-    final tokens equal each block denoised alone, bit for bit."""
-    say(f"case denoise multi-block tiny coreset_top_p={top_p}")
-    s = synth.MoEShape(T=24, H=64, E=16, I=32, k=2)
+def test_denoise_multiblock_tiny(bdm, top_p, T):
+    """Blocks of 8 slots in one loop (each its own commit rule; 20 slots: a
+    ragged last block of 4): every step against the oracle's (teacher-forced,
+    near calls excluded), and the final tokens equal each block denoised
+    alone, bit for bit."""
+    say(f"case denoise multi-block tiny T={T} coreset_top_p={top_p}")
+    s = synth.MoEShape(T=T, H=64, E=16, I=32, k=2)
     V, mask, B = 512, 0, 8
     layers = _layers(s, (21, 22), DEV)
     emb = _embed(V, s.H, 3, DEV)
@@ -113,7 +115,7 @@ def test_denoise_multiblock_tiny(bdm, top_p):
     w_head = (w_head.float() * 30.0).to(torch.bfloat16)
     hl, eb, hb = _host_layers(layers), synth.bf16_bits(emb), synth.bf16_bits(w_head)
     tok0 = torch.full((s.T,), mask, dtype=torch.int32, device=DEV)
-    tok0[[2, 11, 20]] = torch.tensor([7, 8, 9], dtype=torch.int32, device=DEV)
+    tok0[[2, 11, T - 1]] = torch.tensor([7, 8, 9], dtype=torch.int32, device=DEV)
     cur = tok0.clone()
     while (cur == mask).any():
         before = cur.cpu().numpy().astype(np.int64)
