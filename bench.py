@@ -622,13 +622,14 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
     return out
 
 
-def stream_read_gbs(torch, dev, reps):
-    """Read bandwidth of a plain 1 GiB stream with the weight kernels' access
-    (16-byte non-temporal loads, libbdmcal.so), in two orders: a grid-stride
-    loop of 1,024 workgroups, and one contiguous region per workgroup (256
-    and 512 workgroups, the persistent kernels' order).  The best of them is
-    the box's achievable ceiling for this path, measured beside it.  Returns
-    (GB/s, pattern)."""
+def stream_read_gbs(torch, dev, reps, nbytes=None):
+    """Read bandwidth of a plain stream of the head's size (so that its fixed
+    launch, ramp and tail costs weigh as much as the head's) with the weight
+    kernels' access (16-byte non-temporal loads, libbdmcal.so), in two
+    orders: a grid-stride loop of 1,024 workgroups, and one contiguous region
+    per workgroup (256 and 512 workgroups, the persistent kernels' order).
+    The best of them is the box's achievable ceiling for this path, measured
+    beside it.  Returns (GB/s, pattern)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                    "block_diffusion_moe_amd", "libbdmcal.so"))
@@ -636,15 +637,16 @@ def stream_read_gbs(torch, dev, reps):
     for f in (lib.bdmcal_stream_read, lib.bdmcal_stream_read_region):
         f.restype = ctypes.c_int
         f.argtypes = sig
-    nbytes = 1 << 30
+    nbytes = (nbytes or HEAD_BYTES) // 16 * 16
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
     out = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream().cuda_stream
     best = (0.0, "")
-    for name, fn, blocks in (("grid-stride, 1024 workgroups", lib.bdmcal_stream_read, 1024),
-                             ("one region per workgroup, 256", lib.bdmcal_stream_read_region, 256),
-                             ("one region per workgroup, 512", lib.bdmcal_stream_read_region,
-                              512)):
+    unit = 256 * 4 * 16                         # a region workgroup's batch, bytes
+    for name, fn, blocks, region in (
+            ("grid-stride, 1024 workgroups", lib.bdmcal_stream_read, 1024, False),
+            ("one region per workgroup, 256", lib.bdmcal_stream_read_region, 256, True),
+            ("one region per workgroup, 512", lib.bdmcal_stream_read_region, 512, True)):
         def launch(b):
             if fn(b.data_ptr(), nbytes, out.data_ptr(), blocks, st) != 0:
                 raise RuntimeError("stream read probe failed")
@@ -657,7 +659,9 @@ def stream_read_gbs(torch, dev, reps):
             launch(bufs[i % 2])
         e1.record()
         torch.cuda.synchronize()
-        gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+        # a region workgroup reads whole batches only (the remainder is not read)
+        nread = (nbytes // blocks) // unit * unit * blocks if region else nbytes
+        gbs = nread / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
         if gbs > best[0]:
             best = (gbs, name)
     del bufs, out
