@@ -243,8 +243,10 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 // work item (not once per 16 weight rows).  A group of more than 64 tokens
 // is split into sibling slots; their weight loads go through the caches and
 // the siblings run side by side on one XCD, so the repeated reads mostly
-// hit L2.  Per element the arithmetic is that of the kernels above (same K
-// split, same summation order), so the results are bit-identical to theirs.
+// hit L2.  At H = 2048 the per-element arithmetic is that of the kernels
+// above (8 k-steps per wave in both, partials summed in wave order), so the
+// results are bit-identical to theirs; at smaller H the K split differs (a
+// wave's slice is H/256 k-steps here, 8 there).
 #ifndef BDM_WIDE_GU_GROUPS
 #define BDM_WIDE_GU_GROUPS 8           // from kWideGuBigT tokens; 4 below
 #endif
