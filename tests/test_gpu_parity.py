@@ -259,13 +259,15 @@ def test_head_clover_fallback(bdm, layout):
 
 
 @LAYOUTS
-def test_head_two_phase_and_vocab_shards(bdm, layout):
+@pytest.mark.parametrize("T", [32, 100])
+def test_head_two_phase_and_vocab_shards(bdm, layout, T):
     """Phase 1 + phase 2 equals the fused call bit for bit, and the head
     computed as three vocabulary shards (each with its vocab_offset, the
     mask row in the middle shard) and merged once gives the same argmax and
-    decisions, with confidences within the fp32 merge-order tolerance."""
-    say(f"case head two-phase + shards layout={layout}")
-    s = synth.HeadShape(T=32, H=2048, V=100000, mask_id=51234)
+    decisions, with confidences within the fp32 merge-order tolerance (100
+    rows: two passes in each shard's launch)."""
+    say(f"case head two-phase + shards T={T} layout={layout}")
+    s = synth.HeadShape(T=T, H=2048, V=100000, mask_id=51234)
     W = synth.head_weights(s, 3, device=DEV)
     blk = synth.head_block(s, W, block_seed=5, n_boost=10, committed_rows=3, mask_boost_rows=2)
     fused = run_head(bdm, blk, layout=layout)
