@@ -54,8 +54,9 @@ def parse():
                         "at least 10 s of oracle time (0: skip)")
     p.add_argument("--stack-layers", type=int, default=40,
                    help="layers of the denoise-loop stack measured beside the step (0: skip)")
-    p.add_argument("--layout", type=int, default=1,
-                   help="weight layout: 1 = packed MFMA tiles (packed once, untimed), 0 = row-major")
+    p.add_argument("--layout", type=int, default=2,
+                   help="weight layout (packed once, untimed): 2 = MFMA tiles with gate/up "
+                        "packed as pairs, 1 = MFMA tiles, 0 = row-major")
     return p.parse_args()
 
 
@@ -87,7 +88,16 @@ def main():
         sets.append((inp, w_head, blk))
     torch.cuda.synchronize()
     # the weights the kernels read: packed once (not timed) or the row-major tensors
-    if args.layout:
+    if args.layout == 2:
+        pk, pp = bdm.bdm_pack_weights, bdm.bdm_pack_gate_up
+        kw_sets = []
+        for i, _, _ in sets:
+            g, u = pp(i.w_gate, i.w_up)
+            sg, su = pp(i.ws_gate, i.ws_up)
+            kw_sets.append(dict(w_gate=g, w_up=u, w_down=pk(i.w_down), ws_gate=sg, ws_up=su,
+                                ws_down=pk(i.ws_down)))
+        heads = [pk(w) for _, w, _ in sets]
+    elif args.layout:
         pk = bdm.bdm_pack_weights
         kw_sets = [dict(w_gate=pk(i.w_gate), w_up=pk(i.w_up), w_down=pk(i.w_down),
                         ws_gate=pk(i.ws_gate), ws_up=pk(i.ws_up), ws_down=pk(i.ws_down))
@@ -433,7 +443,9 @@ def main():
                         "renormalised) + untied 248,320x2048 head with the 0.95 unmask rule",
             "block_tokens": T, "hidden": H, "experts": L.E, "top_k": L.k, "inter": L.I,
             "vocab": HS.V, "weight_sets_rotated": args.sets, "parallelism": "single GPU",
-            "weight_layout": "mfma_tiles (packed once at load)" if args.layout else "row_major",
+            "weight_layout": {2: "mfma_tiles, gate/up as pairs (packed once at load)",
+                              1: "mfma_tiles (packed once at load)",
+                              0: "row_major"}[args.layout],
         },
         "moe_layer": {"us": round(moe_loop_us, 2), "us_in_step": round(moe_us, 2),
                       "block_tokens_per_s": round(T / (moe_loop_us * 1e-6), 1),
@@ -481,8 +493,13 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
     for l in range(nl):
         wr, wg, wu, wd, sg, su, sd, _ = synth.moe_weights(L, 100 + l, dev)
         pk = bdm.bdm_pack_weights
-        layers.append({"w_router": wr, "w_gate": pk(wg), "w_up": pk(wu), "w_down": pk(wd),
-                       "ws_gate": pk(sg), "ws_up": pk(su), "ws_down": pk(sd)})
+        if args.layout == 2:
+            g, u = bdm.bdm_pack_gate_up(wg, wu)
+            sgp, sup = bdm.bdm_pack_gate_up(sg, su)
+        else:
+            g, u, sgp, sup = pk(wg), pk(wu), pk(sg), pk(su)
+        layers.append({"w_router": wr, "w_gate": g, "w_up": u, "w_down": pk(wd),
+                       "ws_gate": sgp, "ws_up": sup, "ws_down": pk(sd)})
         del wg, wu, wd, sg, su, sd
     g = torch.Generator(device=dev)
     g.manual_seed(902)

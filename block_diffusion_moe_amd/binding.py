@@ -21,6 +21,7 @@ BDM_MASK_ID_CLOVER = 151669
 BDM_THRESHOLD_DEFAULT = 0.95
 BDM_LAYOUT_ROW_MAJOR = 0
 BDM_LAYOUT_MFMA_TILES = 1
+BDM_LAYOUT_MFMA_TILES_GU = 2
 
 _c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -57,6 +58,7 @@ _SIGS = {
                                        _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "bdm_packed_weight_elems": (_c_int, [ctypes.c_long, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_pack_weights": (_c_int, [_vp, ctypes.c_long, _c_int, _vp, _vp]),
+    "bdm_pack_gate_up": (_c_int, [_vp, _vp, ctypes.c_long, _c_int, _vp, _vp]),
     "bdm_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
 }
 
@@ -91,16 +93,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 class Packed:
     """A bf16 weight tensor in the MFMA-tile layout (see bdm_pack_weights):
     `data` holds the packed elements, `shape` the logical row-major shape
-    (the last dimension is the reduction dimension)."""
+    (the last dimension is the reduction dimension).  A gate or up matrix of
+    a gate/up pair (bdm_pack_gate_up) shares `data` with its partner:
+    `offset` elements in, `pair` the name of its role ("gate" or "up")."""
 
-    def __init__(self, data: torch.Tensor, shape):
+    def __init__(self, data: torch.Tensor, shape, offset: int = 0, pair=None):
         self.data = data
         self.shape = tuple(shape)
         self.device = data.device
         self.dtype = data.dtype
+        self.offset = int(offset)
+        self.pair = pair
 
     def data_ptr(self):
-        return self.data.data_ptr()
+        return self.data.data_ptr() + 2 * self.offset
 
 
 def _ptr(t):
@@ -192,6 +198,50 @@ def bdm_pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream
     return Packed(out, w.shape)
 
 
+def bdm_pack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, out=None, stream=None):
+    """The gate and up matrices of a layer (or of its shared expert) packed
+    into one buffer whose 16-row groups alternate gate, up
+    (BDM_LAYOUT_MFMA_TILES_GU); returns the (gate, up) `Packed` views, to be
+    passed as w_gate / w_up (or ws_gate / ws_up) together."""
+    _check(w_gate, "w_gate", torch.bfloat16)
+    _check(w_up, "w_up", torch.bfloat16, tuple(w_gate.shape), w_gate.device)
+    cols = w_gate.shape[-1]
+    rows = w_gate.numel() // cols
+    n = 2 * rows * cols
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=w_gate.device)
+    _check(out, "out", torch.bfloat16, device=w_gate.device)
+    if out.numel() < n:
+        raise ValueError("out: too small for the packed pair")
+    _raise("bdm_pack_gate_up", load().bdm_pack_gate_up(_ptr(w_gate), _ptr(w_up), rows, cols,
+                                                       _ptr(out), _stream(stream)))
+    return (Packed(out, w_gate.shape, 0, "gate"), Packed(out, w_up.shape, 16 * cols, "up"))
+
+
+def _expert_layout(gate, up, down, sgate, sup, sdown) -> int:
+    """weight_layout of one layer's expert matrices: all row-major, all
+    packed plainly, or gate/up (and the shared expert's) as packed pairs."""
+    mats = [t for t in (gate, up, down, sgate, sup, sdown) if t is not None]
+    packed = [isinstance(t, Packed) for t in mats]
+    if any(packed) and not all(packed):
+        raise ValueError("expert weights must be all row-major or all packed")
+    if not all(packed):
+        return BDM_LAYOUT_ROW_MAJOR
+    pairs = [(gate, up)] + ([(sgate, sup)] if sgate is not None else [])
+    roles = [t.pair for g, u in pairs for t in (g, u)]
+    if all(r is None for r in roles) and down.pair is None and (sdown is None or
+                                                                sdown.pair is None):
+        return BDM_LAYOUT_MFMA_TILES
+    for g, u in pairs:
+        if g.pair != "gate" or u.pair != "up" or g.data is not u.data or \
+                u.offset != g.offset + 16 * g.shape[-1]:
+            raise ValueError("gate/up must both come from one bdm_pack_gate_up call "
+                             "(routed and shared alike)")
+    if down.pair is not None or (sdown is not None and sdown.pair is not None):
+        raise ValueError("down matrices are packed with bdm_pack_weights")
+    return BDM_LAYOUT_MFMA_TILES_GU
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     """Device scratch buffer (torch allocations are 256-byte aligned)."""
     return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
@@ -228,11 +278,7 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
     _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
     _check(topk_w, "topk_w", torch.float32, (T, k), dev)
     has_shared = ws_gate is not None
-    packed = [isinstance(t, Packed) for t in (w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
-              if t is not None]
-    if any(packed) and not all(packed):
-        raise ValueError("expert weights must be all row-major or all packed")
-    layout = BDM_LAYOUT_MFMA_TILES if all(packed) else BDM_LAYOUT_ROW_MAJOR
+    layout = _expert_layout(w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
     need = bdm_moe_workspace_bytes(T, H, I, E, k, has_shared)
     if ws is None:
         ws = workspace(need, dev)
@@ -274,7 +320,8 @@ class MoeStack:
     the host array of bdm_moe_layer structs bdm_denoise_block takes (the
     tensors stay referenced here).  `layers`: list of dicts with w_router,
     router_bias (optional), w_gate, w_up, w_down, ws_gate, ws_up, ws_down
-    (tensors, or all expert matrices `Packed`)."""
+    (tensors, or all expert matrices `Packed`, gate/up possibly as
+    bdm_pack_gate_up pairs: the same kind in every layer)."""
 
     def __init__(self, layers):
         if not layers:
@@ -285,7 +332,6 @@ class MoeStack:
         self.E, self.I, self.H = E, I, H
         self.has_shared = self.layers[0].get("ws_gate") is not None
         self.arr = (MoeLayerC * len(self.layers))()
-        mats = []
         for i, lw in enumerate(self.layers):
             _check(lw["w_router"], "w_router", torch.float32, (E, H), dev)
             _check(lw.get("router_bias"), "router_bias", torch.float32, (E,), dev)
@@ -297,12 +343,12 @@ class MoeStack:
             for f, _ in MoeLayerC._fields_:
                 ptr = _ptr(lw.get(f))
                 setattr(self.arr[i], f, None if ptr is None else ptr.value)
-            mats += [lw[n] for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
-                     if lw.get(n) is not None]
-        packed = [isinstance(t, Packed) for t in mats]
-        if any(packed) and not all(packed):
-            raise ValueError("expert weights must be all row-major or all packed")
-        self.packed = all(packed)
+            lay = _expert_layout(*[lw.get(n) for n in ("w_gate", "w_up", "w_down", "ws_gate",
+                                                       "ws_up", "ws_down")])
+            if i > 0 and lay != self.layout:
+                raise ValueError("every layer's expert weights must be of one kind")
+            self.layout = lay
+        self.packed = self.layout != BDM_LAYOUT_ROW_MAJOR
         self.device = dev
 
     def __len__(self):
@@ -330,7 +376,7 @@ def bdm_denoise_block(tokens, w_embed, layers, w_head, k: int, mask_id: int,
         raise ValueError("the stack's hidden size or device differs from w_embed's")
     if isinstance(w_head, Packed) != stack.packed:
         raise ValueError("expert and head weights must be all row-major or all packed")
-    layout = BDM_LAYOUT_MFMA_TILES if stack.packed else BDM_LAYOUT_ROW_MAJOR
+    layout = stack.layout
     need = bdm_denoise_workspace_bytes(T, H, stack.I, stack.E, k, stack.has_shared)
     if ws is None:
         ws = workspace(need, dev)

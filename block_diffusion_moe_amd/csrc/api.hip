@@ -16,6 +16,11 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// the gate/up pair layout: up follows gate by one 16-row group
+bool pair_ok(const uint16_t* gate, const uint16_t* up, int H) {
+  return up == gate + static_cast<size_t>(16) * H;
+}
+
 int check_moe_shape(int T, int H, int I, int E, int k, int has_shared) {
   if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return BDM_ERR_INVALID_ARG;
   if (has_shared != 0 && has_shared != 1) return BDM_ERR_INVALID_ARG;
@@ -191,9 +196,13 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
   const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
   if (nshared != 0 && nshared != 3) return BDM_ERR_INVALID_ARG;
   if (renorm != 0 && renorm != 1) return BDM_ERR_INVALID_ARG;
-  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES &&
+      weight_layout != BDM_LAYOUT_MFMA_TILES_GU)
     return BDM_ERR_INVALID_ARG;
   const int has_shared = nshared == 3 ? 1 : 0;
+  if (weight_layout == BDM_LAYOUT_MFMA_TILES_GU &&
+      (!pair_ok(w_gate, w_up, H) || (has_shared && !pair_ok(ws_gate, ws_up, H))))
+    return BDM_ERR_INVALID_ARG;
   int st = check_moe_shape(T, H, I, E, k, has_shared);
   if (st != BDM_OK) return st;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
@@ -431,8 +440,12 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
   if (!tokens || !w_embed || !w_head || !steps_taken || !workspace || (L > 0 && !layers))
     return BDM_ERR_INVALID_ARG;
   if (L < 0 || max_steps < 0 || (renorm != 0 && renorm != 1)) return BDM_ERR_INVALID_ARG;
-  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES)
+  if (weight_layout != BDM_LAYOUT_ROW_MAJOR && weight_layout != BDM_LAYOUT_MFMA_TILES &&
+      weight_layout != BDM_LAYOUT_MFMA_TILES_GU)
     return BDM_ERR_INVALID_ARG;
+  // the head is packed plainly when the experts use the gate/up pair layout
+  const int head_layout_ =
+      weight_layout == BDM_LAYOUT_MFMA_TILES_GU ? BDM_LAYOUT_MFMA_TILES : weight_layout;
   if (!(threshold == threshold) || threshold == INFINITY || threshold == -INFINITY)
     return BDM_ERR_INVALID_ARG;
   if (!(coreset_top_p >= 0.0f && coreset_top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
@@ -451,6 +464,9 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
     if (!aligned16(w.w_router) || !aligned16(w.w_gate) || !aligned16(w.w_up) ||
         !aligned16(w.w_down) ||
         (ns == 3 && (!aligned16(w.ws_gate) || !aligned16(w.ws_up) || !aligned16(w.ws_down))))
+      return BDM_ERR_INVALID_ARG;
+    if (weight_layout == BDM_LAYOUT_MFMA_TILES_GU &&
+        (!pair_ok(w.w_gate, w.w_up, H) || (ns == 3 && !pair_ok(w.ws_gate, w.ws_up, H))))
       return BDM_ERR_INVALID_ARG;
   }
   int st = check_moe_shape(T, H, I, E, k, has_shared);
@@ -491,7 +507,7 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
       bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
                           w.ws_up, w.ws_down, x, x, xn, meta, weight_layout, s);
     }
-    bdm::launch_head_stats(xn, T, H, w_head, V, 0, weight_layout, mask_id, parts.m, parts.s,
+    bdm::launch_head_stats(xn, T, H, w_head, V, 0, head_layout_, mask_id, parts.m, parts.s,
                            parts.a, parts.grid, parts.grid, s);
     bdm::launch_unmask(parts.m, parts.s, parts.a, T, parts.grid, parts.grid, mask_id, threshold,
                        1, B, tokens, nullptr, nullptr, cnt, cnt + 1, s);
@@ -526,6 +542,24 @@ int bdm_pack_weights(const uint16_t* src, long rows, int cols, uint16_t* dst, vo
   if ((rows + 15) / 16 * (cols / 32) > 4L * 0x7fffffffL) return BDM_ERR_UNSUPPORTED_SHAPE;
   (void)hipGetLastError();
   bdm::launch_pack(src, rows, cols, dst, static_cast<hipStream_t>(stream));
+  return last_hip_status();
+}
+
+int bdm_pack_gate_up(const uint16_t* gate, const uint16_t* up, long rows, int cols,
+                     uint16_t* dst, void* stream) {
+  if (!gate || !up || !dst || rows < 16 || rows % 16 != 0 || cols < 32 || cols % 32 != 0)
+    return BDM_ERR_INVALID_ARG;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(dst)) return BDM_ERR_INVALID_ARG;
+  if ((rows / 16) * (cols / 32) > 4L * 0x7fffffffL) return BDM_ERR_UNSUPPORTED_SHAPE;
+  const size_t n = static_cast<size_t>(rows) * cols;        // elements of one matrix
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), d1 = d0 + 2 * n * sizeof(uint16_t);
+  auto overlaps = [&](const uint16_t* src) {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), s1 = s0 + n * sizeof(uint16_t);
+    return s0 < d1 && d0 < s1;
+  };
+  if (overlaps(gate) || overlaps(up)) return BDM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  bdm::launch_pack_pair(gate, up, rows, cols, dst, static_cast<hipStream_t>(stream));
   return last_hip_status();
 }
 

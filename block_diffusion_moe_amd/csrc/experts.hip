@@ -50,6 +50,16 @@ __device__ __forceinline__ bool slot_ok(int e, int off, int m, int E, int P, boo
 
 __device__ __forceinline__ int clamp_row(int r, int P) { return r < 0 ? 0 : (r >= P ? P - 1 : r); }
 
+// gate/up fragments.  In the pair layout the packed gate and up groups
+// alternate in one buffer (w_up = w_gate + one group), so consecutive groups
+// of either matrix are two groups apart.
+__device__ __forceinline__ FragPtr frag_ptr_gu(const uint16_t* W, long row0, int K, int lane,
+                                               int layout) {
+  if (layout == BDM_LAYOUT_MFMA_TILES_GU)
+    return {W + (row0 / 16) * 2 * (K / 32) * 512 + lane * 8, 512};
+  return frag_ptr(W, row0, K, lane, layout);
+}
+
 // One k-step (8 consecutive k of one row) of a weight row.  With GUARD the
 // k-step may lie past K: the load then reads k-step 0 (always valid) and the
 // value is replaced by zeros, so no load sits behind a branch.
@@ -96,8 +106,8 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
   int row1 = clamp_row(pair_rows[off + (16 + c < m ? 16 + c : 0)], P);
 
   const long wrow0 = (e == E) ? n0 : static_cast<long>(e) * I + n0;
-  const FragPtr rg = frag_ptr(e == E ? ws_gate : w_gate, wrow0, H, lane, layout);
-  const FragPtr ru = frag_ptr(e == E ? ws_up : w_up, wrow0, H, lane, layout);
+  const FragPtr rg = frag_ptr_gu(e == E ? ws_gate : w_gate, wrow0, H, lane, layout);
+  const FragPtr ru = frag_ptr_gu(e == E ? ws_up : w_up, wrow0, H, lane, layout);
   u32x4 bg[KSW], bu[KSW];
 #pragma unroll
   for (int q = 0; q < KSW; ++q) {
@@ -312,7 +322,7 @@ __device__ __forceinline__ void gateup_wide_item(
   // weights of column group q of this run; q >= nq: 16 bytes of token row
   // 0 per lane instead (valid, cached, ignored)
   auto load = [&](const uint16_t* W, int q, u32x4(&b)[KSW]) {
-    const FragPtr f = q < nq ? frag_ptr(W, wrow + 16L * (q0 + q), H, lane, layout)
+    const FragPtr f = q < nq ? frag_ptr_gu(W, wrow + 16L * (q0 + q), H, lane, layout)
                              : FragPtr{x + c * 8, 0};
 #pragma unroll
     for (int s = 0; s < KSW; ++s) b[s] = ld16_w<TEMP>(f.p + (s0 + s) * f.step);
@@ -348,7 +358,7 @@ __device__ __forceinline__ void gateup_wide_item(
   // the partial products of one matrix's group; each k-step of the same
   // matrix's next group is requested as soon as this one has been used
   auto partial = [&](u32x4(&b)[KSW], const uint16_t* W, int qn, float* pp) {
-    const FragPtr fn = qn < nq ? frag_ptr(W, wrow + 16L * (q0 + qn), H, lane, layout)
+    const FragPtr fn = qn < nq ? frag_ptr_gu(W, wrow + 16L * (q0 + qn), H, lane, layout)
                                : FragPtr{x + c * 8, 0};
     f32x4 acc[MT];
 #pragma unroll
@@ -667,6 +677,8 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                     const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                     const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
                     const MoeMeta& meta, int layout, hipStream_t s) {
+  // down reads its own matrices, packed the plain way in the gate/up pair layout
+  const int dl = layout == BDM_LAYOUT_MFMA_TILES_GU ? BDM_LAYOUT_MFMA_TILES : layout;
   // upper bound on the slots; workgroups past the actual list exit at once
   const int groups = moe_max_slots(T, E, k, has_shared);
   const int P = T * (k + 1);
@@ -698,7 +710,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
     guw<<<gu_grid, kGuWaves * 64, 0, s>>>(x, H, I, E, k, P, layout, w_gate, w_up, ws_gate,
                                           ws_up, meta.slots, meta.pair_rows, meta.info, groups,
                                           gpi, meta.act);
-    down_wide_kernel<16><<<groups * dn_runs, 512, 0, s>>>(meta.act, H, I, E, P, layout, w_down,
+    down_wide_kernel<16><<<groups * dn_runs, 512, 0, s>>>(meta.act, H, I, E, P, dl, w_down,
                                                           ws_down, meta.slots, meta.pair_rows,
                                                           meta.ypair);
     combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
@@ -715,13 +727,13 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
                                                        meta.act);
   }
   if (KI == 16) {
-    down_kernel<16, false><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<16, false><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, dl, w_down, ws_down, meta.slots,
                                               meta.pair_rows, meta.ypair);
   } else if (KI < 16) {
-    down_kernel<16, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<16, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, dl, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   } else {
-    down_kernel<32, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, layout, w_down, ws_down, meta.slots,
+    down_kernel<32, true><<<dn, kDnWaves * 64, 0, s>>>(meta.act, H, I, E, P, dl, w_down, ws_down, meta.slots,
                                              meta.pair_rows, meta.ypair);
   }
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,

@@ -103,6 +103,8 @@ void launch_verify_merge(const float* pm, const float* ps, const int32_t* pa, co
                          float* pcand_out, float* entropy_out, hipStream_t s);
 
 void launch_pack(const uint16_t* src, long R, int K, uint16_t* dst, hipStream_t s);
+void launch_pack_pair(const uint16_t* gate, const uint16_t* up, long R, int K, uint16_t* dst,
+                      hipStream_t s);
 
 void launch_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H,
                     uint16_t* out, hipStream_t s);

@@ -63,14 +63,22 @@ extern "C" {
 #define BDM_THRESHOLD_DEFAULT  0.95f
 
 /* Layout of the bf16 weight matrices a call reads (argument weight_layout).
- *   BDM_LAYOUT_ROW_MAJOR   [rows][cols], cols contiguous (the natural layout)
- *   BDM_LAYOUT_MFMA_TILES  the packed layout bdm_pack_weights produces: 1 KB
- *                          tiles of 16 rows x 32 cols in MFMA operand order,
- *                          a 16-row group contiguous over all cols.  The same
- *                          values; only the byte order differs (streams at a
- *                          higher fraction of HBM bandwidth). */
-#define BDM_LAYOUT_ROW_MAJOR   0
-#define BDM_LAYOUT_MFMA_TILES  1
+ *   BDM_LAYOUT_ROW_MAJOR     [rows][cols], cols contiguous (the natural layout)
+ *   BDM_LAYOUT_MFMA_TILES    the packed layout bdm_pack_weights produces: 1 KB
+ *                            tiles of 16 rows x 32 cols in MFMA operand order,
+ *                            a 16-row group contiguous over all cols.  The
+ *                            same values; only the byte order differs (streams
+ *                            at a higher fraction of HBM bandwidth).
+ *   BDM_LAYOUT_MFMA_TILES_GU MoE layer only: down (and the head) as in
+ *                            BDM_LAYOUT_MFMA_TILES, gate and up (routed, and
+ *                            the shared expert's) as one buffer written by
+ *                            bdm_pack_gate_up, whose 16-row groups alternate
+ *                            gate, up; then w_up = w_gate + 16*H elements
+ *                            (ws_up = ws_gate + 16*H), checked.  A gate/up
+ *                            work item then streams one contiguous run. */
+#define BDM_LAYOUT_ROW_MAJOR     0
+#define BDM_LAYOUT_MFMA_TILES    1
+#define BDM_LAYOUT_MFMA_TILES_GU 2
 
 /* Limits of this implementation (checked; BDM_ERR_UNSUPPORTED_SHAPE beyond). */
 #define BDM_MAX_TOKENS   2048   /* T: positions per call (up to 64 blocks of 32 stacked) */
@@ -132,7 +140,10 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   weight_layout layout of w_gate, w_up, w_down and ws_*: BDM_LAYOUT_ROW_MAJOR,
  *                or BDM_LAYOUT_MFMA_TILES with w_gate/w_up packed as one
  *                [E*I][H] matrix, w_down as [E*H][I], ws_gate/ws_up as [I][H]
- *                and ws_down as [H][I] (the router stays fp32 row-major)
+ *                and ws_down as [H][I], or BDM_LAYOUT_MFMA_TILES_GU with
+ *                w_gate/w_up (and ws_gate/ws_up) from bdm_pack_gate_up and
+ *                the down matrices as in BDM_LAYOUT_MFMA_TILES (the router
+ *                stays fp32 row-major)
  *   residual     [T][H] bf16 or NULL; may be the same pointer as y
  *   y            [T][H] bf16        output
  *   y_norm       [T][H] bf16 or NULL: also receives RMSNorm(y) (eps 1e-6,
@@ -255,6 +266,8 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
  *   E, k, I, renorm   as in bdm_moe_block_forward, the same for every layer
  *   w_head      [V][H] bf16 device: the untied head
  *   weight_layout     layout of every expert matrix and of w_head
+ *                     (BDM_LAYOUT_MFMA_TILES_GU: the experts as in
+ *                     bdm_moe_block_forward, w_head packed plainly)
  *   mask_id, threshold   as in bdm_lm_head_unmask
  *   coreset_top_p  0: plain top-k routing; in (0, 1]: the block coreset
  *               expert selector at that top_p in every layer (over blocks
@@ -434,6 +447,20 @@ BDM_API int bdm_packed_weight_elems(long rows, int cols, size_t* n);
  */
 BDM_API int bdm_pack_weights(const uint16_t* src, long rows, int cols, uint16_t* dst,
                              void* stream);
+
+/*
+ * bdm_pack_gate_up -- write the gate and up matrices of a layer (both
+ * row-major bf16 [rows][cols], rows = E*I or I for the shared expert, a
+ * multiple of 16) into one buffer dst of 2*rows*cols elements for
+ * BDM_LAYOUT_MFMA_TILES_GU: 16-row group 2g holds gate group g and group
+ * 2g + 1 up group g, each in the tile order of bdm_pack_weights (a group is
+ * 16*cols consecutive elements).  Pass w_gate = dst and w_up = dst +
+ * 16*cols.  A one-time preparation step; gate, up and dst must not overlap.
+ * Errors: BDM_ERR_INVALID_ARG for NULL pointers, rows < 16 or not a multiple
+ * of 16, cols < 32 or not a multiple of 32, unaligned pointers.
+ */
+BDM_API int bdm_pack_gate_up(const uint16_t* gate, const uint16_t* up, long rows, int cols,
+                             uint16_t* dst, void* stream);
 
 /*
  * bdm_rmsnorm -- RMSNorm of each row, between MoE layers of a pre-norm stack.

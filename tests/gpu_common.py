@@ -41,12 +41,18 @@ def packed(lib_mod, t):
 
 
 def run_moe(lib_mod, inp: synth.MoEInputs, renorm=True, residual=True, shared=True, layout=0):
-    """layout 0: row-major weights; 1: the library packs them first (MFMA tiles)."""
+    """layout 0: row-major weights; 1: the library packs them first (MFMA
+    tiles); 2: gate/up packed as pairs (bdm_pack_gate_up), down as tiles."""
     s = inp.shape
     dev = inp.x.device
     W = (inp.w_gate, inp.w_up, inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
-    if layout:
+    if layout == 1:
         W = tuple(packed(lib_mod, t) for t in W)
+    elif layout == 2:
+        g, u = lib_mod.bdm_pack_gate_up(inp.w_gate, inp.w_up)
+        sg, su = (lib_mod.bdm_pack_gate_up(inp.ws_gate, inp.ws_up) if inp.ws_gate is not None
+                  else (None, None))
+        W = (g, u, packed(lib_mod, inp.w_down), sg, su, packed(lib_mod, inp.ws_down))
     idx = torch.full((s.T, s.k), -1, dtype=torch.int32, device=dev)
     w = torch.full((s.T, s.k), float("nan"), dtype=torch.float32, device=dev)
     y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert syms == sorted(["bdm_version", "bdm_status_string", "bdm_moe_workspace_bytes",
                            "bdm_moe_block_forward", "bdm_head_workspace_bytes",
                            "bdm_lm_head_unmask", "bdm_rmsnorm", "bdm_packed_weight_elems",
-                           "bdm_pack_weights", "bdm_head_stat_parts", "bdm_lm_head_stats",
+                           "bdm_pack_weights", "bdm_pack_gate_up", "bdm_head_stat_parts",
+                           "bdm_lm_head_stats",
                            "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset",
                            "bdm_denoise_workspace_bytes", "bdm_denoise_block",
                            "bdm_head_verify_workspace_bytes", "bdm_lm_head_verify"])
@@ -107,7 +108,17 @@ def test_moe_validation_rejects_before_launch(lib):
     assert call(ws=None) == -1
     assert call(sd=None) == -1                    # shared trio must be all or none
     assert call(renorm=2) == -1
-    assert call(lay=2) == -1
+    assert call(lay=3) == -1
+    # gate/up pair layout: up must follow gate by one 16-row group (16 H
+    # elements), for the routed and the shared expert alike; with both pairs
+    # right the call gets as far as the workspace check
+    G, SG = 1 << 28, 1 << 29
+    pair = dict(lay=2, wg=_fake(G), wu=_fake(G + 32 * 2048), sg=_fake(SG), su=_fake(SG + 32 * 2048))
+    assert call(lay=2) == -1                      # w_up == w_gate
+    assert call(**dict(pair, su=_fake(SG))) == -1
+    assert call(**dict(pair, wu=_fake(G + 32 * 1024))) == -1
+    assert call(**dict(pair, wsb=1)) == -3
+    assert call(**dict(pair, lay=1, wsb=1)) == -3
     assert call(k=0) == -1
     assert call(k=300) == -1
     assert call(H=100) == -2
@@ -163,6 +174,17 @@ def test_packed_weight_size_and_pack_validation(lib):
     assert lib.bdm_pack_weights(None, 16, 64, B, None) == -1
     assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 20) + 64), None) == -1   # overlap
     assert lib.bdm_pack_weights(A, 16, 64, _fake((1 << 26) + 8), None) == -1    # misaligned
+    p = lib.bdm_pack_gate_up
+    C = _fake(1 << 27)
+    assert p(None, A, 16, 64, B, None) == -1
+    assert p(A, None, 16, 64, B, None) == -1
+    assert p(A, C, 16, 64, None, None) == -1
+    assert p(A, C, 24, 64, B, None) == -1                          # rows % 16
+    assert p(A, C, 16, 48, B, None) == -1                          # cols % 32
+    assert p(A, C, 0, 64, B, None) == -1
+    assert p(A, C, 16, 64, _fake((1 << 20) + 1024), None) == -1    # dst overlaps gate
+    assert p(A, C, 16, 64, _fake((1 << 27) - 2048), None) == -1    # dst overlaps up
+    assert p(A, C, 16, 64, _fake((1 << 26) + 8), None) == -1       # misaligned
 
 
 def test_two_phase_head_validation(lib):
@@ -254,7 +276,8 @@ def test_denoise_validation(lib):
     assert call(tokens=None) == -1
     assert call(mask=248320) == -1
     assert call(steps=-1) == -1
-    assert call(layout=2) == -1
+    assert call(layout=3) == -1
+    assert call(layout=2) == -1                 # gate/up pairs: w_up != w_gate + 16 H
     assert call(thr=float("inf")) == -1
     assert call(top_p=-0.1) == -1
     assert call(top_p=1.5) == -1

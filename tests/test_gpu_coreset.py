@@ -33,8 +33,12 @@ def bdm():
 def run_gpu(bdm, inp, top_p, block, layout=1, renorm=True, residual=True):
     s = inp.shape
     W = (inp.w_gate, inp.w_up, inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
-    if layout:
+    if layout == 1:
         W = tuple(bdm.bdm_pack_weights(t) for t in W)
+    elif layout == 2:                                   # gate/up packed as pairs
+        g, u = bdm.bdm_pack_gate_up(inp.w_gate, inp.w_up)
+        sg, su = bdm.bdm_pack_gate_up(inp.ws_gate, inp.ws_up)
+        W = (g, u, bdm.bdm_pack_weights(inp.w_down), sg, su, bdm.bdm_pack_weights(inp.ws_down))
     nb = (s.T + block - 1) // block
     idx = torch.full((s.T, s.k), -7, dtype=torch.int32, device=DEV)
     w = torch.full((s.T, s.k), float("nan"), dtype=torch.float32, device=DEV)
@@ -175,3 +179,17 @@ def test_coreset_repeatable_and_renorm_off(bdm):
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2].view(np.int32), b[2].view(np.int32))
     h, r = oracle_routing(inp, 0.9, 32, renorm=False)
     compare(a, inp, h, r)
+
+
+@pytest.mark.parametrize("T,block", [(32, 32), (256, 32)])
+def test_coreset_gate_up_pair_layout_bitwise(bdm, T, block):
+    """The coreset path with gate/up packed as pairs equals the tile layout
+    bit for bit (one block; eight blocks on the many-token kernels)."""
+    say(f"case coreset gate/up pair layout T={T}")
+    shp = synth.MoEShape(T=T, H=2048, E=256, I=512, k=8)
+    inp = synth.moe_inputs(shp, seed=4, block_seed=T, device=DEV, with_residual=True)
+    a = run_gpu(bdm, inp, 0.9, block, layout=1)
+    b = run_gpu(bdm, inp, 0.9, block, layout=2)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2].view(np.int32), b[2].view(np.int32))
+    assert np.array_equal(a[3], b[3])

@@ -145,6 +145,39 @@ def test_denoise_multiblock_tiny(bdm, top_p, T):
 
 
 @pytest.mark.parametrize("top_p", [None, 0.9])
+def test_denoise_layouts_agree(bdm, top_p):
+    """The whole tiny loop with row-major, tile-packed and pair-packed
+    (gate/up through bdm_pack_gate_up) weights gives the same tokens."""
+    say(f"case denoise layouts coreset_top_p={top_p}")
+    s = synth.MoEShape(T=16, H=64, E=16, I=32, k=2)
+    V, mask = 512, 0
+    layers = _layers(s, (31, 32), DEV)
+    emb = _embed(V, s.H, 4, DEV)
+    w_head = synth.head_weights(synth.HeadShape(T=16, H=64, V=V, mask_id=mask), 7, device=DEV)
+    w_head = (w_head.float() * 30.0).to(torch.bfloat16)
+    pk = bdm.bdm_pack_weights
+    tiles = [{**lw, **{n: pk(lw[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up",
+                                               "ws_down")}} for lw in layers]
+    pairs = []
+    for lw in layers:
+        g, u = bdm.bdm_pack_gate_up(lw["w_gate"], lw["w_up"])
+        sg, su = bdm.bdm_pack_gate_up(lw["ws_gate"], lw["ws_up"])
+        pairs.append({**lw, "w_gate": g, "w_up": u, "w_down": pk(lw["w_down"]), "ws_gate": sg,
+                      "ws_up": su, "ws_down": pk(lw["ws_down"])})
+    tok0 = torch.full((s.T,), mask, dtype=torch.int32, device=DEV)
+    tok0[5] = 9
+    outs = []
+    for lay, wh in ((layers, w_head), (tiles, pk(w_head)), (pairs, pk(w_head))):
+        t = tok0.clone()
+        steps, commits = bdm.bdm_denoise_block(t, emb, lay, wh, s.k, mask, 0.95,
+                                               coreset_top_p=top_p)
+        torch.cuda.synchronize()
+        outs.append((t.cpu(), steps, commits))
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0]) and o[1:] == outs[0][1:]
+
+
+@pytest.mark.parametrize("top_p", [None, 0.9])
 def test_denoise_clover_stack_invariants_and_first_step(bdm, top_p):
     """40 Clover-shaped layers, the 248,320-row head, packed weights; plain
     routing, and the coreset selector at the shipped top_p 0.9."""

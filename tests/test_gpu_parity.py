@@ -195,6 +195,46 @@ def test_uniform_router_ties_on_gpu(bdm):
 # Head + unmask
 # --------------------------------------------------------------------------
 
+def test_pack_gate_up_layout(bdm):
+    """The pair buffer holds the plain packed groups of gate and up,
+    alternating (16-row groups: 2g = gate g, 2g + 1 = up g)."""
+    say("case pack gate/up pair buffer")
+    s = synth.MoEShape(T=8, H=256, E=4, I=96, k=2)
+    inp = synth.moe_inputs(s, seed=7, block_seed=1, device=DEV)
+    g, u = bdm.bdm_pack_gate_up(inp.w_gate, inp.w_up)
+    pg, pu = bdm.bdm_pack_weights(inp.w_gate), bdm.bdm_pack_weights(inp.w_up)
+    S = 16 * s.H
+    pair = g.data.view(-1, 2, S)
+    torch.cuda.synchronize()
+    assert torch.equal(pair[:, 0].reshape(-1).view(torch.int16), pg.data.view(torch.int16))
+    assert torch.equal(pair[:, 1].reshape(-1).view(torch.int16), pu.data.view(torch.int16))
+    assert u.data_ptr() == g.data_ptr() + 2 * S
+
+
+@pytest.mark.parametrize("case", ["tiny", "T5_H128", "T17_I96", "H192", "noshared", "clover32",
+                                  "clover512", "skew256", "I96_T400"])
+def test_moe_gate_up_pair_layout_equals_tiles(bdm, case):
+    """Gate/up packed as pairs give the bits of the plain tile layout, on the
+    few-token and the many-token kernels (routing, weights, outputs)."""
+    say(f"case gate/up pair layout {case}")
+    shapes = {"tiny": (8, 64, 16, 32, 2), "T5_H128": (5, 128, 8, 64, 8),
+              "T17_I96": (17, 256, 64, 96, 4), "H192": (33, 192, 32, 32, 1),
+              "noshared": (24, 512, 32, 64, 4), "clover32": (32, 2048, 256, 512, 8),
+              "clover512": (512, 2048, 256, 512, 8), "skew256": (256, 2048, 256, 512, 8),
+              "I96_T400": (400, 512, 8, 96, 3)}
+    T, H, E, I, k = shapes[case]
+    shp = synth.MoEShape(T=T, H=H, E=E, I=I, k=k)
+    inp = synth.moe_inputs(shp, seed=T + E, block_seed=3, device=DEV, with_residual=True,
+                           zipf_s=1.1 if case == "skew256" else None)
+    shared = case != "noshared"
+    a = run_moe(bdm, inp, layout=1, shared=shared)
+    b = run_moe(bdm, inp, layout=2, shared=shared)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2].view(torch.int32), b[2].view(torch.int32))
+    if case == "tiny":
+        compare_moe(*b, oracle_moe(inp))
+
+
 @LAYOUTS
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("variant", ["plain", "committed", "maskboost", "all_boosted"])
