@@ -15,10 +15,16 @@ tensors already resident in HBM.  To keep the 256 MB Infinity Cache from
 serving repeated weights, the timed steps rotate over --sets independent
 weight sets (router, experts, shared expert, head) and token blocks.
 
+The weights are packed once before the timed region (--layout 2, the
+default: MFMA tiles with gate/up as interleaved pairs).
+
 Output: one JSON line (rank 0).  `value` is block-tokens/s of the whole
 step; the MoE layer alone (its launches back to back over the rotated sets)
-and the head alone are reported beside it, each with its algorithmic HBM bytes (touched experts x 6,291,456 B; head
-1,017,118,720 B) and the fraction of the 8 TB/s HBM peak.  The roofline
+and the head alone are reported beside it, each with its algorithmic HBM
+bytes (touched experts x 6,291,456 B; head 1,017,118,720 B) and the fraction
+of the 8 TB/s HBM peak, and so are the layer with the coreset selector, 16 /
+32 / 64 blocks in one layer call, the load-skew batch, the head over many
+rows, the verify epilogue and one step of the 40-layer loop.  The roofline
 entry is the head GEMM kernel (one launch per step, the largest single
 kernel): after the timed steps the same launches run back to back over the
 rotated sets between two HIP events recorded on the stream they run on; its
