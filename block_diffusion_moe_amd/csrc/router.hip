@@ -33,7 +33,10 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
 }
 
 constexpr int kRtWaves = 4;     // waves per router workgroup
-constexpr int kRtWideTiles = 4; // token tiles per router workgroup in many-block calls
+#ifndef BDM_RT_WIDE_TILES
+#define BDM_RT_WIDE_TILES 4
+#endif
+constexpr int kRtWideTiles = BDM_RT_WIDE_TILES;   // token tiles per router workgroup, many blocks
 #ifndef BDM_RT_WIDE_MIN_T
 #define BDM_RT_WIDE_MIN_T 512
 #endif
