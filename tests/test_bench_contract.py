@@ -1,6 +1,6 @@
 """bench.py's command-line contract, on the CPU: one GPU only (a request for
 more exits with status 2 and says why, before anything touches a device), and
-the defaults the full test run relies on (N = 1, 200 timed steps after 20
+the defaults a plain run uses (N = 1, 200 timed steps after 20
 warm-up steps, the gate/up pair layout)."""
 import os
 import subprocess
