@@ -71,8 +71,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the single-GPU denoise step only: run it with --gpus 1 "
-              "(multi-GPU sharding of this path is described in DESIGN.md, not built).",
-              file=sys.stderr)
+              "(the path is not built for several GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
