@@ -231,3 +231,68 @@ def test_denoise_clover_stack_invariants_and_first_step(bdm, top_p):
     assert int(tok.min()) >= 0 and int(tok.max()) < HS.V
     del players, w_head, emb
     torch.cuda.empty_cache()
+
+
+def test_denoise_clover_stack_two_blocks_gate_up_pairs(bdm):
+    """40 Clover-shaped layers with gate/up packed as pairs, two 32-slot
+    blocks in one call: the first step equals the single calls composed (the
+    head's rule per block), the loop ends with both blocks unmasked, and
+    each block's tokens equal that block denoised alone."""
+    s = synth.LAYER
+    HS = synth.HEAD
+    say("case denoise 40-layer stack, two blocks, gate/up pairs")
+    layers = _layers(s, range(200, 200 + synth.STACK_LAYERS), DEV)
+    pk = bdm.bdm_pack_weights
+    players = []
+    for lw in layers:
+        g, u = bdm.bdm_pack_gate_up(lw["w_gate"], lw["w_up"])
+        sg, su = bdm.bdm_pack_gate_up(lw["ws_gate"], lw["ws_up"])
+        players.append({"w_router": lw["w_router"], "w_gate": g, "w_up": u,
+                        "w_down": pk(lw["w_down"]), "ws_gate": sg, "ws_up": su,
+                        "ws_down": pk(lw["ws_down"])})
+    del layers
+    torch.cuda.empty_cache()
+    stack = bdm.MoeStack(players)
+    emb = _embed(HS.V, s.H, 5, DEV)
+    w_head = pk(synth.head_weights(HS, 1, device=DEV))
+    torch.cuda.synchronize()
+    say("  weights ready")
+    T = 2 * s.T
+    tok0 = torch.full((T,), HS.mask_id, dtype=torch.int32, device=DEV)
+    tok0[[3, 17, 40, 41, 60]] = torch.tensor([21, 22, 23, 24, 25], dtype=torch.int32, device=DEV)
+    # first step by hand
+    x = emb[tok0.long()].contiguous()
+    xn = torch.empty_like(x)
+    ws = bdm.workspace(bdm.bdm_moe_workspace_bytes(T, s.H, s.I, s.E, s.k, True), DEV)
+    for lw in players:
+        bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+        bdm.bdm_moe_block_forward(xn, lw["w_router"], lw["w_gate"], lw["w_up"], lw["w_down"],
+                                  s.k, ws_gate=lw["ws_gate"], ws_up=lw["ws_up"],
+                                  ws_down=lw["ws_down"], residual=x, y=x, ws=ws)
+    bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+    ref = tok0.clone()
+    nc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bdm.bdm_lm_head_unmask(xn, w_head, HS.mask_id, 0.95, True, ref, n_committed=nc,
+                           block_tokens=s.T)
+    one = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(one, emb, stack, w_head, s.k, HS.mask_id, 0.95,
+                                           max_steps=1, block_tokens=s.T)
+    torch.cuda.synchronize()
+    assert steps == 1 and commits == [int(nc.item())] and commits[0] >= 2
+    assert torch.equal(one, ref)
+    # the whole loop, and each block alone
+    tok = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(tok, emb, stack, w_head, s.k, HS.mask_id, 0.95,
+                                           block_tokens=s.T)
+    torch.cuda.synchronize()
+    say(f"  {steps} steps, commits {commits}")
+    assert steps <= s.T and not (tok == HS.mask_id).any()
+    done = tok0 != HS.mask_id
+    assert torch.equal(tok[done], tok0[done])
+    for b in range(2):
+        alone = tok0[b * s.T:(b + 1) * s.T].clone()
+        bdm.bdm_denoise_block(alone, emb, stack, w_head, s.k, HS.mask_id, 0.95)
+        torch.cuda.synchronize()
+        assert torch.equal(alone, tok[b * s.T:(b + 1) * s.T]), b
+    del players, stack, w_head, emb
+    torch.cuda.empty_cache()
