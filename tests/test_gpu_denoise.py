@@ -296,3 +296,38 @@ def test_denoise_clover_stack_two_blocks_gate_up_pairs(bdm):
         assert torch.equal(alone, tok[b * s.T:(b + 1) * s.T]), b
     del players, stack, w_head, emb
     torch.cuda.empty_cache()
+
+
+def test_denoise_degenerate_calls(bdm):
+    """max_steps = 0 does nothing; a block with nothing masked takes one
+    step that commits nothing and leaves it as it was; with several blocks,
+    a block that starts unmasked is never written while the others are
+    denoised, and they end as when run alone."""
+    say("case denoise degenerate calls")
+    s = synth.MoEShape(T=16, H=64, E=16, I=32, k=2)
+    V, mask, B = 512, 0, 8
+    layers = _layers(s, (41, 42), DEV)
+    stack = bdm.MoeStack(layers)
+    emb = _embed(V, s.H, 7, DEV)
+    w_head = synth.head_weights(synth.HeadShape(T=16, H=64, V=V, mask_id=mask), 8, device=DEV)
+    tok = torch.full((s.T,), mask, dtype=torch.int32, device=DEV)
+    steps, commits = bdm.bdm_denoise_block(tok, emb, stack, w_head, s.k, mask, 0.95,
+                                           max_steps=0)
+    torch.cuda.synchronize()
+    assert (steps, commits) == (0, []) and bool((tok == mask).all())
+    full = torch.arange(1, s.T + 1, dtype=torch.int32, device=DEV)
+    tok = full.clone()
+    steps, commits = bdm.bdm_denoise_block(tok, emb, stack, w_head, s.k, mask, 0.95)
+    torch.cuda.synchronize()
+    assert (steps, commits) == (1, [0]) and torch.equal(tok, full)
+    # block 0 unmasked from the start, block 1 all masked
+    tok0 = torch.cat([full[:B], torch.full((B,), mask, dtype=torch.int32, device=DEV)])
+    tok = tok0.clone()
+    steps, commits = bdm.bdm_denoise_block(tok, emb, stack, w_head, s.k, mask, 0.95,
+                                           block_tokens=B)
+    alone = tok0[B:].clone()
+    steps1, commits1 = bdm.bdm_denoise_block(alone, emb, stack, w_head, s.k, mask, 0.95)
+    torch.cuda.synchronize()
+    assert torch.equal(tok[:B], full[:B]) and torch.equal(tok[B:], alone)
+    assert (steps, commits) == (steps1, commits1) and sum(commits) == B
+    assert not (tok == mask).any()
