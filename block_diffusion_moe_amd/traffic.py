@@ -27,6 +27,11 @@ factor is reported for comparison only.
         and GRBM_GUI_ACTIVE: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over
         every SIMD) / (GRBM_GUI_ACTIVE / XCDs (it is summed over the XCDs) x
         CUs x 4 SIMDs); MFMA flop per launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.
+    python -m block_diffusion_moe_amd.traffic timeline --trace FILE --out FILE [--command TEXT]
+        from a `rocprofv3 --kernel-trace` CSV of the benchmark: where the time
+        of one denoise step, and of the MoE layer launched back to back, goes
+        (median duration of each kernel in launch order and median idle gap
+        before it, over every matching launch sequence).
 """
 from __future__ import annotations
 
@@ -185,6 +190,87 @@ def mfma(a):
     print("\n".join(out))
 
 
+# launch sequences of the single-block path (kernel names without arguments)
+MOE_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, false>",
+           "bdm::group_kernel<4>", "bdm::gateup_kernel<8, false>", "bdm::down_kernel<16, false>",
+           "bdm::combine_kernel")
+STEP_SEQ = ("bdm::rmsnorm_kernel",) + MOE_SEQ + ("bdm::head_coop_kernel<8, 2, false, false>",
+                                                   "bdm::head_merge_kernel")
+
+
+def _kernel_name(n: str) -> str:
+    n = n[5:] if n.startswith("void ") else n
+    return n.split("(", 1)[0]
+
+
+def read_trace(path: str):
+    """(start ns, end ns, name) of every bdm kernel dispatch, in start order."""
+    out = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            n = _kernel_name(r["Kernel_Name"])
+            if n.startswith("bdm"):
+                out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), n))
+    out.sort()
+    return out
+
+
+def sequences(trace, seq, before=None, after=None):
+    """Start indices where the dispatches are exactly `seq`; with `before` /
+    `after`, also preceded / followed by a dispatch of that name."""
+    names = [t[2] for t in trace]
+    hits = []
+    for i in range(len(names) - len(seq) + 1):
+        if tuple(names[i:i + len(seq)]) != seq:
+            continue
+        if before is not None and (i == 0 or names[i - 1] != before):
+            continue
+        if after is not None and (i + len(seq) >= len(names) or names[i + len(seq)] != after):
+            continue
+        hits.append(i)
+    return hits
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return 0.0 if n == 0 else (v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2]))
+
+
+def _table(trace, seq, hits, title):
+    out = [f"## {title}", "", f"{len(hits)} launch sequences.", "",
+           "| kernel | median µs | median gap before µs |", "|---|---:|---:|"]
+    tot_d = tot_g = 0.0
+    for j, n in enumerate(seq):
+        d = _median([(trace[i + j][1] - trace[i + j][0]) / 1e3 for i in hits])
+        g = _median([(trace[i + j][0] - trace[i + j - 1][1]) / 1e3 for i in hits]) if j else 0.0
+        tot_d += d
+        tot_g += g
+        out.append(f"| `{n}` | {d:.2f} | {g:.2f} |" if j else f"| `{n}` | {d:.2f} | — |")
+    span = _median([(trace[i + len(seq) - 1][1] - trace[i][0]) / 1e3 for i in hits])
+    out += [f"| sum | {tot_d:.2f} | {tot_g:.2f} |", "",
+            f"First start to last end: median {span:.2f} µs.", ""]
+    return out
+
+
+def timeline(a):
+    trace = read_trace(a.trace)
+    out = ["# Where the time goes: denoise step and MoE layer (rocprofv3 kernel trace)", ""]
+    if a.command:
+        out += ["Made by:", "", "```", a.command, "```", ""]
+    out += ["Medians over every matching launch sequence in the trace; a gap is the idle "
+            "time between the end of the previous dispatch and the start of this one.", ""]
+    step = sequences(trace, STEP_SEQ)
+    moe = sequences(trace, MOE_SEQ, before=MOE_SEQ[-1], after=MOE_SEQ[0])
+    if step:
+        out += _table(trace, STEP_SEQ, step, "Denoise step (eager, plain and graph replays)")
+    if moe:
+        out += _table(trace, MOE_SEQ, moe, "MoE layer launched back to back")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(out))
+    print("\n".join(out))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -199,11 +285,17 @@ def main(argv=None):
     m.add_argument("--cus", type=int, default=256)
     m.add_argument("--xcds", type=int, default=8)
     m.add_argument("--command", default="")
+    t = sub.add_parser("timeline")
+    t.add_argument("--trace", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", default="")
     a = p.parse_args(argv)
     if a.cmd == "copy":
         copy_kernel()
     elif a.cmd == "mfma":
         mfma(a)
+    elif a.cmd == "timeline":
+        timeline(a)
     else:
         summarize(a)
 
