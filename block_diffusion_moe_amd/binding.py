@@ -237,6 +237,12 @@ def _expert_layout(gate, up, down, sgate, sup, sdown) -> int:
                 u.offset != g.offset + 16 * g.shape[-1]:
             raise ValueError("gate/up must both come from one bdm_pack_gate_up call "
                              "(routed and shared alike)")
+        rows = 1
+        for d in g.shape[:-1]:
+            rows *= d
+        if rows % 16 or g.data.numel() - g.offset < 2 * rows * g.shape[-1]:
+            raise ValueError("gate/up pair: rows not a multiple of 16, or the buffer "
+                             "holds less than both matrices")
     if down.pair is not None or (sdown is not None and sdown.pair is not None):
         raise ValueError("down matrices are packed with bdm_pack_weights")
     return BDM_LAYOUT_MFMA_TILES_GU

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bdmoe.h")
@@ -327,3 +328,32 @@ def test_verify_validation(lib):
     assert lib.bdm_head_workspace_bytes(33, 2048, 248320, ctypes.byref(h)) == 0
     assert n.value > h.value
     assert lib.bdm_head_verify_workspace_bytes(33, 768, 248320, ctypes.byref(n)) == -2
+
+
+def test_binding_weight_layout_detection():
+    """The binding's choice of weight_layout from the kinds of expert
+    matrices it is given (host logic only: no library call)."""
+    from block_diffusion_moe_amd import binding as bd
+    I, H = 32, 64
+    rm = torch.zeros((2, I, H), dtype=torch.bfloat16)
+    down = bd.Packed(torch.zeros(2 * H * I, dtype=torch.bfloat16), (2, H, I))
+    plain = bd.Packed(torch.zeros(2 * I * H, dtype=torch.bfloat16), (2, I, H))
+    buf = torch.zeros(2 * 2 * I * H, dtype=torch.bfloat16)
+    g = bd.Packed(buf, (2, I, H), 0, "gate")
+    u = bd.Packed(buf, (2, I, H), 16 * H, "up")
+    assert bd._expert_layout(rm, rm, rm, None, None, None) == bd.BDM_LAYOUT_ROW_MAJOR
+    assert bd._expert_layout(plain, plain, down, None, None, None) == bd.BDM_LAYOUT_MFMA_TILES
+    assert bd._expert_layout(g, u, down, None, None, None) == bd.BDM_LAYOUT_MFMA_TILES_GU
+    with pytest.raises(ValueError):                     # row-major mixed with packed
+        bd._expert_layout(rm, plain, down, None, None, None)
+    with pytest.raises(ValueError):                     # gate and up swapped
+        bd._expert_layout(u, g, down, None, None, None)
+    with pytest.raises(ValueError):                     # halves of different buffers
+        bd._expert_layout(g, bd.Packed(buf.clone(), (2, I, H), 16 * H, "up"), down,
+                          None, None, None)
+    with pytest.raises(ValueError):                     # shared expert not a pair
+        bd._expert_layout(g, u, down, plain, plain, down)
+    short = torch.zeros(2 * I * H + 16 * H, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):                     # buffer shorter than both matrices
+        bd._expert_layout(bd.Packed(short, (2, I, H), 0, "gate"),
+                          bd.Packed(short, (2, I, H), 16 * H, "up"), down, None, None, None)
