@@ -24,7 +24,7 @@
 //                   and 16 up rows in one burst, multiplies the expert's
 //                   token tiles, and the partial sums meet in LDS where
 //                   silu(g) * u is formed and stored as bf16.
-//   down_kernel     work item = (expert, 64 rows of H).  Each wave owns 16
+//   down_kernel     work item = (expert, 32 rows of H).  Each wave owns 16
 //                   output rows and the whole K = I; fp32 results per pair.
 //   combine_kernel  y_t = bf16(r_t + sum_j w_tj Y_tj + Y_t,shared), fixed
 //                   order, no atomics.
@@ -37,7 +37,7 @@ constexpr int kGuCols = 16;     // I columns per gate/up work item
 constexpr int kGuWaves = 8;     // waves splitting K in gate/up
 constexpr int kGuMt = 2;        // 16-token tiles multiplied per pass
 #ifndef BDM_DN_WAVES
-#define BDM_DN_WAVES 4
+#define BDM_DN_WAVES 2
 #endif
 constexpr int kDnWaves = BDM_DN_WAVES;  // waves per down work item, 16 rows of H each
 constexpr int kDnRows = 16 * kDnWaves;  // H rows per down work item
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kGuWaves * 64, 4) void gateup_kernel(
   }
 }
 
-// work item = (touched group, 64 rows of H); each wave owns 16 output rows
+// work item = (touched group, kDnRows rows of H); each wave owns 16 output rows
 // and the whole K = I (KS k-steps, KS <= KSMAX)
 template <int KSMAX, bool GUARD>
 __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
