@@ -56,8 +56,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sets", type=int, default=4, help="rotated weight sets / token blocks")
     p.add_argument("--cpu-blocks", type=int, default=4,
-                   help="weight sets whose blocks the CPU oracle cycles over for cpu_baseline, "
-                        "at least 10 s of oracle time (0: skip)")
+                   help="weight sets whose blocks the CPU oracle cycles over for cpu_baseline "
+                        "(0: skip the CPU baseline)")
+    p.add_argument("--cpu-runs", type=int, default=5,
+                   help="timed oracle runs per workload after one warm-up (median reported)")
     p.add_argument("--stack-layers", type=int, default=40,
                    help="layers of the denoise-loop stack measured beside the step (0: skip)")
     p.add_argument("--layout", type=int, default=2,
@@ -372,6 +374,7 @@ def main():
             "unique_experts": round(ukm, 2), "busiest_expert_tokens": hot, "bytes": int(sk_bytes),
             "GB_s": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(sk_bytes / (sk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    skew_host = [(synth.bf16_bits(skew_x[r]), skew_b[r].cpu().numpy()) for r in range(args.sets)]
     del skew_x, skew_b, wsk, yk, ik
 
     # the head statistics over the same 16 / 32 / 64 blocks (all their rows
@@ -427,7 +430,8 @@ def main():
 
     cpu = None
     if args.cpu_blocks > 0:
-        cpu = cpu_baseline(sets[:args.cpu_blocks])
+        cpu = cpu_baseline(torch, dev, sets[:args.cpu_blocks], skew_host[:args.cpu_blocks],
+                           args.stack_layers, args.cpu_runs)
 
     out = {
         "metric": "denoise-block tokens/s per MoE layer + achieved HBM GB/s (% of MI355X peak)",
@@ -506,21 +510,11 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
         layers.append({"w_router": wr, "w_gate": g, "w_up": u, "w_down": pk(wd),
                        "ws_gate": sgp, "ws_up": sup, "ws_down": pk(sd)})
         del wg, wu, wd, sg, su, sd
-    g = torch.Generator(device=dev)
-    g.manual_seed(902)
-    emb = torch.randn((HS.V, L.H), generator=g, device=dev).to(torch.bfloat16)
+    emb = stack_embedding(torch, L, HS, dev)
     w_head = bdm.bdm_pack_weights(synth.head_weights(HS, 0, device=dev))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    # a block late in its loop: 31 committed tokens (distinct seeded ids) and
-    # one masked slot, so the 32 rows differ (an all-masked block has 32
-    # identical rows and touches only k experts per layer)
-    gt = torch.Generator(device="cpu")
-    gt.manual_seed(903)
-    ids = torch.randperm(HS.V - 1, generator=gt)[:L.T]
-    ids = ids + (ids >= HS.mask_id).long()                  # never the mask id
-    tok0 = ids.to(torch.int32).to(dev)
-    tok0[L.T // 2] = HS.mask_id
+    gt, tok0 = stack_block(torch, L, HS, dev)
     # this step's routing per layer (untimed), for the bytes
     x = emb[tok0.long()].contiguous()
     xn = torch.empty_like(x)
@@ -644,6 +638,27 @@ def stack_step(bdm, synth, torch, np, dev, args, L, HS):
     return out
 
 
+def stack_embedding(torch, L, HS, dev):
+    """The stack step's embedding table [V][H] bf16 (seeded, N(0,1))."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(902)
+    return torch.randn((HS.V, L.H), generator=g, device=dev).to(torch.bfloat16)
+
+
+def stack_block(torch, L, HS, dev):
+    """The stack step's block: late in its loop, 31 committed tokens (distinct
+    seeded ids) and one masked slot, so the 32 rows differ (an all-masked
+    block has 32 identical rows and touches only k experts per layer).
+    Returns (the generator, for further draws; the block on `dev`)."""
+    gt = torch.Generator(device="cpu")
+    gt.manual_seed(903)
+    ids = torch.randperm(HS.V - 1, generator=gt)[:L.T]
+    ids = ids + (ids >= HS.mask_id).long()                  # never the mask id
+    tok0 = ids.to(torch.int32).to(dev)
+    tok0[L.T // 2] = HS.mask_id
+    return gt, tok0
+
+
 def stream_read_gbs(torch, dev, reps, nbytes=None):
     """Read bandwidth of a plain stream of the head's size (so that its fixed
     launch, ramp and tail costs weigh as much as the head's) with the weight
@@ -711,70 +726,172 @@ def head_traffic():
     return int(float(vals["traffic_bytes"]))
 
 
-def cpu_baseline(blocks, min_s=10.0, max_blocks=12):
-    """The CPU oracle (as it stands) on whole blocks of the rotated sets: the
-    same step (RMSNorm, MoE layer, head + unmask) for all 32 slots of a block,
-    with that block's own weights, block after block (cycling over the sets)
-    until at least `min_s` seconds of oracle time or `max_blocks` blocks.
-    Host copies of the weights are made outside the timed region.  Scaled to
-    block-tokens/s."""
+def cpu_baseline(torch, dev, blocks, skew_host, stack_layers, runs=5):
+    """The CPU oracle (as it stands: numpy float64, per-token loops) on the
+    host cores, beside the GPU run, on the same seeded inputs.
+
+    * Thread count: numpy's BLAS runs the oracle's products.  The MoE layer's
+      are per-token matrix-vector products over one expert (512 x 2,048),
+      too small for BLAS threads to pay off; the head's are a real GEMM
+      (32 rows x 248,320 x 2,048).  Each is timed with BLAS limited to one
+      thread and with every host core, and each phase then uses its faster
+      setting.
+    * The one-block MoE layer (Clover shape, 32 tokens) and the head + unmask
+      (32 rows, 248,320-row head): one warm-up, then the median of `runs`
+      timed runs (rotating over the weight sets) at each thread setting.
+    * The load-skew batch (256 tokens, log-Zipf router offset): one warm-up,
+      median of `runs`, at the MoE layer's faster setting.
+    * One step of the 40-layer stack from the GPU stack step's block
+      (embedding rows, 40 x (RMSNorm + MoE layer), final RMSNorm, head +
+      unmask): each layer's weights regenerated on the device from its seed
+      and its touched experts copied to the host before that layer is timed
+      (copy time excluded).
+    Weights are copied to the host before the timed regions.  `value` is the
+    same step the GPU's `value` times (RMSNorm + MoE layer + head + unmask
+    over one 32-slot block), each phase at its faster thread setting."""
+    import numpy as np
     import synth
     from oracle import head as ohead, moe as omoe, norm as onorm
-
-    threads = _blas_threads()
-    host = {}
-    dt, ntok, nblk = 0.0, 0, 0
-    while nblk < max_blocks and (dt < min_s or nblk == 0):
-        r = nblk % len(blocks)
-        inp, w_head, blk = blocks[r]
-        if r not in host:
-            host[r] = (synth.moe_host(inp, lazy=False), synth.bf16_bits(inp.x),
-                       synth.bf16_bits(w_head), blk.tokens.cpu().numpy())
-        h, xb, wh, tok = host[r]
-        t0 = time.perf_counter()
-        xn = onorm.rmsnorm(xb, 1e-6)
-        y = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
-                           h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)["y"]
-        ohead.head_unmask(y, wh, tok, synth.HEAD.mask_id, 0.95)
-        dt += time.perf_counter() - t0
-        ntok += xb.shape[0]
-        nblk += 1
-    # the same step on one host thread (one block), phases timed apart
-    single = None
     try:
         from threadpoolctl import threadpool_limits
-        h, xb, wh, tok = host[0]
-        with threadpool_limits(limits=1, user_api="blas"):
-            t0 = time.perf_counter()
-            xn = onorm.rmsnorm(xb, 1e-6)
-            y = omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
-                               h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)["y"]
-            t1 = time.perf_counter()
-            ohead.head_unmask(y, wh, tok, synth.HEAD.mask_id, 0.95)
-            t2 = time.perf_counter()
-        single = {"value": round(xb.shape[0] / (t2 - t0), 4), "unit": "block-tokens/s",
-                  "cores": 1, "moe_layer_s": round(t1 - t0, 3), "head_s": round(t2 - t1, 3),
-                  "sample": "one 32-slot block, BLAS limited to one thread"}
     except ImportError:
-        pass
-    return {"value": round(ntok / dt, 4), "unit": "block-tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{nblk} whole 32-slot blocks ({ntok} tokens, cycling over "
-                      f"{min(nblk, len(blocks))} weight sets) through RMSNorm + MoE layer + "
-                      f"head/unmask (numpy float64 oracle), {dt:.1f} s; weights copied to host "
-                      f"before the timed region",
-            "single_thread": single}
-
-
-def _blas_threads():
+        threadpool_limits = None
+    ncpu = os.cpu_count() or 1
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
         pass
-    return os.cpu_count()
+
+    def limits(n):
+        if threadpool_limits is None:
+            import contextlib
+            return contextlib.nullcontext()
+        return threadpool_limits(limits=n, user_api="blas")
+
+    def median_of(fn, n_sets):
+        fn(0)                                            # warm-up
+        ts = []
+        for i in range(runs):
+            t0 = time.perf_counter()
+            fn(i % n_sets)
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), [round(t, 4) for t in ts]
+
+    host = []
+    for inp, w_head, blk in blocks:
+        host.append((synth.moe_host(inp, lazy=False), synth.bf16_bits(inp.x),
+                     synth.bf16_bits(w_head), blk.tokens.cpu().numpy()))
+    nsets = len(host)
+    print(f"[bench] cpu baseline: {ncpu} host cores ({model})", file=sys.stderr, flush=True)
+
+    def layer(r):
+        h, xb, _, _ = host[r]
+        xn = onorm.rmsnorm(xb, 1e-6)
+        return omoe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                              h["ws_gate"], h["ws_up"], h["ws_down"], residual=xb)["y"]
+
+    ys = [layer(r) for r in range(nsets)]               # each set's head input
+
+    def head(r):
+        _, _, wh, tok = host[r]
+        ohead.head_unmask(ys[r], wh, tok, synth.HEAD.mask_id, 0.95)
+
+    def skew(r):
+        h = host[r][0]
+        xb, bias = skew_host[r]
+        omoe.moe_block(xb, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], h["k"],
+                       h["ws_gate"], h["ws_up"], h["ws_down"], bias=bias)
+
+    per = {}
+    for name, fn in (("moe_layer", layer), ("head_unmask", head)):
+        per[name] = {}
+        for n in sorted({1, ncpu}):
+            with limits(n):
+                med, ts = median_of(fn, nsets)
+            per[name][f"{n}_threads"] = {"median_s": round(med, 4), "runs_s": ts}
+            print(f"[bench] cpu {name} {n} thread(s): median {med:.3f} s", file=sys.stderr,
+                  flush=True)
+    best = {k: min(((int(t.split("_")[0]), v["median_s"]) for t, v in d.items()),
+                   key=lambda a: a[1]) for k, d in per.items()}
+    with limits(best["moe_layer"][0]):
+        sk_med, sk_ts = median_of(skew, len(skew_host))
+    print(f"[bench] cpu skew batch: median {sk_med:.3f} s", file=sys.stderr, flush=True)
+    step_s = best["moe_layer"][1] + best["head_unmask"][1]
+    out = {"value": round(32 / step_s, 4), "unit": "block-tokens/s",
+           "cores": max(best["moe_layer"][0], best["head_unmask"][0]), "kind": "oracle",
+           "host_cores": ncpu, "cpu_model": model,
+           "sample": f"one 32-slot block step = the one-block MoE layer (median of {runs} runs "
+                     f"after one warm-up, {best['moe_layer'][0]} BLAS thread(s)) + the head and "
+                     f"unmask (median of {runs}, {best['head_unmask'][0]} BLAS thread(s)); "
+                     f"numpy float64 oracle, weights copied to the host before the timed "
+                     f"region",
+           "threads_used": {"moe_layer": best["moe_layer"][0],
+                            "head_unmask": best["head_unmask"][0]},
+           "per_thread_setting": per,
+           "moe_layer_block_tokens_per_s": round(32 / best["moe_layer"][1], 4),
+           "head_unmask_positions_per_s": round(32 / best["head_unmask"][1], 4),
+           "skew_8_blocks": {"median_s": round(sk_med, 4), "runs_s": sk_ts,
+                             "block_tokens_per_s": round(256 / sk_med, 4),
+                             "threads": best["moe_layer"][0]}}
+    del host, ys
+    if stack_layers > 0:
+        out["stack_step"] = cpu_stack_step(torch, dev, stack_layers, best, limits)
+    return out
+
+
+def cpu_stack_step(torch, dev, nl, best, limits):
+    """One step of the stack on the CPU oracle from the GPU stack step's
+    block; per layer the weights are regenerated on the device from their
+    seed and the layer's touched experts (the oracle's own routing, taken
+    untimed first) copied to the host before the layer is timed."""
+    import numpy as np
+    import synth
+    from oracle import head as ohead, moe as omoe, norm as onorm
+    L, HS = synth.LAYER, synth.HEAD
+    emb = stack_embedding(torch, L, HS, dev)
+    _, tok0 = stack_block(torch, L, HS, dev)
+    x = synth.bf16_bits(emb[tok0.long()].contiguous())
+    tok = tok0.cpu().numpy()
+    del emb
+    t_layers = 0.0
+    for l in range(nl):
+        wr, wg, wu, wd, sg, su, sd, _ = synth.moe_weights(L, 100 + l, dev)
+        wr_h = wr.cpu().numpy()
+        xn = onorm.rmsnorm(x, 1e-6)
+        idx = omoe.route(xn, wr_h, L.k)[0]               # untimed: which experts to copy
+        touched = np.unique(idx)
+        W = {n: {int(e): synth.bf16_bits(t[int(e)]) for e in touched}
+             for n, t in (("g", wg), ("u", wu), ("d", wd))}
+        shared = (synth.bf16_bits(sg), synth.bf16_bits(su), synth.bf16_bits(sd))
+        del wg, wu, wd, sg, su, sd
+        with limits(best["moe_layer"][0]):
+            t0 = time.perf_counter()
+            xn = onorm.rmsnorm(x, 1e-6)
+            x = omoe.moe_block(xn, wr_h, W["g"], W["u"], W["d"], L.k, *shared, residual=x)["y"]
+            t_layers += time.perf_counter() - t0
+        del W, shared
+        if (l + 1) % 10 == 0:
+            print(f"[bench] cpu stack step: {l + 1} layers, {t_layers:.1f} s", file=sys.stderr,
+                  flush=True)
+    wh = synth.bf16_bits(synth.head_weights(HS, 0, device=dev))
+    torch.cuda.empty_cache()
+    with limits(best["head_unmask"][0]):
+        t0 = time.perf_counter()
+        h = onorm.rmsnorm(x, 1e-6)
+        ohead.head_unmask(h, wh, tok, HS.mask_id, 0.95)
+        t_head = time.perf_counter() - t0
+    del wh
+    return {"layers": nl, "s": round(t_layers + t_head, 3), "layers_s": round(t_layers, 3),
+            "head_s": round(t_head, 3),
+            "block_tokens_per_s": round(L.T / (t_layers + t_head), 4),
+            "sample": f"one step (embedding rows, {nl} x (RMSNorm + MoE layer), final "
+                      f"RMSNorm, head + unmask) of the GPU stack step's block, each phase at "
+                      f"its faster thread setting; touched experts copied to the host untimed"}
 
 
 if __name__ == "__main__":

@@ -1,11 +1,11 @@
 // Untied output head fused with the low-confidence unmask rule.
 //
 // Page "Clover-35B-A3B: how a diffusion model gets to 680 tokens a second,
-// read from its files", section "What Clover is": the untied head holds
-// 508,559,360 parameters and is read in full at every step; section "How it
-// writes", steps 2-3: per slot the most likely token and its probability
-// with the mask token's logit at minus infinity, then commit every
-// still-masked slot at or above the threshold, else the most confident one.
+// read from its files", section "What Clover is": the head has its own
+// 508,559,360 weights and every step streams all of them; section "How it
+// writes", steps 2-3: each slot's prediction excludes the mask token and
+// carries its probability; masked slots at or above the threshold are
+// filled, and if none is, the best masked slot alone.
 //
 //   head_tile_kernel   persistent, one workgroup per CU.  The weight rows
 //                      stream from HBM once into MFMA B registers; the block's
@@ -528,10 +528,15 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
     }
     st = row_merge_stat(st);
     if (on && sub == 0) {
-      const float cf = 1.0f / st.s;
+      // a row with a finite maximum has s >= 1 (its maximum contributes
+      // e^0); no finite logit (s = 0, id INT32_MAX) or a NaN sum gives no
+      // prediction: argmax -1, conf 0, and the rule never commits it
+      const bool ok = st.a != INT32_MAX && st.s >= 1.0f;
+      const float cf = ok ? 1.0f / st.s : 0.0f;
+      const int a = ok ? st.a : -1;
       sconf[t] = cf;
-      sarg[t] = st.a;
-      if (argmax_out) argmax_out[t] = st.a;
+      sarg[t] = a;
+      if (argmax_out) argmax_out[t] = a;
       if (conf_out) conf_out[t] = cf;
     }
   }
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
       const bool m = t < r1 && stok[t] == mask_id;
       int commit = 0;
       nmasked += wave_sum_i(m ? 1 : 0);
-      if (m) {
+      if (m && sarg[t] >= 0) {
         const float cf = sconf[t];
         if (cf >= threshold) commit = 1;
         if (cf > best_c || (cf == best_c && t < best_t)) {
@@ -630,20 +635,23 @@ __global__ __launch_bounds__(1024) void verify_merge_kernel(
     }
     st = row_merge_vstat(st);
     if (on && sub == 0) {
+      // no finite logit, or a NaN sum: no prediction (argmax -1), rejected
+      const bool ok = st.a != INT32_MAX && st.s >= 1.0f;
+      const int am = ok ? st.a : -1;
       const float ent = logf(st.s) - st.q / st.s;
       const float pc = expf(st.lc - st.m) / st.s;
       int acc = 0;
       if (t < T1 - 1) {
         const int c = cand[t];
-        acc = (c < 0 || c >= V) ? 0
-              : (rule == 0)     ? (c == st.a ? 1 : 0)
-                                : (pc >= fminf(ratio, delta * expf(-ent)) ? 1 : 0);
+        acc = (!ok || c < 0 || c >= V) ? 0
+              : (rule == 0)            ? (c == am ? 1 : 0)
+                                       : (pc >= fminf(ratio, delta * expf(-ent)) ? 1 : 0);
         if (accept_out) accept_out[t] = acc;
         if (pcand_out) pcand_out[t] = pc;
       }
       sacc[t] = acc;
-      sarg[t] = st.a;
-      if (argmax_out) argmax_out[t] = st.a;
+      sarg[t] = am;
+      if (argmax_out) argmax_out[t] = am;
       if (entropy_out) entropy_out[t] = ent;
     }
   }

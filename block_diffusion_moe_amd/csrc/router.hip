@@ -1,8 +1,8 @@
 // Router and top-k selection for the routed MoE layer.
 //
 // Page "Clover-35B-A3B: how a diffusion model gets to 680 tokens a second,
-// read from its files", section "What Clover is": 256 routed experts, each
-// token routed to 8 of them, plus one shared expert that is always on.
+// read from its files", section "What Clover is": 256 routed experts, 8 picked
+// per token, and a shared expert that every token uses.
 //
 //   router_kernel  logits l[t][e] = x_t . w_router[e] (+ bias[e]) in fp32.
 //                  A small GEMM (T x H) . (H x E) on bf16 MFMA: each fp32

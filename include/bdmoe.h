@@ -106,13 +106,13 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
 /*
  * bdm_moe_block_forward -- one routed MoE feed-forward layer over a block.
  *
- * [files] "What Clover is": every layer has 256 routed experts, routes each
- * token to 8 of them and adds one shared expert that is always on; an expert
- * is gate and up at 2,048 by 512 and down at 512 by 2,048.  [deep] "What
- * DiffuSpace actually shipped": top-8 routing plus one shared expert per
- * layer.  [files] "The expert selection": a block of 32 tokens reads the
- * union of the tokens' expert sets, so the layer is computed per expert over
- * all the block's tokens routed to it.
+ * [files] "What Clover is": a layer holds 256 routed experts; each token is
+ * sent to 8 of them, and a 257th, shared expert serves every token; gate and
+ * up map 2,048 to 512 and down maps 512 back to 2,048.  [deep] "What
+ * DiffuSpace actually shipped": the same top-8 plus shared-expert layout.
+ * [files] "The expert selection": a block's step reads every expert that any
+ * of its tokens picked, so the layer is computed per expert over all the
+ * block's tokens routed to it.
  *
  * For every token t (row of x), independently:
  *   l      = fp32(x_t) . w_router^T (+ router_bias)             fp32 logits [E]
@@ -246,11 +246,11 @@ BDM_API int bdm_denoise_workspace_bytes(int T, int H, int I, int E, int k, int h
 /*
  * bdm_denoise_block -- the denoise loop over one block.
  *
- * [files] "How it writes": a block starts masked; each step runs the model
- * over the whole block, takes every slot's most likely token and its
- * probability with the mask logit at -inf, commits every still-masked slot
- * that reaches the threshold (else the single most confident one), and the
- * loop repeats until no slot is masked; committed slots stay as they are.
+ * [files] "How it writes": every slot of a new block holds the mask token; a
+ * step runs the model on all slots at once, predicts each slot (mask logit
+ * excluded) with its probability, fills the masked slots that reach the
+ * threshold (or, if none does, the most confident one), and steps repeat
+ * until the block holds no mask; a filled slot is never rewritten.
  * The model here is the expert part of the stack only (pre-norm):
  *   x = w_embed[tokens];  for each layer: x = bf16(x + MoE(RMSNorm(x)));
  *   h = RMSNorm(x);  tokens = unmask(head(h))        (RMSNorm eps 1e-6, gamma 1)
@@ -301,12 +301,13 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
 /*
  * bdm_lm_head_unmask -- untied output head fused with the unmask rule.
  *
- * [files] "What Clover is": the output head (508,559,360 = 248,320 x 2,048
- * parameters) is untied from the embedding and read in full at every step.
- * [files] "How it writes", steps 2-3: for every slot take the most likely
- * token and its probability, with the mask token's logit set to minus
- * infinity first; commit every still-masked slot whose probability clears
- * the threshold; if none clears it, commit the single most confident one.
+ * [files] "What Clover is": the head has its own weights (not the
+ * embedding's), 248,320 x 2,048 = 508,559,360 of them, and every step streams
+ * all of them.  [files] "How it writes", steps 2-3: each slot's prediction is
+ * its highest-scoring token other than the mask token, with that token's
+ * probability as confidence; masked slots at or above the threshold are
+ * filled, and when no slot qualifies the most confident masked slot is filled
+ * alone.
  *
  *   l_t     = fp32 logits h_t . w_head^T for all V rows (never stored)
  *   l_t[mask_id] = -inf
@@ -316,6 +317,10 @@ BDM_API int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes);
  *         argmax_t) iff conf_t >= threshold.  If fallback != 0 and no row
  *         committed but some row is masked, commit the masked row with the
  *         largest conf_t (equal: lowest t).  Other rows are never changed.
+ *   A row with no finite logit (all -inf or NaN, e.g. a NaN hidden row) or
+ *   whose sum of exponentials is NaN has no prediction: argmax_t = -1,
+ *   conf_t = 0, and the rule never commits it (nor picks it as the
+ *   fallback); it stays masked and n_committed does not count it.
  *
  * Arguments
  *   h            [T][H] bf16        final hidden states of the block
@@ -364,7 +369,8 @@ BDM_API int bdm_lm_head_unmask(const uint16_t* h, int T, int H, const uint16_t* 
  *
  * bdm_unmask_from_stats -- phase 2: per token, merge stat_*[t*stat_stride +
  *   0 .. parts-1] (max of maxima; sums rescaled to the common max and added;
- *   equal maxima keep the lowest id), conf = 1/sum, argmax = that id, then the
+ *   equal maxima keep the lowest id), conf = 1/sum, argmax = that id (a row
+ *   with no finite logit: -1 and conf 0, as in bdm_lm_head_unmask), then the
  *   commit rule of bdm_lm_head_unmask on tokens (same arguments, block_tokens
  *   included, and outputs).
  */
@@ -397,6 +403,8 @@ BDM_API int bdm_unmask_from_stats(const float* stat_max, const float* stat_sum,
  *     rule BDM_VERIFY_EXACT:     cand[t] == argmax_t
  *     rule BDM_VERIFY_THRESHOLD: p_t(cand[t]) >= min(ratio, delta * exp(-H_t))
  *                                (the page gives ratio 0.9, delta 0.6)
+ *   a row with no finite logit (or a NaN sum) has argmax -1 and accepts
+ *   nothing
  *   r        = number of leading accepted candidates (0 <= r <= T)
  *   tokens_out[0..r-1] = cand[0..r-1]; tokens_out[r] = argmax_r;
  *   tokens_out[r+1..T] = -1; *n_accepted = r  (r + 1 tokens this round)

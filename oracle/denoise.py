@@ -1,12 +1,12 @@
 """The denoise loop over one block (test infrastructure only).
 
-The files page, section "How it writes": a block of slots starts all masked;
-every step runs the model over the whole block, takes each slot's most
-likely token and its probability (the mask token's logit at minus
-infinity), commits every still-masked slot whose probability reaches the
-threshold, or the single most confident one if none does, and repeats until
-no slot is masked; committed slots are never revisited ([deep] "What
-DiffuSpace actually shipped").  Section "What Clover is" fixes block 32, the
+The files page, section "How it writes": every slot of a new block holds the
+mask token; a step runs the model on all slots together, predicts each slot
+(the mask token excluded) with the probability of that prediction, fills the
+masked slots whose probability reaches the threshold (the most confident
+masked slot alone when none does), and steps repeat until no mask is left;
+a filled slot is not rewritten later ([deep] "What DiffuSpace actually
+shipped").  Section "What Clover is" fixes block 32, the
 mask token 151669 and the threshold 0.95.
 
 What the "model" is here: the expert feed-forward part of the stack only (the

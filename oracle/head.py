@@ -2,12 +2,12 @@
 
 What it computes (the files page, "How it writes", steps 2 and 3; "What
 Clover is": mask_token_id 151669, denoising_config low_confidence with
-threshold 0.95; the output head of 508,559,360 parameters is untied and read
-in full at every step):
+threshold 0.95; the head has its own 508,559,360 weights, not the
+embedding's, and every step streams all of them):
 
 1. logits l_t = W_head h_t for every vocabulary row, taken to float32;
-2. the mask token's logit is set to minus infinity, so a slot never predicts
-   the mask;
+2. the mask token is excluded (its logit becomes -inf), so no slot can
+   predict it;
 3. a_t = the most likely token (equal logits: lowest vocabulary id) and
    conf_t = its probability = 1 / sum_v exp(l_t,v - max_v l_t,v);
 4. every still-masked slot (tokens[t] == mask_id) whose confidence reaches the

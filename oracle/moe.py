@@ -1,11 +1,10 @@
 """Routed mixture-of-experts layer over one block (test infrastructure only).
 
 What it computes, per token t of the block, independently of every other
-token (the files page, "What Clover is": every layer has 256 routed experts,
-routes each token to 8 of them and adds one shared expert that is always on;
-one expert is gate and up at 2,048 by 512 and down at 512 by 2,048; the
-deep-dive page, "What DiffuSpace actually shipped": top-8 routing plus one
-shared expert per layer):
+token (the files page, "What Clover is": a layer holds 256 routed experts,
+sends each token to 8 of them, and a shared expert serves every token; gate
+and up map 2,048 to 512, down maps 512 to 2,048; the deep-dive page, "What
+DiffuSpace actually shipped": the same top-8 plus shared-expert layout):
 
 1. router logits  l = x_t . W_r^T (+ bias), taken to float32;
 2. routing probabilities p = softmax(l) over all E experts;

@@ -301,30 +301,56 @@ def f32_host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     return t.detach().to("cpu", torch.float32).contiguous().numpy()
 
 
+class LazyPool:
+    """Bounds the host copies of several lazy layers: views created with the
+    same pool and different keys (one key per layer) share it, and indexing a
+    view whose key differs from the last one used drops the cached experts of
+    every other key.  A stack walked layer by layer then holds one layer's
+    touched experts on the host at a time."""
+
+    def __init__(self):
+        self.current = None
+        self.views = []
+
+    def use(self, key):
+        if key != self.current:
+            for v in self.views:
+                if v.key != key:
+                    v._cache.clear()
+            self.current = key
+
+
 class LazyExperts:
     """Indexable view of a [E][...] bf16 weight tensor that copies one expert
     to the host (as uint16 bits) only when it is indexed: the oracle touches
     only the experts it routes to, so a 1.6 GB layer on the device costs only
     the touched experts' bytes on the host."""
 
-    def __init__(self, t: torch.Tensor):
+    def __init__(self, t: torch.Tensor, pool: Optional[LazyPool] = None, key=None):
         self.t = t
         self.shape = tuple(t.shape)
         self._cache = {}
+        self.pool, self.key = pool, key
+        if pool is not None:
+            pool.views.append(self)
 
     def __len__(self):
         return self.shape[0]
 
     def __getitem__(self, e):
         e = int(e)
+        if self.pool is not None:
+            self.pool.use(self.key)
         if e not in self._cache:
             self._cache[e] = bf16_bits(self.t[e])
         return self._cache[e]
 
 
-def moe_host(inp: MoEInputs, lazy: bool = False) -> dict:
-    """Host views of a MoE input set for the oracle."""
-    conv = (lambda t: LazyExperts(t)) if lazy else bf16_bits
+def moe_host(inp: MoEInputs, lazy: bool = False, pool: Optional[LazyPool] = None,
+             key=None) -> dict:
+    """Host views of a MoE input set for the oracle (``pool``/``key``: see
+    LazyPool)."""
+    conv = (lambda t: LazyExperts(t, pool, key)) if lazy else bf16_bits
     d = {
         "x": bf16_bits(inp.x),
         "w_router": f32_host(inp.w_router),

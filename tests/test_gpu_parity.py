@@ -109,14 +109,24 @@ def test_moe_shapes(bdm, shape, layout):
     compare_moe(y, idx, w, o)
 
 
-@LAYOUTS
-def test_moe_clover_layer_full(bdm, layout):
-    """One Clover-shaped layer (H 2048, 256 experts, I 512, top-8, shared),
-    32-token block, every output element against the oracle."""
-    say(f"case moe clover layer T=32 full layout={layout}")
+ALL_LAYOUTS = pytest.mark.parametrize("layout", [0, 1, 2], ids=["rowmajor", "packed", "gu_pairs"])
+
+
+@pytest.fixture(scope="module")
+def clover_layer():
+    """One Clover-shaped layer and its oracle result (computed once)."""
     inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=1, device=DEV, with_residual=True)
+    return inp, oracle_moe(inp, lazy=True)
+
+
+@ALL_LAYOUTS
+def test_moe_clover_layer_full(bdm, clover_layer, layout):
+    """One Clover-shaped layer (H 2048, 256 experts, I 512, top-8, shared),
+    32-token block, every output element against the oracle, in each weight
+    layout (gu_pairs: gate/up packed as pairs, the benchmark's layout)."""
+    say(f"case moe clover layer T=32 full layout={layout}")
+    inp, o = clover_layer
     y, idx, w = run_moe(bdm, inp, layout=layout)
-    o = oracle_moe(inp, lazy=True)
     say(f"  touched experts: {o['touched']}")
     compare_moe(y, idx, w, o)
 
@@ -135,19 +145,25 @@ def test_moe_clover_layer_inplace_residual(bdm):
     assert torch.equal(buf.view(torch.int16), y_sep.view(torch.int16))
 
 
-@LAYOUTS
-def test_moe_skew_sampled(bdm, layout):
-    """Eight 32-token blocks (T = 256) with the log-Zipf router offset: the
-    routing of every token, and the outputs of a seeded sample of 24 tokens
-    (tokens are independent through the layer)."""
-    say(f"case moe skew T=256 sampled layout={layout}")
+@pytest.fixture(scope="module")
+def skew_layer():
+    """The load-skew workload (eight 32-token blocks, T = 256, log-Zipf router
+    offset) and its oracle result over every token (computed once)."""
     inp = synth.skew_inputs(seed=0, block_seed=1, device=DEV)
+    return inp, oracle_moe(inp, residual=False, lazy=True)
+
+
+@ALL_LAYOUTS
+def test_moe_skew_all_tokens(bdm, skew_layer, layout):
+    """The load-skew workload: the routing and every output element of all
+    256 tokens against the oracle, in each weight layout."""
+    say(f"case moe skew T=256 all tokens layout={layout}")
+    inp, o = skew_layer
     y, idx, w = run_moe(bdm, inp, residual=False, layout=layout)
-    tokens = np.sort(np.random.default_rng(0).choice(256, 24, replace=False))
-    o = oracle_moe(inp, residual=False, tokens=tokens, lazy=True)
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=256)
     say(f"  touched {int((counts > 0).sum())} experts, busiest {int(counts.max())} tokens")
-    compare_moe(y, idx, w, o, tokens=tokens)
+    assert int(counts.max()) > 64          # the hottest expert spans several 64-token items
+    compare_moe(y, idx, w, o)
 
 
 def test_moe_repeatable_bitwise(bdm):
