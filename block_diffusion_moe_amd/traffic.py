@@ -196,6 +196,16 @@ MOE_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, false>",
            "bdm::combine_kernel")
 STEP_SEQ = ("bdm::rmsnorm_kernel",) + MOE_SEQ + ("bdm::head_coop_kernel<8, 2, false, false>",
                                                    "bdm::head_merge_kernel")
+# the layer with the block coreset selector over one 32-token block
+CORESET_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, true>",
+               "bdm::coreset_kernel<4, true>", "bdm::gateup_kernel<8, false>",
+               "bdm::down_kernel<16, false>", "bdm::combine_kernel")
+# many-token calls: 256 tokens (the load-skew batch; one-tile router) and
+# 512 .. 2,048 tokens (multi-block batches; four-tile router)
+SKEW_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, false>",
+            "bdm::group_kernel<4>", "bdm::gateup_wide_kernel<8>", "bdm::down_wide_kernel<16>",
+            "bdm::combine_kernel")
+MULTI_SEQ = ("bdm::router_kernel<4>",) + SKEW_SEQ[1:]
 
 
 def _kernel_name(n: str) -> str:
@@ -266,6 +276,28 @@ def timeline(a):
         out += _table(trace, STEP_SEQ, step, "Denoise step (eager, plain and graph replays)")
     if moe:
         out += _table(trace, MOE_SEQ, moe, "MoE layer launched back to back")
+    cs = sequences(trace, CORESET_SEQ, before=CORESET_SEQ[-1], after=CORESET_SEQ[0])
+    if cs:
+        out += _table(trace, CORESET_SEQ, cs,
+                      "MoE layer with the coreset selector (top_p 0.9), back to back")
+    sk = sequences(trace, SKEW_SEQ, before=SKEW_SEQ[-1], after=SKEW_SEQ[0])
+    if sk:
+        out += _table(trace, SKEW_SEQ, sk,
+                      "Load-skew batch (8 blocks, 256 tokens, log-Zipf offset), back to back")
+    # the multi-block calls run size after size: one table per run of
+    # adjacent sequences
+    mb = sequences(trace, MULTI_SEQ)
+    runs, cur = [], []
+    for i in mb:
+        if cur and i != cur[-1] + len(MULTI_SEQ):
+            runs.append(cur)
+            cur = []
+        cur.append(i)
+    if cur:
+        runs.append(cur)
+    for r in runs:
+        if len(r) >= 4:                       # the timed loop (not the routing probes)
+            out += _table(trace, MULTI_SEQ, r[1:], "Multi-block call (one size), back to back")
     with open(a.out, "w") as fh:
         fh.write("\n".join(out))
     print("\n".join(out))

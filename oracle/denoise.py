@@ -37,7 +37,8 @@ from . import head, norm, stack
 
 
 def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
-                 threshold: float = 0.95, eps: float = 1e-6, coreset_top_p=None, block=None):
+                 threshold: float = 0.95, eps: float = 1e-6, coreset_top_p=None, block=None,
+                 picks=None):
     """Steps 1-4 once.  Returns the oracle.head dict (new tokens, argmax, conf,
     n_committed, exclusion masks) plus 'near_route' ([T] any layer's top-k
     near tie, or coreset rounding call) and 'h' (the final normalised hidden
@@ -45,12 +46,13 @@ def denoise_step(tokens, embed_bits, layers, head_bits, k: int, mask_id: int,
     block coreset selector (the files page, "What Clover is": shipped on at
     0.9) over blocks of min(32, B) slots.  ``block`` = B: the rows are
     several blocks of B slots, each with its own commit rule (one block of
-    T slots when None)."""
+    T slots when None).  ``picks``: per-layer expert ids replacing the
+    top-k selection (oracle.stack.stack_forward)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x = np.asarray(embed_bits)[tokens]
     B = block if block else len(tokens)
     y, near = stack.stack_forward(x, layers, k, eps, coreset_top_p=coreset_top_p,
-                                  block=min(32, max(1, B)))
+                                  block=min(32, max(1, B)), picks=picks)
     h = norm.rmsnorm(y, eps)
     out = head.head_unmask(h, head_bits, tokens, mask_id, threshold, block=block)
     out["near_route"] = near.any(axis=0) if len(layers) else np.zeros(len(tokens), bool)

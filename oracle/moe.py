@@ -71,6 +71,16 @@ def select_topk(l32_row, k: int) -> np.ndarray:
     return np.array(out, dtype=np.int64)
 
 
+def pick_weights(l32_row, picks, renorm: bool = True) -> np.ndarray:
+    """Step 4 for one token: the weights of the picked experts (ids, -1 = an
+    empty slot with weight 0) from its float32 logits: softmax over all E,
+    then renormalised over the picks (``renorm``) or not."""
+    p = softmax(np.asarray(l32_row)[None, :])[0]
+    picks = np.asarray(picks)
+    ps = np.where(picks >= 0, p[np.maximum(picks, 0)], 0.0)
+    return ps / ps.sum() if renorm else ps
+
+
 def route(x_bits, w_router, k: int, bias=None, renorm: bool = True):
     """Steps 1-4.  Returns (idx [T][k] int, w [T][k] float64, logits float32
     [T][E], near_tie [T] bool).  near_tie marks tokens whose k-th and
@@ -78,15 +88,13 @@ def route(x_bits, w_router, k: int, bias=None, renorm: bool = True):
     selection is a float-rounding coin toss and is not compared."""
     l32 = router_logits(x_bits, w_router, bias)
     T, E = l32.shape
-    p = softmax(l32)
     idx = np.zeros((T, k), dtype=np.int64)
     w = np.zeros((T, k), dtype=np.float64)
     near = np.zeros(T, dtype=bool)
     for t in range(T):
         s = select_topk(l32[t], k)
         idx[t] = s
-        ps = p[t, s]
-        w[t] = ps / ps.sum() if renorm else ps
+        w[t] = pick_weights(l32[t], s, renorm)
         if k < E:
             srt = np.sort(l32[t].astype(np.float64))[::-1]
             near[t] = (srt[k - 1] - srt[k]) < GAP_EXCLUDE

@@ -427,6 +427,39 @@ def test_stack_tokens_independent_and_matches_chained_brute():
     assert np.array_equal(cur, y)
 
 
+def test_stack_forced_picks():
+    """Routing forced to given picks (for chained comparisons): the stack's
+    own picks give the plain stack bit for bit; with every expert identical
+    the output does not depend on the picks (their weights still sum to 1),
+    so arbitrary forced picks give the plain stack too."""
+    s = synth.TINY
+    layers = [synth.moe_host(synth.moe_inputs(s, seed=110 + l)) for l in range(3)]
+    x, _, _ = synth.moe_tokens(s, 4)
+    xb = synth.bf16_bits(x)
+    y, _ = stack.stack_forward(xb, layers, s.k)
+    own, cur = [], xb
+    for h in layers:
+        xn = norm.rmsnorm(cur, 1e-6)
+        r = moe.moe_block(xn, h["w_router"], h["w_gate"], h["w_up"], h["w_down"], s.k,
+                          h["ws_gate"], h["ws_up"], h["ws_down"], residual=cur)
+        own.append(r["idx"])
+        cur = r["y"]
+    yf, _ = stack.stack_forward(xb, layers, s.k, picks=own)
+    assert np.array_equal(yf, y)
+    same = []
+    for h in layers:
+        g = dict(h)
+        for n in ("w_gate", "w_up", "w_down"):
+            g[n] = np.repeat(h[n][:1], s.E, axis=0)
+        same.append(g)
+    rng = np.random.default_rng(3)
+    rand = [np.stack([rng.choice(s.E, s.k, replace=False) for _ in range(s.T)]) for _ in same]
+    ys, _ = stack.stack_forward(xb, same, s.k)
+    yr, _ = stack.stack_forward(xb, same, s.k, picks=rand)
+    np.testing.assert_allclose(bf16.to_f64(yr), bf16.to_f64(ys), rtol=0, atol=0.04)
+    assert np.mean(yr == ys) > 0.98
+
+
 # --------------------------------------------------------------------------
 # Block coreset expert selector (files page, "The expert selection")
 # --------------------------------------------------------------------------
