@@ -12,7 +12,8 @@ from .binding import (BDM_LAYOUT_MFMA_TILES, BDM_LAYOUT_MFMA_TILES_GU, BDM_LAYOU
                       bdm_denoise_block, bdm_denoise_workspace_bytes,
                       bdm_head_stat_parts, bdm_head_verify_workspace_bytes,
                       bdm_head_workspace_bytes, bdm_lm_head_stats, bdm_lm_head_unmask,
-                      bdm_lm_head_verify, bdm_moe_block_forward, bdm_moe_workspace_bytes,
+                      bdm_lm_head_verify, bdm_moe_block_forward, bdm_moe_block_forward_noalloc,
+                      bdm_moe_workspace_bytes, BDM_STATIC_SCRATCH_BYTES,
                       bdm_unmask_from_stats, bdm_pack_gate_up, bdm_pack_weights,
                       bdm_packed_weight_elems,
                       bdm_rmsnorm, bdm_status_string, bdm_version, load, workspace)
@@ -25,6 +26,7 @@ __all__ = [
     "bdm_head_stat_parts", "bdm_head_verify_workspace_bytes", "bdm_head_workspace_bytes",
     "bdm_lm_head_stats", "bdm_lm_head_verify",
     "bdm_unmask_from_stats", "bdm_lm_head_unmask", "bdm_moe_block_forward",
+    "bdm_moe_block_forward_noalloc", "BDM_STATIC_SCRATCH_BYTES",
     "bdm_moe_workspace_bytes", "bdm_pack_gate_up", "bdm_pack_weights", "bdm_packed_weight_elems",
     "bdm_rmsnorm",
     "bdm_status_string", "bdm_version", "load", "workspace",

@@ -32,6 +32,9 @@ _SIGS = {
     "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                        _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "bdm_moe_block_forward_noalloc": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
+                                               _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
+                                               _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bdm_moe_block_forward_coreset": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
                                                _c_int, _c_float, _c_int, _vp, _vp, _vp, _c_int,
                                                _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
@@ -305,6 +308,45 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
         _ptr(y_norm), _ptr(topk_idx), _ptr(topk_w), _ptr(n_kept), _ptr(ws), ws.numel(),
         _stream(stream))
     _raise("bdm_moe_block_forward_coreset", st)
+    return y
+
+
+BDM_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def bdm_moe_block_forward_noalloc(x, w_router, w_gate, w_up, w_down, k: int, *,
+                                  router_bias=None, ws_gate=None, ws_up=None, ws_down=None,
+                                  residual=None, y=None, topk_idx=None, topk_w=None,
+                                  renorm: bool = True, stream=None, y_norm=None):
+    """bdm_moe_block_forward with the library's static per-device scratch
+    buffer instead of a workspace (nothing is allocated by the call when
+    ``y`` is given).  Calls that overlap on one device race."""
+    T, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(x, "x", torch.bfloat16, (T, H))
+    _check(w_router, "w_router", torch.float32, (E, H), dev)
+    _check(router_bias, "router_bias", torch.float32, (E,), dev)
+    _check(w_gate, "w_gate", torch.bfloat16, (E, I, H), dev)
+    _check(w_up, "w_up", torch.bfloat16, (E, I, H), dev)
+    _check(w_down, "w_down", torch.bfloat16, (E, H, I), dev)
+    _check(ws_gate, "ws_gate", torch.bfloat16, (I, H), dev)
+    _check(ws_up, "ws_up", torch.bfloat16, (I, H), dev)
+    _check(ws_down, "ws_down", torch.bfloat16, (H, I), dev)
+    _check(residual, "residual", torch.bfloat16, (T, H), dev)
+    _check(y, "y", torch.bfloat16, (T, H), dev)
+    _check(y_norm, "y_norm", torch.bfloat16, (T, H), dev)
+    _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    layout = _expert_layout(w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    st = load().bdm_moe_block_forward_noalloc(
+        _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+        layout, _ptr(residual), _ptr(y), _ptr(y_norm), _ptr(topk_idx), _ptr(topk_w),
+        _stream(stream))
+    _raise("bdm_moe_block_forward_noalloc", st)
     return y
 
 

@@ -131,25 +131,39 @@ int check_verify_shape(int T1, int H, int V) {
   return BDM_OK;
 }
 
-// Per-device cache: compute-unit count and one-time kernel set-up.  Filled on
-// the first call made with that device current; -1 marks a failed set-up.
+// The workspace of bdm_moe_block_forward_noalloc: a file-scope device array,
+// one copy per device for the life of the process.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address is
+// taken once per device (hipGetSymbolAddress, with that device current, at
+// the device's set-up below) and only that address is used.
+static __device__ __align__(256) unsigned char scratch[BDM_STATIC_SCRATCH_BYTES];
+
+// Per-device cache: compute-unit count, the device address of `scratch` and
+// one-time kernel set-up.  Filled on the first call made with that device
+// current; -1 marks a failed set-up.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<void*> g_scratch[kMaxDevices];
 
-int device_setup(int* cus) {
+int device_setup(int* cus, void** scratch_ptr = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BDM_ERR_HIP;
   int n = g_cu_count[dev].load(std::memory_order_acquire);
   if (n == 0) {
     int v = 0;
+    void* sp = nullptr;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        v <= 0 || bdm::head_prepare() != 0)
+        v <= 0 || bdm::head_prepare() != 0 ||
+        hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr ||
+        (reinterpret_cast<uintptr_t>(sp) % kAlign) != 0)
       v = -1;
+    g_scratch[dev].store(sp, std::memory_order_relaxed);
     g_cu_count[dev].store(v, std::memory_order_release);
     n = v;
   }
   if (n < 0) return BDM_ERR_HIP;
   *cus = n;
+  if (scratch_ptr) *scratch_ptr = g_scratch[dev].load(std::memory_order_relaxed);
   return BDM_OK;
 }
 
@@ -245,6 +259,31 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
                      I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, topk_idx,
                      topk_w, nullptr, workspace, workspace_bytes, stream);
+}
+
+int bdm_moe_block_forward_noalloc(const uint16_t* x, int T, int H, const float* w_router,
+                                  const float* router_bias, int E, int k, int renorm,
+                                  const uint16_t* w_gate, const uint16_t* w_up,
+                                  const uint16_t* w_down, int I, const uint16_t* ws_gate,
+                                  const uint16_t* ws_up, const uint16_t* ws_down,
+                                  int weight_layout, const uint16_t* residual, uint16_t* y,
+                                  uint16_t* y_norm, int32_t* topk_idx, float* topk_w,
+                                  void* stream) {
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y) return BDM_ERR_INVALID_ARG;
+  const int has_shared = (ws_gate != nullptr || ws_up != nullptr || ws_down != nullptr) ? 1 : 0;
+  const int st = check_moe_shape(T, H, I, E, k, has_shared);
+  if (st != BDM_OK) return st;
+  // sizes whose workspace exceeds the static buffer: rejected before any
+  // device call
+  if (moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr) > BDM_STATIC_SCRATCH_BYTES)
+    return BDM_ERR_WORKSPACE_TOO_SMALL;
+  int cus = 0;
+  void* sp = nullptr;
+  const int ds = device_setup(&cus, &sp);
+  if (ds != BDM_OK) return ds;
+  return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
+                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, topk_idx,
+                     topk_w, nullptr, sp, BDM_STATIC_SCRATCH_BYTES, stream);
 }
 
 int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* w_router,

@@ -176,6 +176,38 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bdm_moe_block_forward_noalloc -- bdm_moe_block_forward without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The same computation, kernels and bits as bdm_moe_block_forward; the
+ * workspace is instead a static device buffer of BDM_STATIC_SCRATCH_BYTES
+ * inside the library, one per device, held until the process ends (its
+ * address is looked up once per device at the library's first call on that
+ * device).  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Arguments as in bdm_moe_block_forward, without
+ * workspace and workspace_bytes.
+ * Limits: sizes whose bdm_moe_workspace_bytes exceed BDM_STATIC_SCRATCH_BYTES
+ * (e.g. T = 256 fits at the Clover shape, T = 2048 does not) return
+ * BDM_ERR_WORKSPACE_TOO_SMALL before any device call.
+ * Every call on a device uses that device's one buffer: two calls that may
+ * overlap on one device (different streams, different host threads) race;
+ * serialise them (e.g. one stream).  The buffer keeps the last call's
+ * intermediate results; nothing in it needs to start at zero.
+ */
+#define BDM_STATIC_SCRATCH_BYTES (32u << 20)
+
+BDM_API int bdm_moe_block_forward_noalloc(const uint16_t* x, int T, int H,
+                          const float* w_router, const float* router_bias, int E, int k,
+                          int renorm,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int I,
+                          const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                          int weight_layout,
+                          const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
+                          int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
  * bdm_moe_block_forward_coreset -- the same layer with the block coreset
  * expert selector in front of the experts.
  *

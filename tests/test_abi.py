@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                            "bdm_lm_head_stats",
                            "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset",
                            "bdm_denoise_workspace_bytes", "bdm_denoise_block",
-                           "bdm_head_verify_workspace_bytes", "bdm_lm_head_verify"])
+                           "bdm_head_verify_workspace_bytes", "bdm_lm_head_verify",
+                           "bdm_moe_block_forward_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -357,3 +358,27 @@ def test_binding_weight_layout_detection():
     with pytest.raises(ValueError):                     # buffer shorter than both matrices
         bd._expert_layout(bd.Packed(short, (2, I, H), 0, "gate"),
                           bd.Packed(short, (2, I, H), 16 * H, "up"), down, None, None, None)
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free MoE entry point rejects, before any device call,
+    null pointers, bad shapes and sizes whose workspace exceeds its static
+    buffer (the pointers below are never dereferenced)."""
+    from block_diffusion_moe_amd import binding
+    A = _fake(1 << 20)
+
+    def call(T=32, x=A, H=2048, E=256, k=8, I=512, y=_fake(2 << 20)):
+        return lib.bdm_moe_block_forward_noalloc(x, T, H, A, None, E, k, 1, A, A, A, I, A, A, A,
+                                                 0, None, y, None, None, None, None)
+
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(k=0) == -1
+    assert call(H=100) == -2
+    assert call(T=4096) == -2
+    for T in (512, 1024, 2048):                  # need more than the static buffer
+        assert binding.bdm_moe_workspace_bytes(T, 2048, 512, 256, 8, True) > \
+            binding.BDM_STATIC_SCRATCH_BYTES
+        assert call(T=T) == -3
+    assert binding.bdm_moe_workspace_bytes(256, 2048, 512, 256, 8, True) <= \
+        binding.BDM_STATIC_SCRATCH_BYTES
