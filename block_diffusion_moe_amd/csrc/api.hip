@@ -45,6 +45,8 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
   char* topk_idx = take(sizeof(int32_t) * T * k);
   char* topk_w = take(sizeof(float) * T * k);
   char* topk_p = take(sizeof(float) * T * k);
+  char* cand_id = take(sizeof(int32_t) * T * bdm::kCoreCand);
+  char* cand_l = take(sizeof(float) * T * bdm::kCoreCand);
   char* info = take(sizeof(int32_t) * 4);
   char* slots = take(sizeof(int) * 4 * bdm::moe_max_slots(T, E, k, has_shared));
   char* pair_rows = take(sizeof(int32_t) * P);
@@ -55,6 +57,8 @@ size_t moe_layout(int T, int H, int I, int E, int k, int has_shared, char* base,
     m->topk_idx = reinterpret_cast<int32_t*>(topk_idx);
     m->topk_w = reinterpret_cast<float*>(topk_w);
     m->topk_p = reinterpret_cast<float*>(topk_p);
+    m->cand_id = reinterpret_cast<int32_t*>(cand_id);
+    m->cand_l = reinterpret_cast<float*>(cand_l);
     m->info = reinterpret_cast<int32_t*>(info);
     m->slots = reinterpret_cast<int4*>(slots);
     m->pair_rows = reinterpret_cast<int32_t*>(pair_rows);

@@ -512,6 +512,9 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
   const int sub = tid & 15;          // thread within the token's row
   for (int t0 = 0; t0 < T; t0 += blockDim.x >> 4) {
     const int t = t0 + (tid >> 4);
+    // a wave holds 4 rows; a wave with none skips the merge (the merge is
+    // VALU-bound on this one CU)
+    if (t0 + (tid / kWave) * (kWave / 16) >= T) continue;
     const bool on = t < T;           // row-uniform
     const size_t base = static_cast<size_t>(on ? t : 0) * pstride;
     SoftStat st = softstat_empty();
@@ -618,6 +621,7 @@ __global__ __launch_bounds__(1024) void verify_merge_kernel(
   const int sub = tid & 15;
   for (int t0 = 0; t0 < T1; t0 += blockDim.x >> 4) {
     const int t = t0 + (tid >> 4);
+    if (t0 + (tid / kWave) * (kWave / 16) >= T1) continue;   // a wave with no row
     const bool on = t < T1;          // row-uniform
     const size_t base = static_cast<size_t>(on ? t : 0) * pstride;
     VStat st = vstat_empty();

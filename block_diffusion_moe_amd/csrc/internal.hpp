@@ -16,6 +16,7 @@ namespace bdm {
 // experts and k picks.  Rows of act / ypair are (token, slot) pairs: row
 // t*(k+1)+j holds the j-th pick of token t, row t*(k+1)+k its shared expert.
 constexpr int kRouterParts = 4;   // K-parts of the router GEMM (summed by select)
+constexpr int kCoreCand = 32;     // ranked first-pass candidates per token (coreset selector)
 
 // An expert work item serves at most kSlotChunk of its group's tokens; a
 // longer group (the shared expert, or a routed expert of a many-block batch)
@@ -37,6 +38,8 @@ struct MoeMeta {
   int32_t* topk_idx;    // [T][k]        picks, decreasing weight
   float* topk_w;        // [T][k]        their weights
   float* topk_p;        // [T][k]        first-pass probabilities (block coreset selector)
+  int32_t* cand_id;     // [T][kCoreCand] first-pass candidates, ranked (coreset selector)
+  float* cand_l;        // [T][kCoreCand] their logits
   int32_t* info;        // [4]           [0] number of touched expert groups
   int4* slots;          // [E+1]         {expert, offset, count, slots of the group} per slot, then -1
   int32_t* pair_rows;   // [T*(k+1)]     (token, slot) rows grouped by expert

@@ -174,17 +174,21 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ part, size
   }
 }
 
-// Top-k of one logit row.  The k-th largest key is found bit by bit from the
-// top with wave ballots (count of keys at or above a candidate), stopping
-// early once exactly k keys lie at or above it; the picks are the keys above
-// that threshold plus, among keys equal to it, the lowest expert ids.  The k
-// picks are gathered into lanes 0..k-1 (ds_permute), ranked there (larger
-// logit first, equal -> lower id) and moved to the lane of their rank.
-// Returns the j-th pick and weight in lane j (j < k).
+// Top-k of one logit row.  The kc-th largest key (kc >= k candidates) is
+// found bit by bit from the top with wave ballots (count of keys at or above
+// a candidate), stopping early once exactly kc keys lie at or above it; the
+// candidates are the keys above that threshold plus, among keys equal to it,
+// the lowest expert ids.  They are gathered into lanes 0..kc-1 (ds_permute),
+// ranked there (larger logit first, equal -> lower id) and moved to the lane
+// of their rank, so lanes 0..k-1 hold the k picks.  Returns the j-th
+// candidate in lane j (j < kc; its logit in *sel_l when asked) and, for
+// j < k, the pick's weight (and probability over all E, WANT_P).
 template <int PER, bool WANT_P = false>
 __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, int renorm,
                                           int lane, int& sel_e, float& sel_w,
-                                          float* sel_p = nullptr) {
+                                          float* sel_p = nullptr, int kc = 0,
+                                          float* sel_l = nullptr) {
+  if (kc < k) kc = k;
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) key[i] = (lane + kWave * i < E) ? logit_key(v[i]) : 0u;
@@ -196,15 +200,15 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) pre = cand;
-    if (cnt == k) {
+    if (cnt >= kc) pre = cand;
+    if (cnt == kc) {
       exact = true;
       break;
     }
   }
   const unsigned long long below = (1ull << lane) - 1ull;
   unsigned long long pm[PER];
-  int need = k;
+  int need = kc;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     pm[i] = __ballot(exact ? key[i] >= pre : key[i] > pre);
@@ -222,7 +226,7 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
     }
   }
   // gather: the pick with compact index j goes to lane j (non-picks are
-  // pushed to lane 63, which is never read: k <= 16)
+  // pushed to lane 63, which is never read: kc <= 32)
   int ck = 0, ce = 0, base = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -236,19 +240,20 @@ __device__ __forceinline__ void topk_pick(const float (&v)[PER], int E, int k, i
     }
     base += n_i;
   }
-  // rank among the k picks, then move each pick to the lane of its rank
+  // rank among the kc candidates, then move each to the lane of its rank
   int rank = 0;
-  for (int q = 0; q < k; ++q) {
+  for (int q = 0; q < kc; ++q) {
     const uint32_t kq = static_cast<uint32_t>(__builtin_amdgcn_readlane(ck, q));
     const int eq = __builtin_amdgcn_readlane(ce, q);
     rank += (kq > static_cast<uint32_t>(ck) || (kq == static_cast<uint32_t>(ck) && eq < ce)) ? 1
                                                                                           : 0;
   }
-  const int dst = lane < k ? rank : kWave - 1;
+  const int dst = lane < kc ? rank : kWave - 1;
   const int sk = __builtin_amdgcn_ds_permute(dst * 4, ck);
   const int se = __builtin_amdgcn_ds_permute(dst * 4, ce);
+  if (sel_l) *sel_l = (lane < kc) ? key_logit(static_cast<uint32_t>(sk)) : -INFINITY;
   const float sel_v = (lane < k) ? key_logit(static_cast<uint32_t>(sk)) : -INFINITY;
-  sel_e = (lane < k) ? se : 0;
+  sel_e = (lane < kc) ? se : 0;
   const float first_v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
   // w_j = exp(l_j - l_max) / (sum over the picks when renormalised, else over
   // all E); p_j (WANT_P) = exp(l_j - l_max) / sum over all E
@@ -410,7 +415,8 @@ template <int PER, int NW, bool SINGLE, bool FIRST>
 __global__ __launch_bounds__(NW * 64) void select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, int has_shared, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ topk_p, int4* __restrict__ slots, int32_t* __restrict__ pair_rows,
+    float* __restrict__ topk_p, int32_t* __restrict__ cand_id, float* __restrict__ cand_l,
+    int4* __restrict__ slots, int32_t* __restrict__ pair_rows,
     int32_t* __restrict__ info, int32_t* __restrict__ user_idx, float* __restrict__ user_w) {
   constexpr bool kGroups = SINGLE && !FIRST;
   __shared__ int cnt[kGroups ? BDM_MAX_EXPERTS + 1 : 1];
@@ -427,8 +433,15 @@ __global__ __launch_bounds__(NW * 64) void select_kernel(
     load_logits<PER>(part + static_cast<size_t>(t) * E, static_cast<size_t>(T) * E, bias, E,
                      lane, v);
     int sel_e;
-    float sel_w, sel_p;
-    topk_pick<PER, FIRST>(v, E, k, renorm, lane, sel_e, sel_w, &sel_p);
+    float sel_w, sel_p, sel_l;
+    // the first pass of the coreset selector also ranks the next candidates:
+    // a token's re-route over the kept experts takes them in this order
+    const int kc = FIRST ? (E < kCoreCand ? E : kCoreCand) : k;
+    topk_pick<PER, FIRST>(v, E, k, renorm, lane, sel_e, sel_w, &sel_p, kc, &sel_l);
+    if (FIRST && lane < kCoreCand) {
+      cand_id[t * kCoreCand + lane] = lane < kc ? sel_e : -1;
+      cand_l[t * kCoreCand + lane] = lane < kc ? sel_l : -INFINITY;
+    }
     if (lane < k) {
       topk_idx[t * k + lane] = sel_e;
       topk_w[t * k + lane] = sel_w;
@@ -561,8 +574,9 @@ __device__ __forceinline__ void reroute_pick(const float (&v)[PER], int fe, cons
 // Block coreset expert selector, one workgroup per block of B <= 32 tokens
 // (page "Clover-35B-A3B: how a diffusion model gets to 680 tokens a second,
 // read from its files", section "The expert selection"):
-//   first pass (select_kernel FIRST): every token's top-k, weights and the
-//             picks' probabilities over all E;
+//   first pass (select_kernel FIRST): every token's top-k, weights, the
+//             picks' probabilities over all E, and its 32 best experts
+//             ranked (the re-route's candidates);
 //   mass_e  = sum over the block's tokens of the probabilities of the picks
 //             of e (fp32; four partial sums over token ranges, added in a
 //             fixed order);
@@ -572,26 +586,41 @@ __device__ __forceinline__ void reroute_pick(const float (&v)[PER], int fe, cons
 //   re-route: each token's top-min(k, |kept|) over the kept experts (the
 //             others at -inf), weights as in the plain routing; the rest of
 //             its k slots hold -1 and weight 0.
+// The workgroup's 16 waves share one CU, so the kernel is bound by its VALU
+// issue rate: the masses are a scatter of each token's picks (a token's
+// picks are distinct experts: one token per step, its picks in parallel,
+// tokens in order, the summation order of a per-expert loop over the
+// picks), ranks are counted over the touched experts only, and a token's
+// re-route takes the first min(k, |kept|) kept experts of its ranked
+// candidates -- the kept first-pass picks in their order, then the best
+// kept experts it did not pick, exactly what rounds of argmax over the kept
+// experts give.  A token whose candidates hold too few kept experts (or any
+// token when the weights are not renormalised, whose denominator needs the
+// whole row) loads its logit row and takes the argmax rounds.
 // Then the grouping: by the block's own workgroup when there is one block
 // (GROUP), else by group_kernel launched after this kernel.
 template <int PER, bool GROUP>
 __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
     int renorm, float top_p, int B, int has_shared, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, const float* __restrict__ topk_p, int4* __restrict__ slots,
-    int32_t* __restrict__ pair_rows, int32_t* __restrict__ info, int32_t* __restrict__ user_idx,
-    float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
+    float* __restrict__ topk_w, const float* __restrict__ topk_p,
+    const int32_t* __restrict__ cand_id, const float* __restrict__ cand_l,
+    int4* __restrict__ slots, int32_t* __restrict__ pair_rows, int32_t* __restrict__ info,
+    int32_t* __restrict__ user_idx, float* __restrict__ user_w, int32_t* __restrict__ n_kept) {
   constexpr int kParts = 4;                     // partial sums per expert mass
   __shared__ int cnt[BDM_MAX_EXPERTS + 1];
   __shared__ int eoff[BDM_MAX_EXPERTS + 1];
   __shared__ int fill[BDM_MAX_EXPERTS + 1];
-  __shared__ __align__(16) float mass[BDM_MAX_EXPERTS];
   __shared__ float mpart[kParts][BDM_MAX_EXPERTS];
   __shared__ float smass[BDM_MAX_EXPERTS];      // masses in mass order
   __shared__ int rank_of[BDM_MAX_EXPERTS];      // position in mass order, -1 untouched
-  __shared__ __align__(16) int sidx[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
-  __shared__ __align__(16) float sp[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
+  __shared__ int tlist[BDM_MAX_EXPERTS];        // touched experts (any order) and masses
+  __shared__ float tmass[BDM_MAX_EXPERTS];
+  __shared__ int sidx[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
+  __shared__ float sp[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
   __shared__ float sw[BDM_CORESET_MAX_BLOCK * BDM_MAX_TOPK];
+  __shared__ int scid[BDM_CORESET_MAX_BLOCK * kCoreCand];
+  __shared__ float scl[BDM_CORESET_MAX_BLOCK * kCoreCand];
   __shared__ int s_ntouch, s_nkeep;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -601,98 +630,89 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
   const int E16 = (E + 15) & ~15;
   const int nbk = nb * k;
   const int nbk16 = (nbk + 15) & ~15;
+  const unsigned long long below = (1ull << lane) - 1ull;
 
-  // this wave's tokens (w, w + 16): logit rows for the re-route; the block's
-  // first-pass picks (padded with id -1 to a multiple of 16), weights and
-  // probabilities
-  const int ta = wave, tb = wave + kCsWaves;
-  const size_t zs = static_cast<size_t>(T) * E;
-  float va[PER], vb[PER];
-  if (ta < nb) load_logits<PER>(part + static_cast<size_t>(t0 + ta) * E, zs, bias, E, lane, va);
-  if (tb < nb) load_logits<PER>(part + static_cast<size_t>(t0 + tb) * E, zs, bias, E, lane, vb);
+  // the block's first-pass picks (padded with id -1 to a multiple of 16),
+  // weights, probabilities and ranked candidates; zeroed partial masses
   for (int i = tid; i < nbk16; i += blockDim.x) {
     const bool in = i < nbk;
     sidx[i] = in ? topk_idx[t0 * k + i] : -1;
     sp[i] = in ? topk_p[t0 * k + i] : 0.0f;
     sw[i] = in ? topk_w[t0 * k + i] : 0.0f;
   }
-  for (int e = tid; e < E16; e += blockDim.x) mass[e] = 0.0f;
+  for (int i = tid; i < nb * kCoreCand; i += blockDim.x) {
+    scid[i] = cand_id[t0 * kCoreCand + i];
+    scl[i] = cand_l[t0 * kCoreCand + i];
+  }
+  for (int i = tid; i < kParts * BDM_MAX_EXPERTS; i += blockDim.x) mpart[0][i] = 0.0f;
   if (tid == 0) s_ntouch = 0;
   __syncthreads();
-  // mass: kParts threads per expert, each over a contiguous range of the
-  // picks (in token order), then the partial sums in part order
+  // mass: part pp holds the picks [pp chunk, (pp + 1) chunk) (in token
+  // order); wave pp adds them token by token, lane j taking a token's pick j
+  // (distinct experts), so every partial sum runs over its picks in order
   const int nparts = (static_cast<int>(blockDim.x) / E16 >= kParts) ? kParts : 1;
   const int chunk = ((nbk16 / 16 + nparts - 1) / nparts) * 16;
-  for (int w = tid; w < E * nparts; w += blockDim.x) {
-    const int e = w % E;
-    const int pp = w / E;
-    const int i1 = min(nbk16, (pp + 1) * chunk);
-    float m = 0.0f;
-    for (int i0 = pp * chunk; i0 < i1; i0 += 16) {
-      int4 id[4];
-      float4 pv[4];
+  if (wave < nparts && lane < k) {
+    const int i0 = wave * chunk;
+    const int i1 = min(nbk, min(nbk16, i0 + chunk));
+    // eight tokens' picks read first, then added in token order
+    for (int tb = i0 / k; tb * k < i1; tb += 8) {
+      int ee[8];
+      float pv[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        id[u] = *reinterpret_cast<const int4*>(sidx + i0 + 4 * u);
-        pv[u] = *reinterpret_cast<const float4*>(sp + i0 + 4 * u);
+      for (int u = 0; u < 8; ++u) {
+        const int i = (tb + u) * k + lane;
+        const bool in = i >= i0 && i < i1;
+        ee[u] = in ? sidx[i] : -1;
+        pv[u] = in ? sp[i] : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        m += (id[u].x == e) ? pv[u].x : 0.0f;
-        m += (id[u].y == e) ? pv[u].y : 0.0f;
-        m += (id[u].z == e) ? pv[u].z : 0.0f;
-        m += (id[u].w == e) ? pv[u].w : 0.0f;
-      }
+      for (int u = 0; u < 8; ++u)
+        if (ee[u] >= 0 && ee[u] < E) mpart[wave][ee[u]] += pv[u];
     }
-    mpart[pp][e] = m;
   }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     float m = mpart[0][e];
     for (int pp = 1; pp < nparts; ++pp) m += mpart[pp][e];
-    mass[e] = m;
     cnt[e] = 0;
-    if (m > 0.0f) atomicAdd(&s_ntouch, 1);
-  }
-  __syncthreads();
-  // rank in mass order (larger first, equal -> lower id): kParts threads
-  // per expert count over quarters of the experts; masses past E are 0
-  const int qchunk = ((E16 / 16 + nparts - 1) / nparts) * 16;
-  for (int w = tid; w < E * nparts; w += blockDim.x) {
-    const int e = w % E;
-    const int pp = w / E;
-    const float m = mass[e];
+    rank_of[e] = -1;
     if (m > 0.0f) {
-      int r = 0;
-      const int q1 = min(E16, (pp + 1) * qchunk);
-      for (int q0 = pp * qchunk; q0 < q1; q0 += 16) {
-        float4 mv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) mv[u] = *reinterpret_cast<const float4*>(mass + q0 + 4 * u);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = q0 + 4 * u;
-          r += (mv[u].x > m || (mv[u].x == m && q < e)) ? 1 : 0;
-          r += (mv[u].y > m || (mv[u].y == m && q + 1 < e)) ? 1 : 0;
-          r += (mv[u].z > m || (mv[u].z == m && q + 2 < e)) ? 1 : 0;
-          r += (mv[u].w > m || (mv[u].w == m && q + 3 < e)) ? 1 : 0;
-        }
-      }
-      atomicAdd(&cnt[e], r);                    // integer counts: any order
+      const int q = atomicAdd(&s_ntouch, 1);
+      tlist[q] = e;
+      tmass[q] = m;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    const float m = mass[e];
-    const int r = (m > 0.0f) ? cnt[e] : -1;
-    if (r >= 0) smass[r] = m;
+  // rank in mass order (larger first, equal -> lower id), counted over the
+  // touched experts, the list split among the threads
+  const int nt = s_ntouch;
+  const int spl = nt > 0 ? max(1, min(16, static_cast<int>(blockDim.x) / nt)) : 1;
+  const int qchunk = (nt + spl - 1) / spl;
+  for (int w = tid; w < nt * spl; w += blockDim.x) {
+    const int q = w % nt;
+    const int pp = w / nt;
+    const int e = tlist[q];
+    const float m = tmass[q];
+    int r = 0;
+    const int j1 = min(nt, (pp + 1) * qchunk);
+    for (int j = pp * qchunk; j < j1; ++j) {
+      const float mj = tmass[j];
+      r += (mj > m || (mj == m && tlist[j] < e)) ? 1 : 0;
+    }
+    atomicAdd(&cnt[e], r);                      // integer counts: any order
+  }
+  __syncthreads();
+  for (int q = tid; q < nt; q += blockDim.x) {
+    const int e = tlist[q];
+    const int r = cnt[e];
+    smass[r] = tmass[q];
     rank_of[e] = r;
   }
   __syncthreads();
   // cumulative mass in order (lane L sums a contiguous chunk, then a fixed
   // scan over lanes) and the cut
   if (wave == 0) {
-    const int nt = s_ntouch;
     const int per = (nt + kWave - 1) / kWave;
     const int i0 = lane * per;
     float loc = 0.0f;
@@ -707,14 +727,14 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     const float thr = top_p * total;
     const float up = __shfl_up(incl, 1, kWave);
     float cum = lane == 0 ? 0.0f : up;           // exclusive prefix of this chunk
-    int below = 0;
+    int below_n = 0;
     for (int i = i0; i < min(i0 + per, nt); ++i) {
       cum += smass[i];
-      below += (cum < thr) ? 1 : 0;
+      below_n += (cum < thr) ? 1 : 0;
     }
-    below = wave_sum_i(below);
+    below_n = wave_sum_i(below_n);
     if (lane == 0) {
-      const int keep = min(max(below + 1, 1), nt);
+      const int keep = min(max(below_n + 1, 1), nt);
       s_nkeep = keep;
       if (n_kept) n_kept[blockIdx.x] = keep;
     }
@@ -724,9 +744,10 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
   // first-pass picks are all kept keeps them and (renormalised) their
   // weights, which is what the re-route would compute
   const int keep = s_nkeep;
+  const int nc = E < kCoreCand ? E : kCoreCand;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int tl = r == 0 ? ta : tb;
+    const int tl = wave + r * kCsWaves;
     if (tl < nb) {
       const int fe = lane < k ? sidx[tl * k + lane] : -1;
       const bool fkeep = lane < k && fe >= 0 && rank_of[fe] >= 0 && rank_of[fe] < keep;
@@ -736,7 +757,31 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
         sel_e = fe;
         sel_w = lane < k ? sw[tl * k + lane] : 0.0f;
       } else {
-        reroute_pick<PER>(r == 0 ? va : vb, fe, rank_of, keep, E, k, renorm, lane, sel_e, sel_w);
+        const int kk = min(k, keep);
+        const int ce = lane < nc ? scid[tl * kCoreCand + lane] : -1;
+        const float cl = lane < nc ? scl[tl * kCoreCand + lane] : -INFINITY;
+        const bool ok = ce >= 0 && ce < E && cl != -INFINITY && rank_of[ce] >= 0 &&
+                        rank_of[ce] < keep;
+        const unsigned long long cm = __ballot(ok);
+        if (renorm && __popcll(cm) >= kk) {
+          // the first kk kept candidates, in rank order, to lanes 0 .. kk-1
+          const int pos = __popcll(cm & below);
+          const int dst = (ok && pos < kk) ? pos : kWave - 1;
+          const int pe = __builtin_amdgcn_ds_permute(dst * 4, ce);
+          const float pv =
+              __int_as_float(__builtin_amdgcn_ds_permute(dst * 4, __float_as_int(cl)));
+          const float sel_v = lane < kk ? pv : -INFINITY;
+          sel_e = lane < kk ? pe : -1;
+          const float first_v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
+          const float z = (lane < kk) ? expf(sel_v - first_v) : 0.0f;
+          const float den = wave_sum(z);
+          sel_w = (lane < kk) ? z / den : 0.0f;
+        } else {
+          float v[PER];
+          load_logits<PER>(part + static_cast<size_t>(t0 + tl) * E, static_cast<size_t>(T) * E,
+                           bias, E, lane, v);
+          reroute_pick<PER>(v, fe, rank_of, keep, E, k, renorm, lane, sel_e, sel_w);
+        }
       }
       if (lane < k) {
         const int t = t0 + tl;
@@ -773,28 +818,31 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
   if (core) {                                                                                  \
     select_kernel<P, kSelWaves, false, true><<<nsel, kSelWaves * 64, 0, s>>>(                  \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+        meta.topk_p, meta.cand_id, meta.cand_l, meta.slots, meta.pair_rows, meta.info,         \
+        user_idx, user_w);                                                                     \
     if (ncs > 1) {                                                                             \
       coreset_kernel<P, false><<<ncs, kCsWaves * 64, 0, s>>>(                                  \
           meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,         \
-          meta.topk_w, meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w,   \
-          n_kept);                                                                             \
+          meta.topk_w, meta.topk_p, meta.cand_id, meta.cand_l, meta.slots, meta.pair_rows,     \
+          meta.info, user_idx, user_w, n_kept);                                                \
       group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,       \
                                          meta.pair_rows, meta.info);                           \
     } else {                                                                                   \
       coreset_kernel<P, true><<<1, kCsWaves * 64, 0, s>>>(                                     \
           meta.logits, bias, T, E, k, renorm, top_p, block, has_shared, meta.topk_idx,         \
-          meta.topk_w, meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w,   \
-          n_kept);                                                                             \
+          meta.topk_w, meta.topk_p, meta.cand_id, meta.cand_l, meta.slots, meta.pair_rows,     \
+          meta.info, user_idx, user_w, n_kept);                                                \
     }                                                                                          \
   } else if (T <= kSelOneMaxT) {                                                               \
     select_kernel<P, kSelOneWaves, true, false><<<1, kSelOneWaves * 64, 0, s>>>(               \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+        meta.topk_p, meta.cand_id, meta.cand_l, meta.slots, meta.pair_rows, meta.info,         \
+        user_idx, user_w);                                                                     \
   } else {                                                                                     \
     select_kernel<P, kSelWaves, false, false><<<nsel, kSelWaves * 64, 0, s>>>(                 \
         meta.logits, bias, T, E, k, renorm, has_shared, meta.topk_idx, meta.topk_w,            \
-        meta.topk_p, meta.slots, meta.pair_rows, meta.info, user_idx, user_w);                 \
+        meta.topk_p, meta.cand_id, meta.cand_l, meta.slots, meta.pair_rows, meta.info,         \
+        user_idx, user_w);                                                                     \
     group_kernel<P><<<1, 1024, 0, s>>>(meta.topk_idx, T, E, k, has_shared, meta.slots,         \
                                        meta.pair_rows, meta.info);                             \
   }
