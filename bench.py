@@ -44,7 +44,7 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-PMC_SUMMARY = os.path.join(HERE, "profiles", "head_coop_kernel_clover_head.traffic.md")
+PMC_SUMMARY = os.path.join(HERE, "profiles", "all_kernels_bench_workloads.traffic.md")
 EXPERT_BYTES = 3 * 2048 * 512 * 2        # gate + up + down, bf16
 HEAD_BYTES = 248320 * 2048 * 2
 
@@ -459,6 +459,7 @@ def main():
         "moe_layer": {"us": round(moe_loop_us, 2), "us_in_step": round(moe_us, 2),
                       "block_tokens_per_s": round(T / (moe_loop_us * 1e-6), 1),
                       "unique_experts": round(u_mean, 2), "bytes": int(moe_bytes),
+                      "traffic": moe_layer_traffic(),
                       "GB_s": round(moe_gbs, 1), "frac_of_peak": round(moe_gbs / PEAK_HBM_GBS, 4),
                       "frac_of_measured_stream_read": round(moe_gbs / stream_gbs, 4)},
         "moe_layer_coreset_top_p_0.9": {
@@ -706,24 +707,40 @@ def stream_read_gbs(torch, dev, reps, nbytes=None):
     return best
 
 
-def head_traffic():
-    """HBM bytes per head GEMM launch from the committed counter summary
-    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing or
-    was taken on other kernel sources."""
+def _summary_records():
     try:
         with open(PMC_SUMMARY) as fh:
             txt = fh.read()
     except OSError:
-        return None
+        return {}
     vals = {}
     for ln in txt.splitlines():
         if ln.startswith("<!--") and "=" in ln:
             k, v = ln.strip("<!-> \n").split("=", 1)
             vals[k.strip()] = v.strip()
+    return vals
+
+
+def head_traffic():
+    """HBM bytes per head GEMM launch from the committed counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when the summary is missing or
+    was taken on other kernel sources."""
+    vals = _summary_records()
     from block_diffusion_moe_amd.traffic import kernel_source_digest
     if vals.get("source_sha256") != kernel_source_digest() or "traffic_bytes" not in vals:
         return None
     return int(float(vals["traffic_bytes"]))
+
+
+def moe_layer_traffic():
+    """HBM bytes of one one-block MoE layer (all its launches) from the same
+    summary, or None when missing or taken on other kernel sources."""
+    vals = _summary_records()
+    from block_diffusion_moe_amd.traffic import MOE_SOURCES, kernel_source_digest
+    if (vals.get("moe_source_sha256") != kernel_source_digest(MOE_SOURCES)
+            or "moe_layer_traffic_bytes" not in vals):
+        return None
+    return int(float(vals["moe_layer_traffic_bytes"]))
 
 
 def cpu_baseline(torch, dev, blocks, skew_host, stack_layers, runs=5):

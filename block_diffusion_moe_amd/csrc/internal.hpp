@@ -25,7 +25,10 @@ constexpr int kCoreCand = 32;     // ranked first-pass candidates per token (cor
 // floor(T*k / kSlotChunk) extra chunks over all routed experts (none unless
 // T > kSlotChunk: an expert holds a token at most once), plus the shared
 // expert's ceil(T / kSlotChunk).
-constexpr int kSlotChunk = 64;
+#ifndef BDM_SLOT_CHUNK
+#define BDM_SLOT_CHUNK 64
+#endif
+constexpr int kSlotChunk = BDM_SLOT_CHUNK;
 __host__ __device__ inline int moe_max_slots(int T, int E, int k, int has_shared) {
   const int routed = T * k < E ? T * k : E;
   const int extra = T > kSlotChunk ? (T * k) / kSlotChunk : 0;

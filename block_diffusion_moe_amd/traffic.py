@@ -50,6 +50,15 @@ COPY_BYTES = 1 << 30
 # many-row one head_coop_kernel<KSW, MT, false, true>)
 HEAD_KERNELS = ("head_coop_kernel", "head_tile_kernel")
 HEAD_SOURCES = ("head.hip", "device.hpp", "internal.hpp")
+MOE_SOURCES = ("router.hip", "experts.hip", "device.hpp", "internal.hpp")
+# the launches of the one-block MoE layer (32 tokens, 256 experts) and their
+# grids in threads: router 16 x 1 x 4 workgroups of 256, top-k 8 of 256,
+# grouping 1 of 1,024, gate/up and down (one-block kernels, used below 256
+# tokens only), combine 32 of 256
+MOE_LAYER_GRIDS = {"bdm::router_kernel<1>": 16384,
+                   "bdm::select_kernel<4, 4, false, false>": 2048,
+                   "bdm::group_kernel<4>": 1024, "bdm::gateup_kernel<8, false>": None,
+                   "bdm::down_kernel<16, false>": None, "bdm::combine_kernel": 8192}
 
 
 def kernel_source_digest(files=HEAD_SOURCES) -> str:
@@ -94,15 +103,18 @@ def copy_kernel():
           flush=True)
 
 
-def read_counters(d: str):
-    """{(kernel short name, counter): [value per dispatch]} from one pass."""
+def read_counters(d: str, by_grid: bool = False):
+    """{(kernel short name, counter): [value per dispatch]} from one pass; with
+    `by_grid` the key is (name, grid size, counter), which tells apart calls
+    of one kernel at different sizes (e.g. 256 against 2,048 tokens)."""
     agg = collections.defaultdict(list)
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
                 name = name.split("(")[0].replace("void ", "").strip()
-                agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
+                key = (name, int(r.get("Grid_Size") or 0)) if by_grid else name
+                agg[(key, r["Counter_Name"])].append(float(r["Counter_Value"]))
     return agg
 
 
@@ -115,30 +127,41 @@ def _copy_factor(agg, counter: str, kernel: str = "stream_copy_kernel") -> float
 
 
 def summarize(a):
-    fetch, write = read_counters(a.fetch), read_counters(a.write)
+    fetch, write = read_counters(a.fetch, True), read_counters(a.write, True)
     cal_f, cal_w = read_counters(a.cal_fetch), read_counters(a.cal_write)
     f_fac = _copy_factor(cal_f, "FETCH_SIZE")
     w_fac = _copy_factor(cal_w, "WRITE_SIZE")
     f_ew = _copy_factor(cal_f, "FETCH_SIZE", "neg_kernel")
     w_ew = _copy_factor(cal_w, "WRITE_SIZE", "neg_kernel")
-    names = sorted({n for n, _ in fetch} | {n for n, _ in write})
+    keys = sorted({k for k, _ in fetch} | {k for k, _ in write})
     rows = []
     head_bytes = None
-    for n in names:
-        fv = fetch.get((n, "FETCH_SIZE"), [])
-        wv = write.get((n, "WRITE_SIZE"), [])
+    for key in keys:
+        n, grid = key
+        fv = fetch.get((key, "FETCH_SIZE"), [])
+        wv = write.get((key, "WRITE_SIZE"), [])
         if not fv or not wv or "bdm" not in n:
             continue
         fb = f_fac * 1024.0 * sum(fv) / len(fv)
         wb = w_fac * 1024.0 * sum(wv) / len(wv)
-        rows.append((n, len(fv), fb, wb))
+        rows.append((n, grid, len(fv), fb, wb))
         short = n.split("::")[-1]
         other_variant = short.startswith("head_coop_kernel<") and "true" in short
         if short.startswith(HEAD_KERNELS) and not other_variant:
             head_bytes = fb + wb if head_bytes is None else max(head_bytes, fb + wb)
+    # the one-block MoE layer: its kernels at their one-block grids
+    layer = {}
+    for n, grid, c, fb, wb in rows:
+        want = MOE_LAYER_GRIDS.get(n, -1)
+        if want == -1 or (want is not None and grid != want):
+            continue
+        layer[n] = max(layer.get(n, 0.0), fb + wb)
     out = [f"<!-- source_sha256 = {kernel_source_digest()} -->"]
     if head_bytes is not None:
         out.append(f"<!-- traffic_bytes = {head_bytes:.0f} -->")
+    if len(layer) == len(MOE_LAYER_GRIDS):
+        out.append(f"<!-- moe_source_sha256 = {kernel_source_digest(MOE_SOURCES)} -->")
+        out.append(f"<!-- moe_layer_traffic_bytes = {sum(layer.values()):.0f} -->")
     out += ["", "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", ""]
     if a.command:
         out += ["Made by:", "", "```", a.command, "```", ""]
@@ -146,10 +169,13 @@ def summarize(a):
             f"loads as in the weight streams): FETCH_SIZE x {f_fac:.4f}, WRITE_SIZE x "
             f"{w_fac:.4f}.  For comparison, a torch elementwise copy (ordinary loads) reads "
             f"FETCH_SIZE x {f_ew:.4f}, WRITE_SIZE x {w_ew:.4f}.", "",
-            "| kernel | dispatches | read B / launch | written B / launch | total B / launch |",
-            "|---|---:|---:|---:|---:|"]
-    for n, c, fb, wb in rows:
-        out.append(f"| `{n}` | {c} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
+            "One row per kernel and launch grid (threads): calls of one kernel at "
+            "different sizes are told apart by their grids.", "",
+            "| kernel | grid | dispatches | read B / launch | written B / launch | "
+            "total B / launch |",
+            "|---|---:|---:|---:|---:|---:|"]
+    for n, grid, c, fb, wb in rows:
+        out.append(f"| `{n}` | {grid} | {c} | {fb:.4g} | {wb:.4g} | {fb + wb:.4g} |")
     out.append("")
     with open(a.out, "w") as fh:
         fh.write("\n".join(out))

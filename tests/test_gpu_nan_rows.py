@@ -139,3 +139,35 @@ def test_verify_nan_row_rejected(bdm):
         assert int(na.item()) <= 3
         r = int(na.item())
         assert tok[:r].tolist() == cand[:r].tolist() and int(tok[r]) == int(am[r])
+
+
+@pytest.mark.parametrize("T", [8, 32, 256])
+def test_moe_layer_nan_rows_stay_in_bounds(bdm, T):
+    """NaN rows in the MoE layer's input (the header: undefined values, never
+    an out-of-bounds access): their expert ids stay in [0, E) and every other
+    row is bit for bit what the call without the NaN rows gives (tokens are
+    independent through the layer); few-token kernels at 8 and 32 tokens,
+    many-token kernels at 256."""
+    say(f"case MoE layer with NaN rows T={T}")
+    s = synth.MoEShape(T=T, H=2048, E=256, I=512, k=8)
+    inp = synth.moe_inputs(s, seed=21, block_seed=T, device=DEV, with_residual=True)
+    outs = []
+    for poison in (False, True):
+        x = inp.x.clone()
+        if poison:
+            x[[1, T // 2]] = float("nan")
+        y = torch.empty_like(x)
+        idx = torch.full((T, s.k), -7, dtype=torch.int32, device=DEV)
+        w = torch.empty((T, s.k), dtype=torch.float32, device=DEV)
+        bdm.bdm_moe_block_forward(x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+                                  ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down,
+                                  residual=inp.residual, y=y, topk_idx=idx, topk_w=w)
+        torch.cuda.synchronize()
+        outs.append((y, idx, w))
+    (y0, i0, w0), (y1, i1, w1) = outs
+    bad = torch.zeros(T, dtype=torch.bool, device=DEV)
+    bad[[1, T // 2]] = True
+    assert int(i1.min()) >= 0 and int(i1.max()) < s.E
+    assert torch.equal(y1[~bad].view(torch.int16), y0[~bad].view(torch.int16))
+    assert torch.equal(i1[~bad], i0[~bad])
+    assert torch.equal(w1[~bad].view(torch.int32), w0[~bad].view(torch.int32))
