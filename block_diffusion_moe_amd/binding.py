@@ -31,14 +31,14 @@ _SIGS = {
     "bdm_moe_workspace_bytes": (_c_int, [_c_int] * 6 + [ctypes.POINTER(_c_size)]),
     "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                        _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
-                                       _vp, _vp, _vp, _vp, _c_size, _vp]),
+                                       _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "bdm_moe_block_forward_noalloc": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
                                                _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
                                                _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bdm_moe_block_forward_coreset": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int,
                                                _c_int, _c_float, _c_int, _vp, _vp, _vp, _c_int,
                                                _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
-                                               _vp, _vp, _c_size, _vp]),
+                                               _vp, _vp, _vp, _c_size, _vp]),
     "bdm_head_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
     "bdm_denoise_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              ctypes.POINTER(_c_size)]),
@@ -260,11 +260,13 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
                           ws_gate=None, ws_up=None, ws_down=None, residual=None, y=None,
                           topk_idx=None, topk_w=None, renorm: bool = True, ws=None, stream=None,
                           coreset_top_p=None, coreset_block: int = 32, n_kept=None,
-                          y_norm=None):
+                          y_norm=None, x_norm=None):
     """y = MoE layer over the block x (see include/bdmoe.h).  ``y`` may be
     ``residual`` (in-place residual add); a new tensor is made when None.
     Expert weights may be row-major tensors or all `Packed`.  ``y_norm``
-    (optional) receives RMSNorm(y), the next layer's input.  With
+    (optional) receives RMSNorm(y), the next layer's input.  ``x_norm``
+    (optional): x is un-normalised; the layer takes RMSNorm(x) itself, writes
+    it there and computes y = residual + MoE(RMSNorm(x)).  With
     ``coreset_top_p`` the block coreset selector runs first
     (bdm_moe_block_forward_coreset; ``n_kept`` receives |kept| per block)."""
     T, H = x.shape
@@ -284,6 +286,7 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
     _check(residual, "residual", torch.bfloat16, (T, H), dev)
     _check(y, "y", torch.bfloat16, (T, H), dev)
     _check(y_norm, "y_norm", torch.bfloat16, (T, H), dev)
+    _check(x_norm, "x_norm", torch.bfloat16, (T, H), dev)
     _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
     _check(topk_w, "topk_w", torch.float32, (T, k), dev)
     has_shared = ws_gate is not None
@@ -295,8 +298,8 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
         st = load().bdm_moe_block_forward(
             _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm),
             _ptr(w_gate), _ptr(w_up), _ptr(w_down), I, _ptr(ws_gate), _ptr(ws_up),
-            _ptr(ws_down), layout, _ptr(residual), _ptr(y), _ptr(y_norm), _ptr(topk_idx),
-            _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(ws_down), layout, _ptr(residual), _ptr(y), _ptr(y_norm), _ptr(x_norm),
+            _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream))
         _raise("bdm_moe_block_forward", st)
         return y
     nb = (T + coreset_block - 1) // max(1, coreset_block)
@@ -305,8 +308,8 @@ def bdm_moe_block_forward(x, w_router, w_gate, w_up, w_down, k: int, *, router_b
         _ptr(x), T, H, _ptr(w_router), _ptr(router_bias), E, int(k), int(renorm),
         float(coreset_top_p), int(coreset_block), _ptr(w_gate), _ptr(w_up), _ptr(w_down), I,
         _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), layout, _ptr(residual), _ptr(y),
-        _ptr(y_norm), _ptr(topk_idx), _ptr(topk_w), _ptr(n_kept), _ptr(ws), ws.numel(),
-        _stream(stream))
+        _ptr(y_norm), _ptr(x_norm), _ptr(topk_idx), _ptr(topk_w), _ptr(n_kept), _ptr(ws),
+        ws.numel(), _stream(stream))
     _raise("bdm_moe_block_forward_coreset", st)
     return y
 

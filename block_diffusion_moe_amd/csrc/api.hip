@@ -179,7 +179,7 @@ int last_hip_status() {
 
 extern "C" {
 
-int bdm_version(void) { return 100; }
+int bdm_version(void) { return 101; }
 
 const char* bdm_status_string(int status) {
   switch (status) {
@@ -206,9 +206,9 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
                 int E, int k, int renorm, float top_p, int block, const uint16_t* w_gate,
                 const uint16_t* w_up, const uint16_t* w_down, int I, const uint16_t* ws_gate,
                 const uint16_t* ws_up, const uint16_t* ws_down, int weight_layout,
-                const uint16_t* residual, uint16_t* y, uint16_t* y_norm, int32_t* topk_idx,
-                float* topk_w, int32_t* n_kept, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                const uint16_t* residual, uint16_t* y, uint16_t* y_norm, uint16_t* x_norm,
+                int32_t* topk_idx, float* topk_w, int32_t* n_kept, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
     return BDM_ERR_INVALID_ARG;
   const int nshared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr);
@@ -229,10 +229,18 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
       (has_shared && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(ws_down))) ||
       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return BDM_ERR_INVALID_ARG;
-  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return BDM_ERR_INVALID_ARG;
+  // x may be y only when the layer normalises x itself (the router reads x
+  // before the combine writes y)
+  if (static_cast<const void*>(x) == static_cast<const void*>(y) && !x_norm)
+    return BDM_ERR_INVALID_ARG;
   if (y_norm && (static_cast<const void*>(y_norm) == static_cast<const void*>(y) ||
                  static_cast<const void*>(y_norm) == static_cast<const void*>(x) ||
                  static_cast<const void*>(y_norm) == static_cast<const void*>(residual)))
+    return BDM_ERR_INVALID_ARG;
+  if (x_norm && (!aligned16(x_norm) || static_cast<void*>(x_norm) == static_cast<const void*>(x) ||
+                 static_cast<void*>(x_norm) == static_cast<void*>(y) ||
+                 static_cast<void*>(x_norm) == static_cast<void*>(y_norm) ||
+                 static_cast<const void*>(x_norm) == static_cast<const void*>(residual)))
     return BDM_ERR_INVALID_ARG;
   const size_t need = moe_layout(T, H, I, E, k, has_shared, nullptr, nullptr);
   if (workspace_bytes < need) return BDM_ERR_WORKSPACE_TOO_SMALL;
@@ -244,10 +252,11 @@ int moe_forward(const uint16_t* x, int T, int H, const float* w_router, const fl
   moe_layout(T, H, I, E, k, has_shared, static_cast<char*>(workspace), &meta);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  // with x_norm the router normalises x and the experts read the result
   bdm::launch_router(x, T, H, w_router, router_bias, E, k, renorm, has_shared, top_p, block,
-                     meta, topk_idx, topk_w, n_kept, s);
-  bdm::launch_experts(x, T, H, I, E, k, has_shared, w_gate, w_up, w_down, ws_gate, ws_up,
-                      ws_down, residual, y, y_norm, meta, weight_layout, s);
+                     meta, topk_idx, topk_w, n_kept, x_norm, s);
+  bdm::launch_experts(x_norm ? x_norm : x, T, H, I, E, k, has_shared, w_gate, w_up, w_down,
+                      ws_gate, ws_up, ws_down, residual, y, y_norm, meta, weight_layout, s);
   return last_hip_status();
 }
 
@@ -258,11 +267,11 @@ int bdm_moe_block_forward(const uint16_t* x, int T, int H, const float* w_router
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int I, const uint16_t* ws_gate, const uint16_t* ws_up,
                           const uint16_t* ws_down, int weight_layout, const uint16_t* residual,
-                          uint16_t* y, uint16_t* y_norm, int32_t* topk_idx, float* topk_w,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          uint16_t* y, uint16_t* y_norm, uint16_t* x_norm, int32_t* topk_idx,
+                          float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
-                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, topk_idx,
-                     topk_w, nullptr, workspace, workspace_bytes, stream);
+                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, x_norm,
+                     topk_idx, topk_w, nullptr, workspace, workspace_bytes, stream);
 }
 
 int bdm_moe_block_forward_noalloc(const uint16_t* x, int T, int H, const float* w_router,
@@ -286,8 +295,8 @@ int bdm_moe_block_forward_noalloc(const uint16_t* x, int T, int H, const float* 
   const int ds = device_setup(&cus, &sp);
   if (ds != BDM_OK) return ds;
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, 0.0f, 0, w_gate, w_up, w_down,
-                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, topk_idx,
-                     topk_w, nullptr, sp, BDM_STATIC_SCRATCH_BYTES, stream);
+                     I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm, nullptr,
+                     topk_idx, topk_w, nullptr, sp, BDM_STATIC_SCRATCH_BYTES, stream);
 }
 
 int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* w_router,
@@ -297,13 +306,14 @@ int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H, const float* 
                                   const uint16_t* ws_gate, const uint16_t* ws_up,
                                   const uint16_t* ws_down, int weight_layout,
                                   const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
-                                  int32_t* topk_idx, float* topk_w, int32_t* n_kept,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+                                  uint16_t* x_norm, int32_t* topk_idx, float* topk_w,
+                                  int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return BDM_ERR_INVALID_ARG;
   if (block_tokens < 1 || block_tokens > BDM_CORESET_MAX_BLOCK) return BDM_ERR_INVALID_ARG;
   return moe_forward(x, T, H, w_router, router_bias, E, k, renorm, top_p, block_tokens, w_gate,
                      w_up, w_down, I, ws_gate, ws_up, ws_down, weight_layout, residual, y, y_norm,
-                     topk_idx, topk_w, n_kept, workspace, workspace_bytes, stream);
+                     x_norm, topk_idx, topk_w, n_kept, workspace, workspace_bytes, stream);
 }
 
 int bdm_head_workspace_bytes(int T, int H, int V, size_t* bytes) {
@@ -539,14 +549,13 @@ int bdm_denoise_block(int32_t* tokens, int T, const uint16_t* w_embed, int V, in
   int steps = 0;
   *steps_taken = 0;
   while (steps < max_steps) {
-    bdm::launch_embed(tokens, T, w_embed, V, H, x, s);
-    bdm::launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
+    bdm::launch_embed(tokens, T, w_embed, V, H, x, xn, s);     // x and RMSNorm(x)
     // each layer's combine also writes RMSNorm of its output: the next
     // layer's input, after the last layer the final norm
     for (int l = 0; l < L; ++l) {
       const bdm_moe_layer& w = layers[l];
       bdm::launch_router(xn, T, H, w.w_router, w.router_bias, E, k, renorm, has_shared,
-                         coreset_top_p, cs_block, meta, nullptr, nullptr, nullptr, s);
+                         coreset_top_p, cs_block, meta, nullptr, nullptr, nullptr, nullptr, s);
       bdm::launch_experts(xn, T, H, I, E, k, has_shared, w.w_gate, w.w_up, w.w_down, w.ws_gate,
                           w.ws_up, w.ws_down, x, x, xn, meta, weight_layout, s);
     }

@@ -51,11 +51,13 @@ struct MoeMeta {
 };
 
 // top_p > 0: block coreset selector over blocks of `block` tokens (n_kept
-// nullable, one count per block); top_p <= 0: plain top-k routing
+// nullable, one count per block); top_p <= 0: plain top-k routing.  xn
+// non-null: x is un-normalised, the router routes on RMSNorm(x) (eps 1e-6,
+// unit gamma) and writes it to xn.
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    int k, int renorm, int has_shared, float top_p, int block,
                    const MoeMeta& meta, int32_t* user_idx, float* user_w, int32_t* n_kept,
-                   hipStream_t s);
+                   uint16_t* xn, hipStream_t s);
 
 void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int has_shared,
                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
@@ -92,9 +94,10 @@ void launch_unmask(const float* pm, const float* ps, const int32_t* pa, int T, i
                    int32_t* tokens, int32_t* argmax, float* conf, int32_t* n_committed,
                    int32_t* n_left, hipStream_t s);
 
-// x[t] = w_embed[tokens[t]] (ids clamped to [0, V)), bf16 rows of H
+// x[t] = w_embed[tokens[t]] (ids clamped to [0, V)), bf16 rows of H, and
+// xn = RMSNorm(x) (eps 1e-6, unit gamma; bit for bit the RMSNorm kernel)
 void launch_embed(const int32_t* tokens, int T, const uint16_t* w_embed, int V, int H,
-                  uint16_t* x, hipStream_t s);
+                  uint16_t* x, uint16_t* xn, hipStream_t s);
 
 // the verify epilogue: statistics with the entropy term and the candidates'
 // logits (H % 256 == 0), then the merge and the accept rule

@@ -48,16 +48,76 @@ constexpr int kRtMaxKs = 4;     // k-steps per wave: H <= kRouterParts * 4 * 4 *
 // step.
 // NTT token tiles of 32 per workgroup share one load and split of the
 // router weights (NTT > 1 for many-block calls).
-template <int NTT>
+// NORM (NTT = 1): x is the layer's un-normalised input.  The workgroup first
+// takes the RMSNorm scale of each of its 32 rows with the arithmetic of the
+// RMSNorm kernel (its 256 threads hold a row's 8-element chunks in the same
+// order: per thread fmaf over 8 values, DPP within the wave, then the 4
+// waves pairwise; eps 1e-6), routes on bf16(x * scale), and the workgroups of
+// expert tile 0 write those rows, bit for bit what the RMSNorm kernel
+// writes, to xn (the experts' input).
+template <int NTT, bool NORM = false>
 __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* __restrict__ x,
                                                               int T, int H,
                                                               const float* __restrict__ wr, int E,
-                                                              float* __restrict__ part) {
+                                                              float* __restrict__ part,
+                                                              uint16_t* __restrict__ xn) {
+  static_assert(!NORM || NTT == 1, "the fused RMSNorm covers one token tile");
+  static_assert(kRtWaves * 64 == 256, "the RMSNorm chunk map needs 256 threads");
   __shared__ f32x4 red[2][kRtWaves][2][kWave];
+  __shared__ float rpart[NORM ? 32 : 1][kRtWaves];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
+  // NORM: the scales of this lane's rows t0 + c and t0 + 16 + c
+  float rsc0 = 1.0f, rsc1 = 1.0f;
+  if constexpr (NORM) {
+    const int tt0 = blockIdx.y * 32;
+    const int i0 = threadIdx.x * 8;
+    const bool on = i0 < H;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {                  // eight rows at a time, loads first
+      u32x4 raw[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int row = tt0 + 8 * b + r;
+        const bool ok = on && row < T;
+        const u32x4 v = ld16(x + static_cast<size_t>(ok ? row : 0) * H + (on ? i0 : 0));
+        raw[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = __uint_as_float(raw[r][j] << 16);
+          const float hi = __uint_as_float(raw[r][j] & 0xffff0000u);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) rpart[8 * b + r][wave] = ss;
+      }
+    }
+    __syncthreads();
+    auto scale = [&](int r) {
+      const float tot = (rpart[r][0] + rpart[r][1]) + (rpart[r][2] + rpart[r][3]);
+      return 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+    };
+    rsc0 = scale(c);
+    rsc1 = scale(16 + c);
+  }
+  // 16 bytes of a row times its scale, rounded as the RMSNorm kernel rounds
+  auto norm16 = [](u32x4 v, float r) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = __uint_as_float(v[j] << 16) * r;
+      const float b = __uint_as_float(v[j] & 0xffff0000u) * r;
+      o[j] = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    }
+    return o;
+  };
   const int e0 = blockIdx.x * 16;
   const int z = blockIdx.z;
   const int KS = H / 32;
@@ -78,6 +138,22 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
       const u32x4 v0 = ld16(x0 + s * 32), v1 = ld16(x1 + s * 32);
       a0[q] = ok0 ? v0 : u32x4{0u, 0u, 0u, 0u};
       a1[q] = ok1 ? v1 : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int q = 0; q < kRtMaxKs; ++q) {
+        a0[q] = norm16(a0[q], rsc0);
+        a1[q] = norm16(a1[q], rsc1);
+        // expert tile 0 writes the normalised rows (each (row, k-step) once)
+        if (blockIdx.x == 0 && s0 + q < s1) {
+          const int s = s0 + q;
+          if (ok0)
+            *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + c) * H + s * 32 + g * 8) = a0[q];
+          if (ok1)
+            *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + 16 + c) * H + s * 32 + g * 8) =
+                a1[q];
+        }
+      }
     }
   };
 
@@ -802,14 +878,23 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
 void launch_router(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    int k, int renorm, int has_shared, float top_p, int block,
                    const MoeMeta& meta, int32_t* user_idx, float* user_w, int32_t* n_kept,
-                   hipStream_t s) {
+                   uint16_t* xn, hipStream_t s) {
   if (T >= kRtWideMinT) {
+    // many tiles per workgroup: a separate RMSNorm when asked for
+    if (xn) {
+      launch_rmsnorm(x, nullptr, 1e-6f, T, H, xn, s);
+      x = xn;
+    }
     const dim3 grid((E + 15) / 16, (T + 32 * kRtWideTiles - 1) / (32 * kRtWideTiles),
                     kRouterParts);
-    router_kernel<kRtWideTiles><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits);
+    router_kernel<kRtWideTiles><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits,
+                                                               nullptr);
   } else {
     const dim3 grid((E + 15) / 16, (T + 31) / 32, kRouterParts);
-    router_kernel<1><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits);
+    if (xn)
+      router_kernel<1, true><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, xn);
+    else
+      router_kernel<1><<<grid, kRtWaves * 64, 0, s>>>(x, T, H, wr, E, meta.logits, nullptr);
   }
   const int nsel = (T + kSelWaves - 1) / kSelWaves;
   const bool core = top_p > 0.0f;

@@ -150,6 +150,13 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *                unit gamma; bit for bit what bdm_rmsnorm gives on y), the
  *                next layer's input in a pre-norm stack; must not alias x, y
  *                or residual
+ *   x_norm       [T][H] bf16 or NULL.  When given, x is the layer's
+ *                un-normalised input: the layer itself takes RMSNorm(x)
+ *                (eps 1e-6, unit gamma; bit for bit what bdm_rmsnorm gives),
+ *                writes it here and routes and runs the experts on it, i.e.
+ *                y = residual + MoE(RMSNorm(x)) without a separate RMSNorm
+ *                call; x may then be y (and residual).  Must not alias x, y,
+ *                y_norm or residual.
  *   topk_idx     [T][k] int32 or NULL   receives S_t (decreasing weight)
  *   topk_w       [T][k] fp32 or NULL    receives w_t
  *   workspace, workspace_bytes: see bdm_moe_workspace_bytes
@@ -157,6 +164,7 @@ BDM_API int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_s
  *   Pointers 16-byte aligned (workspace 256-byte aligned).  NaN inputs give
  *   undefined values, never an out-of-bounds access.
  * No other aliasing is allowed.
+ * (The argument list grew x_norm in library version 101.)
  *
  * Several blocks in one call (multi-block batching): stack the blocks' rows
  * in x (T = 32 x blocks, up to 64 blocks).  Tokens never interact, so each
@@ -172,7 +180,7 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
                           const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                           int weight_layout,
                           const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
-                          int32_t* topk_idx, float* topk_w,
+                          uint16_t* x_norm, int32_t* topk_idx, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -180,13 +188,14 @@ BDM_API int bdm_moe_block_forward(const uint16_t* x, int T, int H,
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation).
  *
- * The same computation, kernels and bits as bdm_moe_block_forward; the
+ * The same computation, kernels and bits as bdm_moe_block_forward with
+ * x_norm = NULL (x is the normalised input); the
  * workspace is instead a static device buffer of BDM_STATIC_SCRATCH_BYTES
  * inside the library, one per device, held until the process ends (its
  * address is looked up once per device at the library's first call on that
  * device).  The call allocates nothing (no hipMalloc, hipFree or allocating
  * library routine).  Arguments as in bdm_moe_block_forward, without
- * workspace and workspace_bytes.
+ * x_norm, workspace and workspace_bytes.
  * Limits: sizes whose bdm_moe_workspace_bytes exceed BDM_STATIC_SCRATCH_BYTES
  * (e.g. T = 256 fits at the Clover shape, T = 2048 does not) return
  * BDM_ERR_WORKSPACE_TOO_SMALL before any device call.
@@ -249,7 +258,7 @@ BDM_API int bdm_moe_block_forward_coreset(const uint16_t* x, int T, int H,
                           const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                           int weight_layout,
                           const uint16_t* residual, uint16_t* y, uint16_t* y_norm,
-                          int32_t* topk_idx, float* topk_w, int32_t* n_kept,
+                          uint16_t* x_norm, int32_t* topk_idx, float* topk_w, int32_t* n_kept,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*

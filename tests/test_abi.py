@@ -102,8 +102,8 @@ def test_moe_validation_rejects_before_launch(lib):
         return lib.bdm_moe_block_forward(a["x"], a["T"], a["H"], a["wr"], a["bias"], a["E"],
                                          a["k"], a["renorm"], a["wg"], a["wu"], a["wd"], a["I"],
                                          a["sg"], a["su"], a["sd"], a["lay"], a["res"], a["y"],
-                                         a.get("yn"), a["idx"], a["w"], a["ws"], a["wsb"],
-                                         a["stream"])
+                                         a.get("yn"), a.get("xn"), a["idx"], a["w"], a["ws"],
+                                         a["wsb"], a["stream"])
 
     assert call(x=None) == -1
     assert call(y=None) == -1
@@ -133,6 +133,13 @@ def test_moe_validation_rejects_before_launch(lib):
     assert call(y=Y, yn=A) == -1                  # y_norm aliases x
     assert call(y=Y, yn=_fake((1 << 23) + 8)) == -1   # y_norm misaligned
     assert call(wsb=1024) == -3
+    # x_norm: x is the raw input; it may then be y, but x_norm aliases nothing
+    XN = _fake(1 << 25)
+    assert call(y=A, xn=XN, wsb=1024) == -3       # x == y allowed: reaches the size check
+    assert call(y=Y, xn=A) == -1                  # x_norm aliases x
+    assert call(y=Y, xn=Y) == -1                  # x_norm aliases y
+    assert call(y=Y, yn=XN, xn=XN) == -1          # x_norm aliases y_norm
+    assert call(y=Y, xn=_fake((1 << 25) + 4)) == -1   # misaligned
 
 
 def test_head_and_rmsnorm_validation(lib):
@@ -245,7 +252,7 @@ def test_coreset_validation(lib):
     def call(top_p=0.9, block=32, T=32):
         return lib.bdm_moe_block_forward_coreset(
             A, T, 2048, A, None, 256, 8, 1, top_p, block, A, A, A, 512, A, A, A, 0, None, A,
-            None, None, None, None, A, size, None)
+            None, None, None, None, None, A, size, None)
     assert call(top_p=0.0) == -1
     assert call(top_p=-0.5) == -1
     assert call(top_p=1.5) == -1

@@ -166,6 +166,41 @@ def test_moe_skew_all_tokens(bdm, skew_layer, layout):
     compare_moe(y, idx, w, o)
 
 
+@pytest.mark.parametrize("T,coreset", [(8, False), (32, False), (32, True), (256, False),
+                                       (512, False)])
+def test_moe_prenorm_equals_rmsnorm_then_layer(bdm, T, coreset):
+    """x_norm given: the layer normalises its raw input itself (inside the
+    router below 512 tokens, a separate RMSNorm launch from 512); the
+    normalised rows, routing and output equal bdm_rmsnorm followed by the
+    layer bit for bit, also in place (x is the residual and the output)."""
+    say(f"case moe pre-norm T={T} coreset={coreset}")
+    s = synth.MoEShape(T=T, H=2048, E=256, I=512, k=8)
+    inp = synth.moe_inputs(s, seed=31, block_seed=T, device=DEV)
+    x = (inp.x.float() * 2.5).to(torch.bfloat16)          # a residual stream, not unit RMS
+    kw = dict(ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down)
+    if coreset:
+        kw.update(coreset_top_p=0.9, coreset_block=32,
+                  n_kept=torch.zeros(1, dtype=torch.int32, device=DEV))
+    xn = torch.empty_like(x)
+    bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+    ref, idx0 = torch.empty_like(x), torch.empty((T, s.k), dtype=torch.int32, device=DEV)
+    bdm.bdm_moe_block_forward(xn, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+                              residual=x, y=ref, topk_idx=idx0, **kw)
+    xn2, y2 = torch.empty_like(x), torch.empty_like(x)
+    idx2 = torch.empty_like(idx0)
+    bdm.bdm_moe_block_forward(x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+                              residual=x, y=y2, topk_idx=idx2, x_norm=xn2, **kw)
+    buf, xn3 = x.clone(), torch.empty_like(x)
+    bdm.bdm_moe_block_forward(buf, inp.w_router, inp.w_gate, inp.w_up, inp.w_down, s.k,
+                              residual=buf, y=buf, x_norm=xn3, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(xn2.view(torch.int16), xn.view(torch.int16))
+    assert torch.equal(xn3.view(torch.int16), xn.view(torch.int16))
+    assert torch.equal(idx2, idx0)
+    assert torch.equal(y2.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(buf.view(torch.int16), ref.view(torch.int16))
+
+
 def test_moe_repeatable_bitwise(bdm):
     say("case moe repeatability (and row-major == packed bits)")
     inp = synth.moe_inputs(synth.LAYER, seed=0, block_seed=3, device=DEV, with_residual=True)
