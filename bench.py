@@ -3,8 +3,8 @@
 
 A step is one pass of the whole hot path over one 32-slot block:
 
-    x' = x + MoE(RMSNorm(x))  (Clover-shaped layer;   bdm_moe_block_forward with
-         the RMSNorm taken inside the router)          x_norm
+    xn = RMSNorm(x)                                   bdm_rmsnorm
+    x' = x + MoE(xn)   (Clover-shaped layer)          bdm_moe_block_forward
     stats = head(x')   (online-softmax partials)      bdm_lm_head_stats
     tokens = unmask(merge(stats))                     bdm_unmask_from_stats
 
@@ -65,6 +65,10 @@ def parse():
     p.add_argument("--layout", type=int, default=2,
                    help="weight layout (packed once, untimed): 2 = MFMA tiles with gate/up "
                         "packed as pairs, 1 = MFMA tiles, 0 = row-major")
+    p.add_argument("--norm-in-router", action="store_true",
+                   help="take the step's RMSNorm inside the router (x_norm) instead of its own "
+                        "launch (the same bits; measured no faster: every router workgroup "
+                        "reduces all 32 rows)")
     return p.parse_args()
 
 
@@ -135,19 +139,31 @@ def main():
         x = xs[r]
         if ev is not None:
             ev[0].record()
-        # the RMSNorm of the layer's input is taken inside the router (x_norm)
-        bdm.bdm_moe_block_forward(x, inp.w_router, kw["w_gate"], kw["w_up"], kw["w_down"], L.k,
-                                  ws_gate=kw["ws_gate"], ws_up=kw["ws_up"], ws_down=kw["ws_down"],
-                                  residual=x, y=xo[r], topk_idx=idx, ws=moe_ws, x_norm=xn)
-        if ev is not None:
-            ev[1].record()
-        bdm.bdm_lm_head_stats(xo[r], w_head, HS.mask_id, st_m, st_s, st_a)
+        if args.norm_in_router:
+            # the RMSNorm taken inside the router (x_norm)
+            bdm.bdm_moe_block_forward(x, inp.w_router, kw["w_gate"], kw["w_up"], kw["w_down"],
+                                      L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                      ws_down=kw["ws_down"], residual=x, y=xo[r], topk_idx=idx,
+                                      ws=moe_ws, x_norm=xn)
+            if ev is not None:
+                ev[1].record()
+        else:
+            bdm.bdm_rmsnorm(x, xn, eps=1e-6)
+            if ev is not None:
+                ev[1].record()
+            bdm.bdm_moe_block_forward(xn, inp.w_router, kw["w_gate"], kw["w_up"], kw["w_down"],
+                                      L.k, ws_gate=kw["ws_gate"], ws_up=kw["ws_up"],
+                                      ws_down=kw["ws_down"], residual=x, y=xo[r], topk_idx=idx,
+                                      ws=moe_ws)
         if ev is not None:
             ev[2].record()
+        bdm.bdm_lm_head_stats(xo[r], w_head, HS.mask_id, st_m, st_s, st_a)
+        if ev is not None:
+            ev[3].record()
         bdm.bdm_unmask_from_stats(st_m, st_s, st_a, HS.mask_id, 0.95, True, tokens[r],
                                   n_committed=nc)
         if ev is not None:
-            ev[3].record()
+            ev[4].record()
 
     # touched experts per set (routing of each set's step input)
     touched, xns = [], []
@@ -167,7 +183,7 @@ def main():
     torch.cuda.synchronize()
 
     # per-call timing (events between the three calls of every step)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -180,10 +196,14 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    moe_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    merge_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
+    # (with the RMSNorm inside the router, events 1 and 2 coincide)
+    norm_us = 0.0 if args.norm_in_router else \
+        1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    moe_us = 1e3 * float(np.mean([e[0 if args.norm_in_router else 1].elapsed_time(e[2])
+                                  for e in evs]))
+    gemm_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    merge_us = 1e3 * float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
     head_us = gemm_us + merge_us
 
     # untimed-by-events replay of the same steps (no event records in between)
@@ -444,10 +464,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random init)",
         "config": {
-            "workload": "one denoise step over a 32-slot block: one Clover-shaped MoE layer on "
-                        "the RMSNorm of its input (H 2048, 256 experts SwiGLU 2048->512->2048 + "
-                        "1 shared, top-8 renormalised; the RMSNorm inside the router) + untied "
-                        "248,320x2048 head with the 0.95 unmask rule",
+            "workload": "one denoise step over a 32-slot block: RMSNorm + one Clover-shaped MoE "
+                        "layer (H 2048, 256 experts SwiGLU 2048->512->2048 + 1 shared, top-8 "
+                        "renormalised) + untied 248,320x2048 head with the 0.95 unmask rule",
+            "rmsnorm": "inside the router (x_norm)" if args.norm_in_router else
+                       "its own launch (bdm_rmsnorm)",
             "block_tokens": T, "hidden": H, "experts": L.E, "top_k": L.k, "inter": L.I,
             "vocab": HS.V, "weight_sets_rotated": args.sets, "parallelism": "single GPU",
             "weight_layout": {2: "mfma_tiles, gate/up as pairs (packed once at load)",
@@ -475,6 +496,7 @@ def main():
                                 "GB_s": round(verify_gbs, 1),
                                 "frac_of_peak": round(verify_gbs / PEAK_HBM_GBS, 4)},
         "denoise_step_stack": stack,
+        "rmsnorm_us": round(norm_us, 2),
         "ms_per_step_with_events": round(ms_step, 4),
         "ms_per_step_event_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4)
                                           for q in (10, 50, 90)],

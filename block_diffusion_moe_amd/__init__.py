@@ -8,8 +8,8 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
 from .binding import (BDM_LAYOUT_MFMA_TILES, BDM_LAYOUT_MFMA_TILES_GU, BDM_LAYOUT_ROW_MAJOR,
                       BDM_MASK_ID_CLOVER, BDM_THRESHOLD_DEFAULT, BDM_VERIFY_EXACT, BDM_VERIFY_THRESHOLD, EXPORTS,
-                      LIB_PATH, BdmError, MoeLayerC, MoeStack, Packed,
-                      bdm_denoise_block, bdm_denoise_workspace_bytes,
+                      DEBUG_LIB_PATH, LIB_PATH, BdmError, MoeLayerC, MoeStack, Packed,
+                      bdm_debug_bounds, bdm_denoise_block, bdm_denoise_workspace_bytes,
                       bdm_head_stat_parts, bdm_head_verify_workspace_bytes,
                       bdm_head_workspace_bytes, bdm_lm_head_stats, bdm_lm_head_unmask,
                       bdm_lm_head_verify, bdm_moe_block_forward, bdm_moe_block_forward_noalloc,
@@ -21,8 +21,8 @@ from .binding import (BDM_LAYOUT_MFMA_TILES, BDM_LAYOUT_MFMA_TILES_GU, BDM_LAYOU
 __all__ = [
     "BDM_LAYOUT_MFMA_TILES", "BDM_LAYOUT_MFMA_TILES_GU", "BDM_LAYOUT_ROW_MAJOR",
     "BDM_MASK_ID_CLOVER", "BDM_THRESHOLD_DEFAULT", "BDM_VERIFY_EXACT", "BDM_VERIFY_THRESHOLD", "EXPORTS",
-    "LIB_PATH", "BdmError", "MoeLayerC", "MoeStack", "Packed",
-    "bdm_denoise_block", "bdm_denoise_workspace_bytes",
+    "DEBUG_LIB_PATH", "LIB_PATH", "BdmError", "MoeLayerC", "MoeStack", "Packed",
+    "bdm_debug_bounds", "bdm_denoise_block", "bdm_denoise_workspace_bytes",
     "bdm_head_stat_parts", "bdm_head_verify_workspace_bytes", "bdm_head_workspace_bytes",
     "bdm_lm_head_stats", "bdm_lm_head_verify",
     "bdm_unmask_from_stats", "bdm_lm_head_unmask", "bdm_moe_block_forward",

@@ -15,6 +15,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbdmoe.so")
+# the same entry points with device-side bounds checks (bdm_debug_bounds)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libbdmoe_debug.so")
 
 BDM_OK = 0
 BDM_MASK_ID_CLOVER = 151669
@@ -28,6 +30,7 @@ _c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, 
 _SIGS = {
     "bdm_version": (_c_int, []),
     "bdm_status_string": (ctypes.c_char_p, [_c_int]),
+    "bdm_debug_bounds": (_c_int, [ctypes.POINTER(ctypes.c_uint)]),
     "bdm_moe_workspace_bytes": (_c_int, [_c_int] * 6 + [ctypes.POINTER(_c_size)]),
     "bdm_moe_block_forward": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int,
                                        _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp,
@@ -76,12 +79,15 @@ class BdmError(RuntimeError):
         self.status = status
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the library (once).  torch is imported first so the library binds
-    to the HIP runtime torch uses."""
+def load(path: str = None) -> ctypes.CDLL:
+    """Load the library (once): `path`, else $BDM_LIBRARY, else libbdmoe.so
+    (DEBUG_LIB_PATH is the bounds-checked build).  torch is imported first so
+    the library binds to the HIP runtime torch uses."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("BDM_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m block_diffusion_moe_amd.build`")
     lib = ctypes.CDLL(path)
@@ -161,6 +167,18 @@ def bdm_version() -> int:
 
 def bdm_status_string(status: int) -> str:
     return load().bdm_status_string(status).decode()
+
+
+BDM_ERR_NOT_DEBUG_BUILD = -5
+
+
+def bdm_debug_bounds() -> int:
+    """The debug build's bounds-check violation bits since the last call
+    (0: none), cleared; synchronises with the device.  Raises BdmError on
+    the release library."""
+    v = ctypes.c_uint(0)
+    _raise("bdm_debug_bounds", load().bdm_debug_bounds(ctypes.byref(v)))
+    return int(v.value)
 
 
 def bdm_moe_workspace_bytes(T, H, I, E, k, has_shared) -> int:

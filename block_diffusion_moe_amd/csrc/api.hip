@@ -179,7 +179,7 @@ int last_hip_status() {
 
 extern "C" {
 
-int bdm_version(void) { return 101; }
+int bdm_version(void) { return 102; }
 
 const char* bdm_status_string(int status) {
   switch (status) {
@@ -188,8 +188,22 @@ const char* bdm_status_string(int status) {
     case BDM_ERR_UNSUPPORTED_SHAPE: return "shape outside the supported limits";
     case BDM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case BDM_ERR_HIP: return "HIP launch or runtime error";
+    case BDM_ERR_NOT_DEBUG_BUILD: return "not the bounds-checked debug build";
     default: return "unknown status";
   }
+}
+
+int bdm_debug_bounds(unsigned int* violations) {
+  if (!violations) return BDM_ERR_INVALID_ARG;
+  *violations = 0u;
+  if (!BDM_DEBUG_BOUNDS) return BDM_ERR_NOT_DEBUG_BUILD;
+  if (hipDeviceSynchronize() != hipSuccess) return BDM_ERR_HIP;
+  unsigned int w = 0u;
+  if (bdm::debug_words_router(&w) || bdm::debug_words_experts(&w) ||
+      bdm::debug_words_head(&w) || bdm::debug_words_embed(&w))
+    return BDM_ERR_HIP;
+  *violations = w;
+  return BDM_OK;
 }
 
 int bdm_moe_workspace_bytes(int T, int H, int I, int E, int k, int has_shared, size_t* bytes) {

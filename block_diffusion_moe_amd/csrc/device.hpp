@@ -18,6 +18,57 @@
 
 namespace bdm {
 
+// ---- bounds checks of data-dependent indices ------------------------------
+// An index read from memory (a slot of the table, a pair row, a pick, a
+// token id) or derived from one is passed through chk(i, n, code) before it
+// addresses a buffer of n elements.  In the debug build (BDM_DEBUG_BOUNDS=1,
+// libbdmoe_debug.so) an index outside [0, n) sets bit `code` of this source
+// file's violation word and is clamped into range, so the access stays in
+// its buffer and the call completes; bdm_debug_bounds() reads and clears
+// the words.  In the release build chk is the index itself.  Checks that a
+// release kernel already makes (it clamps or skips) report through
+// note_oob(code) in the debug build.
+#ifndef BDM_DEBUG_BOUNDS
+#define BDM_DEBUG_BOUNDS 0
+#endif
+enum BdmCheck : unsigned {
+  kChkSlot = 0,       // a slot-table entry that is neither a valid group nor the end mark
+  kChkPairRow = 1,    // a (token, slot) pair row outside [0, T (k+1))
+  kChkExpert = 2,     // an expert id outside [0, E) (-1 = empty pick is allowed)
+  kChkTokenRow = 3,   // a token row outside [0, T)
+  kChkVocabRow = 4,   // a head / embedding row outside [0, V)
+  kChkTokenId = 5,    // a token id outside [0, V) given to the embedding gather
+  kChkStat = 6,       // an online-softmax partial outside [0, T * parts)
+  kChkCand = 7,       // a re-route candidate or rank outside its table
+  kChkWs = 8,         // a workspace table index outside its sized extent
+};
+#if BDM_DEBUG_BOUNDS
+static __device__ unsigned int g_bdm_oob;
+__device__ __forceinline__ void note_oob(unsigned code) { atomicOr(&g_bdm_oob, 1u << code); }
+__device__ __forceinline__ long chk(long i, long n, unsigned code) {
+  if (i >= 0 && i < n) return i;
+  note_oob(code);
+  return i < 0 || n <= 0 ? 0 : n - 1;
+}
+// Host side: read this file's violation word into *out and clear it.
+#define BDM_DEBUG_WORD_READER(NAME)                                              \
+  int NAME(unsigned int* out) {                                                  \
+    unsigned int v = 0u;                                                         \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_bdm_oob), sizeof(v)) != hipSuccess) \
+      return -1;                                                                 \
+    const unsigned int z = 0u;                                                   \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_bdm_oob), &z, sizeof(z)) != hipSuccess)   \
+      return -1;                                                                 \
+    *out |= v;                                                                   \
+    return 0;                                                                    \
+  }
+#else
+__device__ __forceinline__ void note_oob(unsigned) {}
+__device__ __forceinline__ long chk(long i, long, unsigned) { return i; }
+#define BDM_DEBUG_WORD_READER(NAME) \
+  int NAME(unsigned int*) { return 0; }
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -16,8 +16,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
                                                     uint16_t* __restrict__ xn) {
   __shared__ float part[4];
   const int t = blockIdx.x;
-  int id = tokens[t];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  // an id outside the vocabulary reads the nearest row (and is reported in
+  // the debug build)
+  const int tid_raw = tokens[t];
+  if ((tid_raw < 0 || tid_raw >= V) && threadIdx.x == 0) note_oob(kChkTokenId);
+  const int id = tid_raw < 0 ? 0 : (tid_raw >= V ? V - 1 : tid_raw);
   const int i0 = threadIdx.x * 8;
   const bool on = i0 < H;
   const u32x4 raw = on ? ld16(w + static_cast<size_t>(id) * H + i0) : u32x4{0u, 0u, 0u, 0u};
@@ -42,5 +45,7 @@ void launch_embed(const int32_t* tokens, int T, const uint16_t* w_embed, int V, 
                   uint16_t* x, uint16_t* xn, hipStream_t s) {
   embed_kernel<<<T, 256, 0, s>>>(tokens, w_embed, V, H, x, xn);
 }
+
+BDM_DEBUG_WORD_READER(debug_words_embed)
 
 }  // namespace bdm

@@ -44,11 +44,21 @@ constexpr int kDnRows = 16 * kDnWaves;  // H rows per down work item
 
 // A slot names a real group: expert id in [0, E] (E only with a shared
 // expert), 1 <= count, and its pair rows inside [0, P).
+// (The end mark {-1, 0, 0, 0} is not a group; any other entry that fails
+// is reported in the debug build.)
 __device__ __forceinline__ bool slot_ok(int e, int off, int m, int E, int P, bool has_shared) {
-  return e >= 0 && (e < E || (e == E && has_shared)) && m >= 1 && off >= 0 && off <= P - m;
+  const bool ok =
+      e >= 0 && (e < E || (e == E && has_shared)) && m >= 1 && off >= 0 && off <= P - m;
+  if (!ok && !(e == -1 && off == 0 && m == 0)) note_oob(kChkSlot);
+  return ok;
 }
 
-__device__ __forceinline__ int clamp_row(int r, int P) { return r < 0 ? 0 : (r >= P ? P - 1 : r); }
+// A pair row read from the table, kept inside [0, P) (a row outside is
+// reported in the debug build).
+__device__ __forceinline__ int clamp_row(int r, int P) {
+  if (r < 0 || r >= P) note_oob(kChkPairRow);
+  return r < 0 ? 0 : (r >= P ? P - 1 : r);
+}
 
 // gate/up fragments.  In the pair layout the packed gate and up groups
 // alternate in one buffer (w_up = w_gate + one group), so consecutive groups
@@ -739,5 +749,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
   combine_kernel<<<T, 256, 0, s>>>(meta.ypair, H, k, has_shared, meta.topk_idx, meta.topk_w,
                                    residual, y, y_norm);
 }
+
+BDM_DEBUG_WORD_READER(debug_words_experts)
 
 }  // namespace bdm

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_tile_kernel(
   if (tid < ntok) {
     SoftStat s = red[tid];
     for (int wv = 1; wv < kHeadWaves; ++wv) s = softstat_merge(s, red[wv * kHeadTokChunk + tid]);
-    const size_t o = static_cast<size_t>(tok0 + tid) * pstride + blockIdx.x;
+    const size_t o = static_cast<size_t>(tok0 + tid) * pstride + chk(blockIdx.x, pstride, kChkStat);
     pm[o] = s.m;
     ps[o] = s.s;
     pa[o] = s.a;
@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
   // weight fragments of group gi (n <= gi: the hidden rows, never used)
   auto wfrag = [&](long gi) -> FragPtr {
     if (gi >= G1) return FragPtr{h + c * 8, 0};
+    gi = chk(gi, ngroups, kChkVocabRow);
     if (layout == BDM_LAYOUT_MFMA_TILES) return frag_ptr(w, gi * 16, H, lane, layout);
     long v = gi * 16 + c;
     v = v < V ? v : V - 1;
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 1) void head_coop_kernel(
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int ot = 16 * (2 * f + (wave >> 2)) + 4 * g + (wave & 3);
-      const size_t o = static_cast<size_t>(pt0 + ot) * pstride + q;
+      const size_t o = static_cast<size_t>(pt0 + ot) * pstride + chk(q, pstride, kChkStat);
       if constexpr (VERIFY) {
         const VStat r = row_merge_vstat(vs[f]);
         if (c == 0 && ot < pn) {
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int i = i0 + u * 16 + sub;
-        part[u] = (on && i < nparts) ? SoftStat{pm[base + i], ps[base + i], pa[base + i]}
-                                     : softstat_empty();
+        const size_t ix = base + chk(i < nparts ? i : 0, pstride, kChkStat);
+        part[u] = (on && i < nparts) ? SoftStat{pm[ix], ps[ix], pa[ix]} : softstat_empty();
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) st = softstat_merge(st, part[u]);
@@ -578,7 +579,10 @@ __global__ __launch_bounds__(1024) void head_merge_kernel(
     }
     wave_argmax(best_c, best_t);
     if (fallback && ncommit == 0 && best_t != INT32_MAX) {
-      if (lane == 0) tokens[best_t] = sarg[best_t];
+      if (lane == 0) {
+        const int bt = chk(best_t, T, kChkTokenRow);
+        tokens[bt] = sarg[bt];
+      }
       ncommit = 1;
     }
     wcommit += ncommit;
@@ -788,5 +792,7 @@ int head_prepare() {
       return -1;
   return 0;
 }
+
+BDM_DEBUG_WORD_READER(debug_words_head)
 
 }  // namespace bdm

@@ -10,6 +10,11 @@
 #define BDM_MAX_HIDDEN_ BDM_MAX_HIDDEN
 #define BDM_MAX_EXPERTS_ BDM_MAX_EXPERTS
 
+// 1 in the bounds-checked debug build (libbdmoe_debug.so)
+#ifndef BDM_DEBUG_BOUNDS
+#define BDM_DEBUG_BOUNDS 0
+#endif
+
 namespace bdm {
 
 // Views into the MoE workspace (all device pointers) for T tokens, E routed
@@ -117,5 +122,12 @@ void launch_pack_pair(const uint16_t* gate, const uint16_t* up, long R, int K, u
 
 void launch_rmsnorm(const uint16_t* x, const float* gamma, float eps, int T, int H,
                     uint16_t* out, hipStream_t s);
+
+// Violation words of the debug build, one per source file (see chk in
+// device.hpp): each ORs its word into *out and clears it; 0 on success.
+int debug_words_router(unsigned int* out);
+int debug_words_experts(unsigned int* out);
+int debug_words_head(unsigned int* out);
+int debug_words_embed(unsigned int* out);
 
 }  // namespace bdm

@@ -48,13 +48,14 @@ constexpr int kRtMaxKs = 4;     // k-steps per wave: H <= kRouterParts * 4 * 4 *
 // step.
 // NTT token tiles of 32 per workgroup share one load and split of the
 // router weights (NTT > 1 for many-block calls).
-// NORM (NTT = 1): x is the layer's un-normalised input.  The workgroup first
-// takes the RMSNorm scale of each of its 32 rows with the arithmetic of the
+// NORM (NTT = 1): x is the layer's un-normalised input.  The workgroup takes
+// the RMSNorm scale of each of its 32 rows with the arithmetic of the
 // RMSNorm kernel (its 256 threads hold a row's 8-element chunks in the same
-// order: per thread fmaf over 8 values, DPP within the wave, then the 4
-// waves pairwise; eps 1e-6), routes on bf16(x * scale), and the workgroups of
-// expert tile 0 write those rows, bit for bit what the RMSNorm kernel
-// writes, to xn (the experts' input).
+// order; the same summation tree, eps 1e-6), routes on bf16(x * scale), and
+// the workgroups of expert tile 0 write those rows, bit for bit what the
+// RMSNorm kernel writes, to xn (the experts' input).  Every workgroup reads
+// and reduces all 32 rows (128 KB at H = 2048), which costs about what the
+// separate RMSNorm launch does.
 template <int NTT, bool NORM = false>
 __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* __restrict__ x,
                                                               int T, int H,
@@ -64,48 +65,33 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
   static_assert(!NORM || NTT == 1, "the fused RMSNorm covers one token tile");
   static_assert(kRtWaves * 64 == 256, "the RMSNorm chunk map needs 256 threads");
   __shared__ f32x4 red[2][kRtWaves][2][kWave];
-  __shared__ float rpart[NORM ? 32 : 1][kRtWaves];
+  // NORM: per-thread sums of squares [thread][row] (row pitch 33: the
+  // column reads below are conflict-free), the 32-thread partials and the
+  // row scales
+  __shared__ float rss[NORM ? 256 * 33 : 1];
+  __shared__ float rq[NORM ? 8 * 32 : 1];
+  __shared__ float rscale[NORM ? 32 : 1];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int c = lane & 15;
   const int g = lane >> 4;
   // NORM: the scales of this lane's rows t0 + c and t0 + 16 + c
   float rsc0 = 1.0f, rsc1 = 1.0f;
+  // NORM: this thread's 8-element chunk of each of the 32 rows, requested
+  // before the router weights and the K-slice (in-order completion: the sums
+  // below wait for these rows only)
+  u32x4 raw[NORM ? 32 : 1];
   if constexpr (NORM) {
     const int tt0 = blockIdx.y * 32;
     const int i0 = threadIdx.x * 8;
     const bool on = i0 < H;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {                  // eight rows at a time, loads first
-      u32x4 raw[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int row = tt0 + 8 * b + r;
-        const bool ok = on && row < T;
-        const u32x4 v = ld16(x + static_cast<size_t>(ok ? row : 0) * H + (on ? i0 : 0));
-        raw[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = __uint_as_float(raw[r][j] << 16);
-          const float hi = __uint_as_float(raw[r][j] & 0xffff0000u);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
-        }
-        ss = wave_sum(ss);
-        if (lane == 0) rpart[8 * b + r][wave] = ss;
-      }
+    for (int r = 0; r < 32; ++r) {
+      const int row = tt0 + r;
+      const bool ok = on && row < T;
+      const u32x4 v = ld16(x + static_cast<size_t>(ok ? row : 0) * H + (on ? i0 : 0));
+      raw[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
-    auto scale = [&](int r) {
-      const float tot = (rpart[r][0] + rpart[r][1]) + (rpart[r][2] + rpart[r][3]);
-      return 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
-    };
-    rsc0 = scale(c);
-    rsc1 = scale(16 + c);
   }
   // 16 bytes of a row times its scale, rounded as the RMSNorm kernel rounds
   auto norm16 = [](u32x4 v, float r) {
@@ -139,20 +125,22 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
       a0[q] = ok0 ? v0 : u32x4{0u, 0u, 0u, 0u};
       a1[q] = ok1 ? v1 : u32x4{0u, 0u, 0u, 0u};
     }
-    if constexpr (NORM) {
+  };
+  // NORM: scale the K-slice of rows t0 + c and t0 + 16 + c; expert tile 0
+  // writes the normalised rows (each (row, k-step) once)
+  auto xnorm = [&](int t0, u32x4(&a0)[kRtMaxKs], u32x4(&a1)[kRtMaxKs]) {
+    const bool ok0 = (t0 + c) < T, ok1 = (t0 + 16 + c) < T;
 #pragma unroll
-      for (int q = 0; q < kRtMaxKs; ++q) {
-        a0[q] = norm16(a0[q], rsc0);
-        a1[q] = norm16(a1[q], rsc1);
-        // expert tile 0 writes the normalised rows (each (row, k-step) once)
-        if (blockIdx.x == 0 && s0 + q < s1) {
-          const int s = s0 + q;
-          if (ok0)
-            *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + c) * H + s * 32 + g * 8) = a0[q];
-          if (ok1)
-            *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + 16 + c) * H + s * 32 + g * 8) =
-                a1[q];
-        }
+    for (int q = 0; q < kRtMaxKs; ++q) {
+      a0[q] = norm16(a0[q], rsc0);
+      a1[q] = norm16(a1[q], rsc1);
+      if (blockIdx.x == 0 && s0 + q < s1) {
+        const int s = s0 + q;
+        if (ok0)
+          *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + c) * H + s * 32 + g * 8) = a0[q];
+        if (ok1)
+          *reinterpret_cast<u32x4*>(xn + static_cast<size_t>(t0 + 16 + c) * H + s * 32 + g * 8) =
+              a1[q];
       }
     }
   };
@@ -167,6 +155,50 @@ __global__ __launch_bounds__(kRtWaves * 64) void router_kernel(const uint16_t* _
     wb[q] = *reinterpret_cast<const float4*>(wrow + s * 32 + 4);
   }
   xload(blockIdx.y * NTT * 32, a0, a1);
+  if constexpr (NORM) {
+    // each row's sum of squares, the RMSNorm kernel's summation tree: per
+    // thread fmaf over its 8 values in order, then a balanced binary tree
+    // over the 256 threads in thread order (its DPP steps, rows of 16
+    // lanes, the wave's 4 rows and the 4 waves pairwise are exactly that
+    // tree).  Here the 32 rows are reduced side by side: thread (part p =
+    // tid / 32, row r = tid % 32) sums threads 32p .. 32p + 31 of row r as a
+    // 5-level tree, thread r < 32 the 8 parts as a 3-level one.
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(raw[r][j] << 16);
+        const float hi = __uint_as_float(raw[r][j] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      rss[threadIdx.x * 33 + r] = ss;
+    }
+    __syncthreads();
+    {
+      const int r = threadIdx.x % 32, p = threadIdx.x / 32;
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = rss[(32 * p + j) * 33 + r];
+#pragma unroll
+      for (int w = 1; w < 32; w *= 2)
+#pragma unroll
+        for (int j = 0; j < 32; j += 2 * w) v[j] = v[j] + v[j + w];
+      rq[p * 32 + r] = v[0];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int r = threadIdx.x;
+      const float tot = ((rq[r] + rq[32 + r]) + (rq[64 + r] + rq[96 + r])) +
+                        ((rq[128 + r] + rq[160 + r]) + (rq[192 + r] + rq[224 + r]));
+      rscale[r] = 1.0f / sqrtf(tot / static_cast<float>(H) + 1e-6f);
+    }
+    __syncthreads();
+    rsc0 = rscale[c];
+    rsc1 = rscale[16 + c];
+    xnorm(blockIdx.y * NTT * 32, a0, a1);
+  }
   u32x4 bh[kRtMaxKs], bm[kRtMaxKs], bl[kRtMaxKs];
 #pragma unroll
   for (int q = 0; q < kRtMaxKs; ++q) {
@@ -392,11 +424,14 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
       eb[u] = p < np ? picks[p] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) {
       if (eb[u] >= 0 && eb[u] < E) atomicAdd(&cnt[eb[u]], 1);
+      else if (eb[u] != -1) note_oob(kChkExpert);   // -1: an empty pick
+    }
   }
   __syncthreads();
   const int nsh = has_shared ? (T + kSlotChunk - 1) / kSlotChunk : 0;   // shared chunks
+  const int nslot = moe_max_slots(T, E, k, has_shared);                // slots[] extent
   if (wave == 0) {
     constexpr int EPL = PER;                          // experts per lane, at most
     const int epl = (E + kWave - 1) / kWave;          // E <= 64 * PER
@@ -437,11 +472,11 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
           int q = 0;
           for (int o = 0; o < c[j]; o += kSlotChunk, ++q) {
             const int m = c[j] - o < kSlotChunk ? c[j] - o : kSlotChunk;
-            slots[pos + q] = int4{e, pref + o, m, nch};
+            slots[chk(pos + q, nslot, kChkWs)] = int4{e, pref + o, m, nch};
           }
           ho += q;
         } else {
-          slots[nsh + nh + lb + lo] = int4{e, pref, c[j], 1};
+          slots[chk(nsh + nh + lb + lo, nslot, kChkWs)] = int4{e, pref, c[j], 1};
           ++lo;
         }
         eoff[e] = pref;
@@ -453,8 +488,7 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
       const int o = i * kSlotChunk;
       slots[i] = int4{E, o, T - o < kSlotChunk ? T - o : kSlotChunk, nsh};
     }
-    const int nmax = moe_max_slots(T, E, k, has_shared);
-    for (int i = n + lane; i < nmax; i += kWave) slots[i] = int4{-1, 0, 0, 0};
+    for (int i = n + lane; i < nslot; i += kWave) slots[i] = int4{-1, 0, 0, 0};
     if (lane == 0) info[0] = n;
   }
   // scatter the pairs
@@ -472,7 +506,8 @@ __device__ void group_picks(const int32_t* picks, int T, int E, int k, int has_s
       if (e < 0 || e >= E) continue;
       const int p = p0 + u * static_cast<int>(blockDim.x) + tid;
       const int tt = p / k;
-      pair_rows[eoff[e] + atomicAdd(&fill[e], 1)] = tt * K1 + (p - tt * k);
+      pair_rows[chk(eoff[e] + atomicAdd(&fill[e], 1), T * K1, kChkPairRow)] =
+          tt * K1 + (p - tt * k);
     }
   }
   if (has_shared)
@@ -561,7 +596,8 @@ __device__ __forceinline__ void reroute_pick(const float (&v)[PER], int fe, cons
                                              int keep, int E, int k, int renorm, int lane,
                                              int& sel_e, float& sel_w) {
   const unsigned long long below = (1ull << lane) - 1ull;
-  const bool fkeep = lane < k && fe >= 0 && rank_of[fe] >= 0 && rank_of[fe] < keep;
+  const int fr = (lane < k && fe >= 0) ? rank_of[chk(fe, E, kChkExpert)] : -1;
+  const bool fkeep = fr >= 0 && fr < keep;
   const unsigned long long km = __ballot(fkeep);
   const int nfk = __popcll(km);
   const int kk = min(k, keep);
@@ -743,8 +779,10 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
         pv[u] = in ? sp[i] : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 8; ++u) {
         if (ee[u] >= 0 && ee[u] < E) mpart[wave][ee[u]] += pv[u];
+        else if (ee[u] != -1) note_oob(kChkExpert);
+      }
     }
   }
   __syncthreads();
@@ -754,7 +792,7 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     cnt[e] = 0;
     rank_of[e] = -1;
     if (m > 0.0f) {
-      const int q = atomicAdd(&s_ntouch, 1);
+      const int q = chk(atomicAdd(&s_ntouch, 1), E, kChkCand);
       tlist[q] = e;
       tmass[q] = m;
     }
@@ -781,7 +819,7 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
   __syncthreads();
   for (int q = tid; q < nt; q += blockDim.x) {
     const int e = tlist[q];
-    const int r = cnt[e];
+    const int r = chk(cnt[e], E, kChkCand);
     smass[r] = tmass[q];
     rank_of[e] = r;
   }
@@ -826,7 +864,8 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
     const int tl = wave + r * kCsWaves;
     if (tl < nb) {
       const int fe = lane < k ? sidx[tl * k + lane] : -1;
-      const bool fkeep = lane < k && fe >= 0 && rank_of[fe] >= 0 && rank_of[fe] < keep;
+      const int fr = (lane < k && fe >= 0) ? rank_of[chk(fe, E, kChkExpert)] : -1;
+      const bool fkeep = fr >= 0 && fr < keep;
       int sel_e;
       float sel_w;
       if (renorm && __popcll(__ballot(fkeep)) == k) {
@@ -940,5 +979,7 @@ void launch_router(const uint16_t* x, int T, int H, const float* wr, const float
   }
 #undef BDM_SELECT
 }
+
+BDM_DEBUG_WORD_READER(debug_words_router)
 
 }  // namespace bdm

@@ -57,6 +57,7 @@ extern "C" {
 #define BDM_ERR_UNSUPPORTED_SHAPE   -2  /* legal sizes outside the kernels' limits */
 #define BDM_ERR_WORKSPACE_TOO_SMALL -3
 #define BDM_ERR_HIP                 -4  /* a HIP call failed */
+#define BDM_ERR_NOT_DEBUG_BUILD     -5  /* bdm_debug_bounds on the release library */
 
 /* [files] "What Clover is": mask_token_id 151669, low_confidence threshold 0.95 */
 #define BDM_MASK_ID_CLOVER     151669
@@ -93,6 +94,29 @@ BDM_API int bdm_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 BDM_API const char* bdm_status_string(int status);
+
+/*
+ * bdm_debug_bounds -- the bounds checks of the debug build.
+ *
+ * The library is also built as libbdmoe_debug.so (BDM_DEBUG_BOUNDS=1), the
+ * same entry points with a device-side check on every index the kernels
+ * read from memory or derive from what they read: slot-table entries, pair
+ * rows, expert picks, re-route candidates and ranks, token ids given to the
+ * embedding gather, head row groups and partial indices.  A check that
+ * fails sets one bit of a violation word (the bit numbers are the kChk*
+ * codes of the kernels' device header: 0 slot entry, 1 pair row, 2 expert
+ * id, 3 token row, 4 vocabulary row, 5 token id, 6 softmax partial, 7
+ * re-route candidate or rank, 8 workspace table index) and the index is
+ * clamped into its buffer, so the call still completes.
+ *
+ * Writes the OR of the words of every kernel file, on the current device,
+ * to *violations and clears them.  It synchronises with the device's work
+ * (call it after the calls it checks have been ordered before it).
+ * Returns BDM_OK; BDM_ERR_NOT_DEBUG_BUILD from the release library (which
+ * has no checks; *violations is set to 0); BDM_ERR_INVALID_ARG for a NULL
+ * pointer; BDM_ERR_HIP if reading the words fails.
+ */
+BDM_API int bdm_debug_bounds(unsigned int* violations);
 
 /*
  * bdm_moe_workspace_bytes -- workspace size for bdm_moe_block_forward.

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                            "bdm_unmask_from_stats", "bdm_moe_block_forward_coreset",
                            "bdm_denoise_workspace_bytes", "bdm_denoise_block",
                            "bdm_head_verify_workspace_bytes", "bdm_lm_head_verify",
-                           "bdm_moe_block_forward_noalloc"])
+                           "bdm_moe_block_forward_noalloc", "bdm_debug_bounds"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,8 +44,31 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
     assert sorted(binding.EXPORTS) == declared_symbols()
     assert lib.bdm_version() >= 100
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.bdm_status_string(st), bytes)
+
+
+def test_debug_bounds_library_and_release_answer(lib):
+    """The bounds-checked build exports the same symbols (and holds gfx950
+    code); the release library answers bdm_debug_bounds with
+    BDM_ERR_NOT_DEBUG_BUILD before any device call."""
+    from block_diffusion_moe_amd import binding
+    assert os.path.exists(binding.DEBUG_LIB_PATH), "libbdmoe_debug.so not built"
+    dbg = ctypes.CDLL(binding.DEBUG_LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(dbg, name), name
+    dbg.bdm_version.restype = ctypes.c_int
+    assert dbg.bdm_version() == lib.bdm_version()
+    assert b"gfx950" in open(binding.DEBUG_LIB_PATH, "rb").read()
+    dbg.bdm_debug_bounds.restype = ctypes.c_int
+    assert dbg.bdm_debug_bounds(None) == -1
+    v = ctypes.c_uint(123)
+    assert lib.bdm_debug_bounds(ctypes.byref(v)) == binding.BDM_ERR_NOT_DEBUG_BUILD
+    assert v.value == 0
+    assert lib.bdm_debug_bounds(None) == -1
+    assert b"debug" in lib.bdm_status_string(binding.BDM_ERR_NOT_DEBUG_BUILD)
+    with pytest.raises(binding.BdmError):
+        binding.bdm_debug_bounds()
 
 
 def test_library_is_gfx950_code_object():
