@@ -13,6 +13,11 @@
 //                      A operand.  The logits never leave registers: each
 //                      (token, workgroup) keeps only the online-softmax triple
 //                      (max, sum of exp, argmax).
+//   head_coop_kernel   the same with the 8 waves of a workgroup splitting K
+//                      and moving in step (up to 64 rows per pass; the passes
+//                      of more rows in one launch).
+//   head_gemm_kernel   from 256 rows: a tiled GEMM (256 x 256 tiles staged in
+//                      LDS, the whole K per tile) with the same epilogue.
 //   head_merge_kernel  one workgroup: merges the triples of all workgroups in
 //                      a fixed tree per token -> conf = 1 / sum, argmax; then
 //                      applies the commit rule and its progress fallback.
@@ -705,6 +710,295 @@ static HeadKernel head_kernel_for(int H) {
   return kHeadKernels[(u == kHeadU ? 0 : 2) + (even ? 0 : 1)];
 }
 
+// ---- many rows: the head as a tiled GEMM ----------------------------------
+// From kGmMinRows rows (several blocks in one call) the head has enough rows
+// to be bound by the MFMA units and the caches, not by HBM: 2 * rows * V * H
+// flops over a gigabyte of weights.  Workgroup (range q, row block mb): the
+// 256 rows of block mb against the vocabulary range q (the same 16-row
+// groups as the persistent kernel's workgroup q, so the partials have the
+// same meaning), in chunks of 256 vocabulary rows, each chunk over the whole
+// K = H.  A stage is one MFMA k-step: 16 tiles of hidden rows and 16 of
+// vocabulary rows (16 x 32 each, 1 KB), loaded straight into LDS in MFMA
+// operand order (global_load_lds: lane l's 16 bytes land at l * 16, so the
+// operand reads are conflict-free 16-byte reads); four stage buffers, the
+// loads of the next three stages in flight while one is multiplied, one
+// barrier per stage.  Wave (wm, wn) of the 8 owns rows 64 wm .. +63 and
+// vocabulary rows 128 wn .. +127 of the chunk: 4 x 8 accumulator tiles, 12
+// KB of LDS reads for 32 MFMAs per k-step.  The chunk's logits never leave
+// the accumulators: each lane folds its 8 logits per row into its own
+// online-softmax state of that row (max, sum of exp, argmax; the mask token
+// and rows past the range at -inf, NaN as -inf), and after the last chunk the
+// 16 lanes of a row and the two vocabulary halves are merged in a fixed tree.
+// The row blocks of one range run next to each other on one XCD (workgroup b
+// on XCD b % 8), so a chunk's weights come from HBM about once and from L2
+// for the other row blocks.
+constexpr int kGmBM = 256;          // hidden rows per workgroup
+constexpr int kGmBN = 256;          // vocabulary rows per chunk
+constexpr int kGmBK = 32;           // k per stage (one MFMA k-step)
+constexpr int kGmTiles = 32;        // 1 KB operand tiles per stage: 16 of rows, 16 of vocabulary
+#ifndef BDM_HEAD_GEMM_BUFS
+#define BDM_HEAD_GEMM_BUFS 4
+#endif
+constexpr int kGmBufs = BDM_HEAD_GEMM_BUFS;   // stage buffers: all but one in flight (4 or 5)
+static_assert(kGmBufs == 4 || kGmBufs == 5, "four or five stage buffers");
+#ifndef BDM_HEAD_GEMM_MIN_T
+#define BDM_HEAD_GEMM_MIN_T 256
+#endif
+constexpr int kGmMinRows = BDM_HEAD_GEMM_MIN_T;
+#ifndef BDM_HEAD_GEMM_MGROUP
+#define BDM_HEAD_GEMM_MGROUP 0      // row blocks per group (0: all of them)
+#endif
+
+// fold the 8 logits of one row this lane holds (vocabulary ids v0 + 16 j,
+// increasing) into this lane's running state of the row (max, sum of exp
+// relative to it, argmax; ids increase from chunk to chunk, so a strictly
+// larger value is what moves the argmax and equal maxima keep the lowest id)
+__device__ __forceinline__ void gm_fold_lane(const float (&l)[8], long v0, long vend, int voff,
+                                             int32_t mask_id, float& m, float& s, int& a) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  float x[8];
+  float cm = -INFINITY;
+  int ca = INT32_MAX;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const long v = v0 + 16 * j;
+    const bool live = v < vend && static_cast<long>(voff) + v != mask_id && l[j] == l[j];
+    x[j] = live ? l[j] : -INFINITY;
+    if (x[j] > cm) {
+      cm = x[j];
+      ca = static_cast<int>(v) + voff;
+    }
+  }
+  if (cm > m) {                                    // a new maximum: rescale the sum
+    s = (m == -INFINITY) ? 0.0f : s * exp2f((m - cm) * kLog2e);
+    m = cm;
+    a = ca;
+  }
+  if (m != -INFINITY) {
+    const float m2 = m * kLog2e;
+    float add = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add += (x[j] == -INFINITY) ? 0.0f : exp2f(fmaf(x[j], kLog2e, -m2));
+    s += add;
+  }
+}
+
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// A workgroup barrier that orders memory operations in the compiler but
+// waits for nothing itself: the stage loads that must have landed are
+// waited for explicitly before it (__syncthreads would wait for every load
+// into LDS still in flight, the stages ahead included).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(512, 2) void head_gemm_kernel(
+    const uint16_t* __restrict__ h, int T, int H, const uint16_t* __restrict__ w, int V,
+    int voff, int layout, int32_t mask_id, int tok0, int P, float* __restrict__ pm,
+    float* __restrict__ ps, int32_t* __restrict__ pa, int pstride) {
+  // the stage buffers as separate arrays: the loads into all but one of
+  // them are in flight while that one is read
+  __shared__ u32x4 lds0[kGmTiles][kWave];                       // 32 KB each
+  __shared__ u32x4 lds1[kGmTiles][kWave];
+  __shared__ u32x4 lds2[kGmTiles][kWave];
+  __shared__ u32x4 lds3[kGmTiles][kWave];
+  __shared__ u32x4 lds4[kGmBufs == 5 ? kGmTiles : 1][kWave];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int wm = wave & 3;
+  const int wn = wave >> 2;
+  const int nmb = (T + kGmBM - 1) / kGmBM;
+  // XCD x (workgroup b runs on XCD b % 8) takes ranges [x P/8, (x+1) P/8);
+  // its workgroups run the ranges for a group of G row blocks at a time,
+  // the G row blocks of one range consecutive (they share the range's
+  // weights through L2; fewer row blocks at a time keep their hidden rows
+  // in L2)
+  int q, mb;
+  if (P % 8 == 0) {
+    const int x = static_cast<int>(blockIdx.x % 8), i = static_cast<int>(blockIdx.x / 8);
+    const int R8 = P / 8;
+    int G = BDM_HEAD_GEMM_MGROUP;
+    G = (G <= 0 || G > nmb) ? nmb : G;
+    const int per = R8 * G;                                     // items of a full group
+    const int mg = i / per, rem = i % per;
+    const int gsz = (mg * G + G <= nmb) ? G : nmb - mg * G;     // the last group may be short
+    q = x * R8 + rem / gsz;
+    mb = mg * G + rem % gsz;
+  } else {
+    q = static_cast<int>(blockIdx.x) / nmb;
+    mb = static_cast<int>(blockIdx.x) % nmb;
+  }
+  if (q >= P) return;                                            // (grid = nmb * P)
+  const long ngroups = (V + 15) / 16;
+  const long G0 = static_cast<long>(q) * ngroups / P;
+  const long G1 = static_cast<long>(q + 1) * ngroups / P;
+  const long vend = G1 * 16 < V ? G1 * 16 : V;                   // this range: [16 G0, vend)
+  const int nchunk = static_cast<int>((G1 - G0 + 15) / 16);
+  const int rb = mb * kGmBM;                                      // first row of the block
+  const int KST = H / kGmBK;                                      // stages per chunk
+  const int total = nchunk * KST;
+
+  // loads of a stage: waves 0-3 the 16 hidden-row tiles (wave w: row tiles
+  // 4w .. 4w+3), waves 4-7 the 16 vocabulary tiles; lane l's 16 bytes land
+  // at l * 16 of the tile (the MFMA operand order)
+  const bool rows_side = wave < 4;
+  const int t16 = (wave & 3) * 4;                                 // first 16-row tile
+  const bool packed = !rows_side && layout == BDM_LAYOUT_MFMA_TILES;
+  const int sstride = packed ? 512 : kGmBK;                       // elements per stage
+  const uint16_t* base[4];                                        // k = 0 of tile row u
+  if (rows_side) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int r = rb + (t16 + u) * 16 + c;
+      r = r < T ? r : T - 1;
+      base[u] = h + static_cast<size_t>(tok0 + r) * H + g * 8;
+    }
+  }
+  auto chunk_rows = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      long gi = G0 + ch * 16 + t16 + u;
+      gi = chk(gi < ngroups ? gi : ngroups - 1, ngroups, kChkVocabRow);
+      if (packed) {
+        base[u] = w + static_cast<size_t>(gi) * (H / 32) * 512 + lane * 8;
+      } else {
+        long v = gi * 16 + c;
+        v = v < V ? v : V - 1;
+        base[u] = w + static_cast<size_t>(v) * H + g * 8;
+      }
+    }
+  };
+  const int tbase = (rows_side ? 0 : 16) + t16;
+  auto stage = [&](int it, u32x4 (*buf)[kWave]) __attribute__((always_inline)) {
+    const int st = it % KST;
+    if (st == 0 && !rows_side) chunk_rows(it / KST);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base[u] + st * sstride),
+          (__attribute__((address_space(3))) void*)&buf[tbase + u][0], 16, 0, 0);
+  };
+
+  // this lane's running state of its 16 rows (row tile i, row 4 g + e)
+  float sm[16], ss[16];
+  int sa[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sm[r] = -INFINITY;
+    ss[r] = 0.0f;
+    sa[r] = INT32_MAX;
+  }
+  f32x4 acc[4][8];
+  auto zero = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto mma = [&](u32x4 (*buf)[kWave]) __attribute__((always_inline)) {
+    u32x4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = buf[wm * 4 + i][lane];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 b = buf[16 + wn * 8 + j][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_bf16(a[i], b, acc[i][j]);
+    }
+  };
+  auto fold = [&](int ch) __attribute__((always_inline)) {
+    const long v0 = (G0 + ch * 16) * 16 + wn * 128 + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float l[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) l[j] = acc[i][j][e];
+        gm_fold_lane(l, v0, vend, voff, mask_id, sm[i * 4 + e], ss[i * 4 + e], sa[i * 4 + e]);
+      }
+  };
+  // stage it: stage it + NB - 1's loads first, then this one's products (a
+  // finished chunk folded); then this wave's loads of stage it + 1 are
+  // waited for (those of the later stages stay in flight) and the barrier
+  // makes every wave's visible
+  // (every step issues four loads, branch-free, so that the compiler can
+  // count them: past the last stage it loads the last one again into the
+  // buffer no stage uses any more)
+  constexpr int NB = kGmBufs;
+  auto step = [&](int it, u32x4 (*cur)[kWave], u32x4 (*ahead)[kWave]) __attribute__((always_inline)) {
+    stage(it + NB - 1 < total ? it + NB - 1 : total - 1, ahead);
+    mma(cur);
+    if ((it + 1) % KST == 0) {
+      fold(it / KST);
+      zero();
+    }
+    wait_vmcnt<4 * (NB - 2)>();
+    stage_barrier();
+  };
+  auto last = [&](int it) { return it < total ? it : total - 1; };
+
+  if (total > 0) {
+    stage(0, lds0);
+    stage(last(1), lds1);
+    stage(last(2), lds2);
+    if constexpr (NB == 5) stage(last(3), lds3);
+    wait_vmcnt<4 * (NB - 2)>();
+    stage_barrier();
+    zero();
+    int it = 0;
+    if constexpr (NB == 4) {
+      for (; it + 3 < total; it += 4) {
+        step(it, lds0, lds3);
+        step(it + 1, lds1, lds0);
+        step(it + 2, lds2, lds1);
+        step(it + 3, lds3, lds2);
+      }
+      if (it < total) step(it, lds0, lds3);
+      if (it + 1 < total) step(it + 1, lds1, lds0);
+      if (it + 2 < total) step(it + 2, lds2, lds1);
+    } else {
+      for (; it + 4 < total; it += 5) {
+        step(it, lds0, lds4);
+        step(it + 1, lds1, lds0);
+        step(it + 2, lds2, lds1);
+        step(it + 3, lds3, lds2);
+        step(it + 4, lds4, lds3);
+      }
+      if (it < total) step(it, lds0, lds4);
+      if (it + 1 < total) step(it + 1, lds1, lds0);
+      if (it + 2 < total) step(it + 2, lds2, lds1);
+      if (it + 3 < total) step(it + 3, lds3, lds2);
+    }
+    wait_vmcnt<0>();                         // no load into LDS outlives the loop
+  }
+  // merge: the 16 lanes of each row (a fixed DPP tree), then the two
+  // vocabulary halves
+  SoftStat* red = reinterpret_cast<SoftStat*>(&lds0[0][0]);       // [2][kGmBM]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = i * 4 + e;
+      const SoftStat x = row_merge_stat(SoftStat{sm[r], ss[r], sa[r]});
+      if (c == 0) red[wn * kGmBM + wm * 64 + i * 16 + g * 4 + e] = x;
+    }
+  __syncthreads();
+  if (tid < kGmBM && rb + tid < T) {
+    const SoftStat x = softstat_merge(red[tid], red[kGmBM + tid]);
+    const size_t o = static_cast<size_t>(tok0 + rb + tid) * pstride + chk(q, pstride, kChkStat);
+    pm[o] = x.m;
+    ps[o] = x.s;
+    pa[o] = x.a;
+  }
+}
+
 using CoopKernel = void (*)(const uint16_t*, int, const uint16_t*, int, int, int, int32_t, int,
                             int, int, int, float*, float*, int32_t*, int, const int32_t*, int,
                             float*, float*);
@@ -731,6 +1025,13 @@ void launch_head_stats(const uint16_t* h, int T, int H, const uint16_t* w, int V
 #ifndef BDM_HEAD_PASS_PAR
 #define BDM_HEAD_PASS_PAR 1
 #endif
+  if (T >= kGmMinRows && H % kGmBK == 0 && grid >= 1 &&
+      (layout == BDM_LAYOUT_ROW_MAJOR || layout == BDM_LAYOUT_MFMA_TILES)) {
+    const int nmb = (T + kGmBM - 1) / kGmBM;
+    head_gemm_kernel<<<nmb * grid, 512, 0, s>>>(h, T, H, w, V, voff, layout, mask_id, 0, grid,
+                                                pm, ps, pa, pstride);
+    return;
+  }
   if (BDM_HEAD_COOP && H % 256 == 0 && coop_kernel_for<2, false>(H)) {
     // more rows than one pass takes: every pass in one launch (a power of
     // two of them, at most 32, so that whole groups of them fill each XCD)

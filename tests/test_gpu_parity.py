@@ -398,14 +398,15 @@ def test_head_two_phase_and_vocab_shards(bdm, layout, T):
 
 
 @pytest.mark.parametrize("T,V", [(33, 70001), (64, 70001), (100, 70001), (130, 70001),
-                                 (300, 70001), (2048, 70001), (512, 248320), (97, 1000)])
+                                 (255, 70001), (97, 1000)])
 def test_head_wide_pass_equals_32_row_calls(bdm, T, V):
-    """Up to 64 rows share one pass over the head weights, and more rows run
-    as several passes in one launch (2 .. 32 of them, workgroups of one
+    """Up to 64 rows share one pass over the head weights, and up to 255 rows
+    run as several passes in one launch (2 .. 4 of them, workgroups of one
     vocabulary range side by side); every row's partial statistics equal
     those of the same row computed in a call of at most 32 rows, bit for bit
     (the per-row arithmetic and the vocabulary ranges do not change).  V =
-    1000 leaves most ranges empty."""
+    1000 leaves most ranges empty.  (From 256 rows the head runs as a tiled
+    GEMM whose sums run in another order: test_head_gemm_rows.)"""
     say(f"case head wide pass T={T} V={V}")
     s = synth.HeadShape(T=T, H=2048, V=V, mask_id=5)
     W = synth.head_weights(s, 6, device=DEV)
@@ -426,7 +427,35 @@ def test_head_wide_pass_equals_32_row_calls(bdm, T, V):
 
 
 @LAYOUTS
-@pytest.mark.parametrize("T", [65, 130, 256])
+@pytest.mark.parametrize("T,V,H", [(256, 70001, 2048), (300, 70001, 2048), (512, 248320, 2048),
+                                   (2048, 70001, 2048), (300, 1000, 2048), (700, 4099, 256),
+                                   (260, 5000, 64)])
+def test_head_gemm_rows(bdm, T, V, H, layout):
+    """From 256 rows (several blocks in one call) the head is a tiled GEMM
+    (256 rows x 256 vocabulary rows per tile, the whole K per tile, the
+    online softmax folded per tile): every row's argmax and conf against the
+    oracle and the commit rule per 32-row block.  Ragged row counts (a
+    partial last row block), V = 1,000 (most ranges empty), small H."""
+    say(f"case head GEMM rows T={T} V={V} H={H} layout={layout}")
+    s = synth.HeadShape(T=T, H=H, V=V, mask_id=V // 7)
+    W = synth.head_weights(s, T + 3, device=DEV)
+    blk = synth.head_block(s, W, block_seed=T + 4, n_boost=T // 3, committed_rows=7)
+    w_head = bdm.bdm_pack_weights(W) if layout else W
+    tokens = blk.tokens.clone()
+    am = torch.full((T,), -1, dtype=torch.int32, device=DEV)
+    cf = torch.full((T,), float("nan"), dtype=torch.float32, device=DEV)
+    nc = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    bdm.bdm_lm_head_unmask(blk.h, w_head, s.mask_id, 0.95, True, tokens, argmax=am, conf=cf,
+                           n_committed=nc, block_tokens=32)
+    torch.cuda.synchronize()
+    o = ohead.head_unmask(synth.bf16_bits(blk.h), synth.bf16_bits(W), blk.tokens.cpu().numpy(),
+                          s.mask_id, 0.95, True, block=32)
+    o["mask_id"] = s.mask_id
+    compare_head((tokens, am, cf, nc), o, blk.tokens.cpu().numpy())
+
+
+@LAYOUTS
+@pytest.mark.parametrize("T", [65, 130, 255])
 def test_head_many_rows(bdm, T, layout):
     """Several 64-row passes in one launch against the oracle: every row's
     argmax/conf and the commit decisions."""
