@@ -273,6 +273,9 @@ __global__ __launch_bounds__(kDnWaves * 64, 2) void down_kernel(
 #ifndef BDM_WIDE_GU_BIG_T
 #define BDM_WIDE_GU_BIG_T 512
 #endif
+#ifndef BDM_WIDE_GU_SMALL_GROUPS
+#define BDM_WIDE_GU_SMALL_GROUPS 4     // column groups per gate/up item below BDM_WIDE_GU_BIG_T
+#endif
 #ifndef BDM_WIDE_DN_GROUPS
 #define BDM_WIDE_DN_GROUPS 1
 #endif
@@ -705,7 +708,7 @@ void launch_experts(const uint16_t* x, int T, int H, int I, int E, int k, int ha
   if (T >= BDM_WIDE_MIN_T && H % 256 == 0 && (ksw == 1 || ksw == 2 || ksw == 4 || ksw == 8) &&
       KI <= 16) {
     // fewer tokens, fewer slots: narrower gate/up items keep every CU busy
-    const int gpi = T >= kWideGuBigT ? kWideGuGroups : 4;
+    const int gpi = T >= kWideGuBigT ? kWideGuGroups : BDM_WIDE_GU_SMALL_GROUPS;
     const int gu_runs = (I / 16 + gpi - 1) / gpi;
     const int dn_runs = (H / 16 + 8 * kWideDnGroups - 1) / (8 * kWideDnGroups);
     using GuWide = void (*)(const uint16_t*, int, int, int, int, int, int, const uint16_t*,
