@@ -32,6 +32,11 @@ factor is reported for comparison only.
         of one denoise step, and of the MoE layer launched back to back, goes
         (median duration of each kernel in launch order and median idle gap
         before it, over every matching launch sequence).
+    python -m block_diffusion_moe_amd.traffic stats --csv FILE --out FILE [--command TEXT]
+        [--note TEXT]
+        the `rocprofv3 --stats` kernel table (calls, mean, min and max
+        duration of every kernel of this library and of the calibration
+        library) as markdown.
 """
 from __future__ import annotations
 
@@ -329,6 +334,33 @@ def timeline(a):
     print("\n".join(out))
 
 
+def stats(a):
+    rows = []
+    with open(a.csv, newline="") as fh:
+        for r in csv.DictReader(fh):
+            n = r["Name"].replace("(anonymous namespace)::", "")
+            n = (n[5:] if n.startswith("void ") else n).split("(", 1)[0]
+            if not n.startswith("bdm"):
+                continue
+            rows.append((float(r["TotalDurationNs"]), n, int(r["Calls"]),
+                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3))
+    rows.sort(reverse=True)
+    out = ["# rocprofv3 kernel statistics", ""]
+    if a.note:
+        out += [a.note, ""]
+    if a.command:
+        out += ["Command (run from the repository root on one MI355X):", "", "```", a.command,
+                "```", ""]
+    out += ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for _, n, calls, avg, mn, mx in rows:
+        out.append(f"| {n} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+    out.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(out))
+    print("\n".join(out))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -347,9 +379,16 @@ def main(argv=None):
     t.add_argument("--trace", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="")
+    k = sub.add_parser("stats")
+    k.add_argument("--csv", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--command", default="")
+    k.add_argument("--note", default="")
     a = p.parse_args(argv)
     if a.cmd == "copy":
         copy_kernel()
+    elif a.cmd == "stats":
+        stats(a)
     elif a.cmd == "mfma":
         mfma(a)
     elif a.cmd == "timeline":
