@@ -60,7 +60,7 @@ MOE_SOURCES = ("router.hip", "experts.hip", "device.hpp", "internal.hpp")
 # grids in threads: router 16 x 1 x 4 workgroups of 256, top-k 8 of 256,
 # grouping 1 of 1,024, gate/up and down (one-block kernels, used below 256
 # tokens only), combine 32 of 256
-MOE_LAYER_GRIDS = {"bdm::router_kernel<1>": 16384,
+MOE_LAYER_GRIDS = {"bdm::router_kernel<1, false>": 16384,
                    "bdm::select_kernel<4, 4, false, false>": 2048,
                    "bdm::group_kernel<4>": 1024, "bdm::gateup_kernel<8, false>": None,
                    "bdm::down_kernel<16, false>": None, "bdm::combine_kernel": 8192}
@@ -222,21 +222,21 @@ def mfma(a):
 
 
 # launch sequences of the single-block path (kernel names without arguments)
-MOE_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, false>",
+MOE_SEQ = ("bdm::router_kernel<1, false>", "bdm::select_kernel<4, 4, false, false>",
            "bdm::group_kernel<4>", "bdm::gateup_kernel<8, false>", "bdm::down_kernel<16, false>",
            "bdm::combine_kernel")
 STEP_SEQ = ("bdm::rmsnorm_kernel",) + MOE_SEQ + ("bdm::head_coop_kernel<8, 2, false, false>",
                                                    "bdm::head_merge_kernel")
 # the layer with the block coreset selector over one 32-token block
-CORESET_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, true>",
+CORESET_SEQ = ("bdm::router_kernel<1, false>", "bdm::select_kernel<4, 4, false, true>",
                "bdm::coreset_kernel<4, true>", "bdm::gateup_kernel<8, false>",
                "bdm::down_kernel<16, false>", "bdm::combine_kernel")
 # many-token calls: 256 tokens (the load-skew batch; one-tile router) and
 # 512 .. 2,048 tokens (multi-block batches; four-tile router)
-SKEW_SEQ = ("bdm::router_kernel<1>", "bdm::select_kernel<4, 4, false, false>",
+SKEW_SEQ = ("bdm::router_kernel<1, false>", "bdm::select_kernel<4, 4, false, false>",
             "bdm::group_kernel<4>", "bdm::gateup_wide_kernel<8>", "bdm::down_wide_kernel<16>",
             "bdm::combine_kernel")
-MULTI_SEQ = ("bdm::router_kernel<4>",) + SKEW_SEQ[1:]
+MULTI_SEQ = ("bdm::router_kernel<4, false>",) + SKEW_SEQ[1:]
 
 
 def _kernel_name(n: str) -> str:
@@ -245,13 +245,15 @@ def _kernel_name(n: str) -> str:
 
 
 def read_trace(path: str):
-    """(start ns, end ns, name) of every bdm kernel dispatch, in start order."""
+    """(start ns, end ns, name, grid size) of every bdm kernel dispatch, in
+    start order."""
     out = []
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
             n = _kernel_name(r["Kernel_Name"])
             if n.startswith("bdm"):
-                out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), n))
+                grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+                out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), n, grid))
     out.sort()
     return out
 
@@ -315,20 +317,16 @@ def timeline(a):
     if sk:
         out += _table(trace, SKEW_SEQ, sk,
                       "Load-skew batch (8 blocks, 256 tokens, log-Zipf offset), back to back")
-    # the multi-block calls run size after size: one table per run of
-    # adjacent sequences
-    mb = sequences(trace, MULTI_SEQ)
-    runs, cur = [], []
-    for i in mb:
-        if cur and i != cur[-1] + len(MULTI_SEQ):
-            runs.append(cur)
-            cur = []
-        cur.append(i)
-    if cur:
-        runs.append(cur)
-    for r in runs:
-        if len(r) >= 4:                       # the timed loop (not the routing probes)
-            out += _table(trace, MULTI_SEQ, r[1:], "Multi-block call (one size), back to back")
+    # the multi-block calls, one table per size (the combine's grid is one
+    # workgroup per token)
+    by_size = collections.defaultdict(list)
+    for i in sequences(trace, MULTI_SEQ):
+        by_size[trace[i + len(MULTI_SEQ) - 1][3] // 256].append(i)
+    for T in sorted(by_size):
+        hits = by_size[T]
+        if len(hits) >= 4:                    # the timed loop (not the routing probes)
+            out += _table(trace, MULTI_SEQ, hits,
+                          f"Multi-block call, {T} tokens ({T // 32} blocks), back to back")
     with open(a.out, "w") as fh:
         fh.write("\n".join(out))
     print("\n".join(out))
