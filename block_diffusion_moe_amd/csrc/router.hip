@@ -799,22 +799,46 @@ __global__ __launch_bounds__(kCsWaves * 64) void coreset_kernel(
   }
   __syncthreads();
   // rank in mass order (larger first, equal -> lower id), counted over the
-  // touched experts, the list split among the threads
+  // touched experts: every wave holds the whole list in registers (lane l:
+  // entries l, l + 64, ...; a positive mass orders as its bits), wave w
+  // ranks the 64 entries of group w % ng against the part w / ng of the
+  // list, reading the other entries with readlane (no memory in the loop)
   const int nt = s_ntouch;
-  const int spl = nt > 0 ? max(1, min(16, static_cast<int>(blockDim.x) / nt)) : 1;
-  const int qchunk = (nt + spl - 1) / spl;
-  for (int w = tid; w < nt * spl; w += blockDim.x) {
-    const int q = w % nt;
-    const int pp = w / nt;
-    const int e = tlist[q];
-    const float m = tmass[q];
-    int r = 0;
-    const int j1 = min(nt, (pp + 1) * qchunk);
-    for (int j = pp * qchunk; j < j1; ++j) {
-      const float mj = tmass[j];
-      r += (mj > m || (mj == m && tlist[j] < e)) ? 1 : 0;
+  {
+    uint32_t kb[PER];
+    int kid[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = lane + kWave * i;
+      kb[i] = q < nt ? __float_as_uint(tmass[chk(q, E, kChkCand)]) : 0u;
+      kid[i] = q < nt ? tlist[chk(q, E, kChkCand)] : INT32_MAX;
     }
-    atomicAdd(&cnt[e], r);                      // integer counts: any order
+    const int ng = (nt + kWave - 1) / kWave;               // groups of 64 entries
+    const int nsp = ng > 0 ? max(1, kCsWaves / ng) : 1;   // parts of the list
+    if (ng > 0 && wave < ng * nsp) {
+      const int gq = wave % ng, pp = wave / ng;
+      const int chunk = (nt + nsp - 1) / nsp;
+      const int j0 = pp * chunk, j1 = min(nt, j0 + chunk);
+      uint32_t mb = 0u;
+      int me = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == gq) {
+          mb = kb[i];
+          me = kid[i];
+        }
+      int r = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int lo = max(j0 - kWave * i, 0), hi = min(j1 - kWave * i, kWave);
+        for (int l = lo; l < hi; ++l) {
+          const uint32_t bj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kb[i]), l));
+          const int idj = __builtin_amdgcn_readlane(kid[i], l);
+          r += (bj > mb || (bj == mb && idj < me)) ? 1 : 0;
+        }
+      }
+      if (gq * kWave + lane < nt) atomicAdd(&cnt[chk(me, E, kChkExpert)], r);   // any order
+    }
   }
   __syncthreads();
   for (int q = tid; q < nt; q += blockDim.x) {
